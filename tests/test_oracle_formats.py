@@ -1,0 +1,220 @@
+"""Pins of the oracle's E4M3 / E2M1 / NVFP4 codecs (CPU only).
+
+The pins are independent of the oracle's own code: PyTorch's float8_e4m3fn
+conversion (a library routine), the OCP format anchors and the E2M1 rounding
+table worked by hand (tests/golden), and properties the formats fix.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import read_golden
+
+
+def _torch_e4m3_values():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_decode_all_codes_matches_torch(oracle):
+    got = oracle.e4m3_value(np.arange(256))
+    want = _torch_e4m3_values()
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+    assert (np.signbit(got) == np.signbit(want))[~np.isnan(want)].all()
+
+
+def test_e4m3_anchor_values(oracle):
+    for code, val in read_golden("e4m3_anchors.txt"):
+        got = float(oracle.e4m3_value([int(code, 16)])[0])
+        want = float(val)
+        if math.isnan(want):
+            assert math.isnan(got)
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), code
+
+
+def test_e4m3_structure(oracle):
+    v = oracle.e4m3_value(np.arange(128))
+    finite = v[:127]
+    assert np.all(np.diff(finite) > 0), "non-negative codes 0x00..0x7E must increase strictly"
+    assert np.isnan(v[127])
+    neg = oracle.e4m3_value(np.arange(128, 256))
+    assert np.array_equal(neg[:127], -finite)
+    assert (np.isnan(oracle.e4m3_value(np.arange(256)))).sum() == 2
+
+
+def _e4m3_encode_inputs():
+    vals = _torch_e4m3_values()[:127]
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(0)
+    pts = np.concatenate([
+        vals, mids,
+        np.nextafter(mids.astype(np.float32), np.float32(0)).astype(np.float64),
+        np.nextafter(mids.astype(np.float32), np.float32(1e9)).astype(np.float64),
+        rng.uniform(0, 464, 4000), np.exp(rng.uniform(-16, 6.1, 4000)),
+    ]).astype(np.float32)
+    pts = pts[pts <= 464.0]
+    return np.concatenate([pts, -pts])
+
+
+def test_e4m3_encode_rne_matches_torch(oracle):
+    x = _e4m3_encode_inputs()
+    got = oracle.e4m3_encode(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(want[i])) for i in bad[:10]]
+
+
+def test_e4m3_encode_saturates_and_nan(oracle):
+    big = np.array([448.0, 464.0, 464.01, 480.0, 1e6, 1e30, np.inf], dtype=np.float32)
+    assert (oracle.e4m3_encode(big) == 0x7E).all()
+    assert (oracle.e4m3_encode(-big) == 0xFE).all()
+    assert oracle.e4m3_encode([np.nan])[0] & 0x7F == 0x7F
+    assert oracle.e4m3_encode([-0.0])[0] == 0x80
+
+
+def test_e2m1_table(oracle):
+    for code, val in read_golden("e2m1_table.txt"):
+        got = float(oracle.e2m1_value([int(code, 16)])[0])
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), code
+
+
+def test_e2m1_rounding_table(oracle):
+    for x, code in read_golden("e2m1_rounding.txt"):
+        assert int(oracle.e2m1_encode([float(x)])[0]) == int(code, 16), x
+
+
+def test_e2m1_encode_is_nearest(oracle):
+    """Any input maps to a grid point at least as close as every other one."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    x = np.random.default_rng(1).uniform(-7, 7, 20000).astype(np.float32)
+    codes = oracle.e2m1_encode(x)
+    vals = oracle.e2m1_value(codes)
+    ax = np.minimum(np.abs(x.astype(np.float64)), 6.0)
+    best = np.min(np.abs(grid[None, :] - ax[:, None]), axis=1)
+    assert np.all(np.abs(np.abs(vals) - ax) <= best + 0.0)
+    assert np.all((np.signbit(vals)) == np.signbit(x))
+
+
+# ------------------------------------------------------------------ NVFP4
+def test_nvfp4_product_table_exhaustive(oracle):
+    """All 16 E2M1 codes x 256 E4M3 scales: the value is the exact product, it
+    has at most 6 significant bits, and lies in [2^-10, 2688] when nonzero."""
+    e2m1 = oracle.e2m1_value(np.arange(16))
+    e4m3 = _torch_e4m3_values()
+    L = oracle.lib()
+    n_exact = 0
+    for s in range(256):
+        if np.isnan(e4m3[s]):
+            continue
+        for c in range(16):
+            v = L.ref_nvfp4_value(c, s, 1.0)
+            assert v == e2m1[c] * e4m3[s]
+            if v != 0:
+                m, e = math.frexp(abs(v))
+                assert (m * 64) == int(m * 64), "more than 6 significant bits"
+                assert 2.0 ** -10 <= abs(v) <= 2688.0
+                # exact in float16 (11 significant bits, range to 65504)
+                assert float(np.float16(v)) == v
+            n_exact += 1
+    assert n_exact == 254 * 16
+
+
+def test_page_table_counts(oracle):
+    facts = {r[0]: int(r[1]) for r in read_golden("page_facts.txt")}
+    # 256 scales x 8 magnitudes x 1 byte = the pages' 2 KB lookup table
+    assert facts["e4m3_scale_values"] * facts["e2m1_magnitudes"] == facts["lds_table_bytes"]
+    assert len(set(np.abs(oracle.e2m1_value(np.arange(16))))) == facts["e2m1_magnitudes"]
+
+
+def test_nvfp4_byte_cost_matches_pages(oracle):
+    """16 elements -> 8 code bytes + 1 scale byte = 0.5625 B/element, the pages' 34,560/61,440."""
+    facts = {r[0]: int(r[1]) for r in read_golden("page_facts.txt")}
+    codes, scales = oracle.nvfp4_quantize(np.ones((1, 16), np.float32), 1.0)
+    per_elem = (codes.size + scales.size) / 16
+    assert per_elem == facts["nvfp4_kv_bytes_per_token"] / facts["fp8_kv_bytes_per_token"]
+    assert 10000 - 10000 * per_elem == facts["saving_percent_x100"]
+    # K+V of 4 heads x 128 dims per layer at 0.5625 B = 576 B; 34,560 / 576 = 60 layers
+    assert facts["nvfp4_kv_bytes_per_token"] % int(2 * 4 * 128 * per_elem) == 0
+
+
+def _deq(oracle, codes, scales, ts):
+    e2m1 = oracle.e2m1_value(np.arange(16))
+    e4m3 = _torch_e4m3_values()
+    lo = codes & 0xF
+    hi = codes >> 4
+    c = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (16,))
+    return e2m1[c] * e4m3[scales][..., None] * ts
+
+
+def test_nvfp4_zero_block(oracle):
+    codes, scales = oracle.nvfp4_quantize(np.zeros((3, 16), np.float32), 0.01)
+    assert (codes == 0).all() and (scales == 0).all()
+    tiny = np.full((1, 16), 1e-30, np.float32)
+    codes, scales = oracle.nvfp4_quantize(tiny, 1.0)
+    assert (codes == 0).all() and (scales == 0).all()
+
+
+def test_nvfp4_roundtrip_of_representable_blocks(oracle):
+    """A block whose values are c * s * ts with some |c| = 6 quantises back to the same bytes."""
+    rng = np.random.default_rng(2)
+    e4m3 = _torch_e4m3_values()
+    ts = float(np.float32(8 / (6 * 448)))
+    for _ in range(300):
+        c = rng.integers(0, 16, 16).astype(np.uint8)
+        c[rng.integers(0, 16)] = 7 | (8 * rng.integers(0, 2))
+        s = int(rng.integers(8, 0x7E))  # normal scales
+        vals = (oracle.e2m1_value(c) * e4m3[s] * ts).astype(np.float32)
+        codes, scales = oracle.nvfp4_quantize(vals, ts)
+        got_vals = _deq(oracle, codes, scales, ts)[0]
+        assert scales[0] == s
+        # +0 and -0 may differ only where the value is zero
+        assert np.array_equal(got_vals, oracle.e2m1_value(c) * e4m3[s] * ts)
+        nz = oracle.e2m1_value(c) != 0
+        lo = codes[0] & 0xF
+        hi = codes[0] >> 4
+        got_c = np.stack([lo, hi], -1).reshape(16)
+        assert np.array_equal(got_c[nz], c[nz])
+
+
+def test_nvfp4_error_bound(oracle):
+    """|x - q(x)| is at most half an E2M1 grid step (1, 0.5 or 0.25 scaled by s*ts), unless saturated."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2000, 16)).astype(np.float32)
+    ts = float(np.float32(8 / (6 * 448)))
+    codes, scales = oracle.nvfp4_quantize(x, ts)
+    codes, scales = codes.reshape(2000, 8), scales.reshape(2000)
+    e4m3 = _torch_e4m3_values()
+    deq = _deq(oracle, codes, scales, ts)
+    step = e4m3[scales][:, None] * ts
+    y = np.abs(x / step)
+    half = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
+    sat = y > 6
+    err = np.abs(deq - x)
+    assert np.all(err[~sat] <= half[~sat] * step.repeat(16, 1)[~sat] * (1 + 1e-6))
+    # amax maps close to 6: the scale is the E4M3 rounding of amax/6/ts
+    amax = np.abs(x).max(1)
+    assert np.all(np.abs(e4m3[scales] - amax / 6 / ts) <= e4m3[scales] / 16 + 1e-12)
+
+
+def test_nvfp4_saturation(oracle):
+    x = np.full((1, 16), 1e6, np.float32)
+    x[0, 3] = -1e6
+    codes, scales = oracle.nvfp4_quantize(x, 1.0)
+    assert scales[0] == 0x7E
+    lo = codes[0] & 0xF
+    hi = codes[0] >> 4
+    c = np.stack([lo, hi], -1).reshape(16)
+    assert (c[np.arange(16) != 3] == 7).all() and c[3] == 0xF
+
+
+def test_queries_e4m3(oracle):
+    x = np.random.default_rng(4).standard_normal(5000).astype(np.float32)
+    got = oracle.quantize_queries(x, 1.0)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    dec = oracle.decode_queries(got, oracle.FP8_E4M3, 0.5)
+    assert np.array_equal(dec, torch.from_numpy(want).view(torch.float8_e4m3fn).double().numpy() * 0.5)

@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for the MSA decode step.
+
+This module is shared by the tests, ``bench.py`` and ``smoke()``.  It feeds both
+the HIP path and the CPU oracle, so it holds none of the method's arithmetic:
+it draws FP32 key/value/index-key rows, FP32 queries, context lengths and page
+tables, and nothing else.  Quantisation to NVFP4 / FP8 happens on each side
+separately (the HIP insert and query kernels; the oracle's own quantiser).
+
+Shapes follow the workloads the pages describe (one sparse layer of the
+MiniMax-M3 family, [vLLM M3.1 post, "How MiniMax Sparse Attention works" and
+"NVFP4 indexer DCP on CDNA4"]): 4 KV heads of dim 128, 8 query heads per GQA
+group, one shared index-key head of dim 128, 128-token pages = selection
+blocks, top-16.  The pages' own workloads (agentic traces, "45 requests of
+30K-210K tokens") are not available; these seeded N(0,1) caches stand in for
+them and take only their shapes.
+
+Draw order is fixed: lengths -> physical page permutation -> per-request
+token rows (one stream per request, idx then K then V) -> queries (q_idx then q).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+PAGE = 128
+DIM = 128
+G = 4  # KV heads = GQA groups
+HPG = 8  # query heads per group
+H = G * HPG
+TOPK = 16
+# NVFP4 per-tensor FP32 scale for N(0,1) rows: amax bound 8 over (E2M1 max 6 x E4M3 max 448).
+NVFP4_TENSOR_SCALE = float(np.float32(8.0 / (6.0 * 448.0)))
+SM_SCALE = float(np.float32(1.0 / np.sqrt(DIM)))
+
+CONFIGS = {
+    1: dict(name="tiny_f32_4k", B=1, R=1, lens=("fixed", 4096), cache="f32", table="contiguous"),
+    2: dict(name="nvfp4_b8_32k", B=8, R=1, lens=("fixed", 32768), cache="nvfp4", table="shuffled"),
+    3: dict(name="long_ctx_b32_64k_192k", B=32, R=1, lens=("uniform", 65536, 196608), cache="nvfp4",
+            table="shuffled"),
+    4: dict(name="spec_r4_b16_30k_210k", B=16, R=4, lens=("uniform", 30720, 215040), cache="nvfp4",
+            table="shuffled"),
+    5: dict(name="shared_prefix_b64_256k", B=64, R=1, lens=("uniform", 1024, 8192), prefix=262144,
+            cache="nvfp4", table="shuffled"),
+}
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    B: int
+    R: int
+    cache: str  # "f32" | "nvfp4"
+    lengths: np.ndarray  # [B] int32, tokens in cache incl. the R new rows
+    block_table: np.ndarray  # [B][max_pages] int32 physical page ids (unused tail = 0)
+    num_pages: int
+    prefix_tokens: int = 0  # leading tokens shared by every request (same pages)
+    topk: int = TOPK
+    G: int = G
+    H: int = H
+    D: int = DIM
+    tensor_scale: float = 1.0
+    q_scale: float = 1.0
+    sm_scale: float = SM_SCALE
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def prefix_pages(self) -> int:
+        return self.prefix_tokens // PAGE
+
+    def own_positions(self, b: int) -> np.ndarray:
+        """Positions whose rows belong to request b alone (the prefix is written once)."""
+        return np.arange(self.prefix_tokens, int(self.lengths[b]), dtype=np.int64)
+
+    def slots(self, b: int, positions: np.ndarray) -> np.ndarray:
+        """Slot (physical page * 128 + offset) of request b's token positions."""
+        positions = np.asarray(positions, dtype=np.int64)
+        return self.block_table[b, positions // PAGE].astype(np.int64) * PAGE + positions % PAGE
+
+    def new_row_positions(self, b: int) -> np.ndarray:
+        L = int(self.lengths[b])
+        return np.arange(max(L - self.R, 0), L, dtype=np.int64)
+
+
+def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int = 1,
+                  lengths: list[int] | None = None, R: int | None = None) -> Workload:
+    """Build the shapes of a configuration.  ``B``/``len_div`` shrink it for
+    parity tests; ``lengths`` overrides the drawn lengths (edge cases)."""
+    cfg = CONFIGS[config]
+    rng = np.random.default_rng([seed, 0])
+    B = cfg["B"] if B is None else B
+    R = cfg["R"] if R is None else R
+    kind = cfg["lens"]
+    if lengths is not None:
+        lens = np.asarray(lengths, dtype=np.int64)
+        B = lens.shape[0]
+    elif kind[0] == "fixed":
+        lens = np.full(B, kind[1], dtype=np.int64)
+    else:
+        lens = rng.integers(kind[1], kind[2], size=B, endpoint=True).astype(np.int64)
+    prefix = cfg.get("prefix", 0)
+    if len_div > 1:
+        lens = np.maximum(lens // len_div, 1 if lengths is None else 0)
+        prefix = (prefix // len_div) // PAGE * PAGE
+    if lengths is None:
+        lens = lens + prefix
+    prefix_pages = prefix // PAGE
+    own_pages = [max(0, -(-int(L) // PAGE) - prefix_pages) for L in lens]
+    max_pages = max(1, max(prefix_pages + n for n in own_pages))
+    num_pages = prefix_pages + sum(own_pages)
+    num_pages = max(num_pages, 1)
+    if cfg["table"] == "contiguous":
+        perm = np.arange(num_pages, dtype=np.int64)
+    else:
+        perm = rng.permutation(num_pages)
+    table = np.zeros((B, max_pages), dtype=np.int32)
+    nxt = prefix_pages
+    for b in range(B):
+        table[b, :prefix_pages] = perm[:prefix_pages]
+        n = own_pages[b]
+        table[b, prefix_pages:prefix_pages + n] = perm[nxt:nxt + n]
+        nxt += n
+    ts = NVFP4_TENSOR_SCALE if cfg["cache"] == "nvfp4" else 1.0
+    return Workload(name=cfg["name"], seed=seed, B=B, R=R, cache=cfg["cache"], lengths=lens.astype(np.int32),
+                    block_table=table, num_pages=int(num_pages), prefix_tokens=int(prefix), tensor_scale=ts)
+
+
+def request_rows(wl: Workload, b: int):
+    """FP32 N(0,1) rows for request b's own positions: (idx [n][128], k [n][G][128], v [n][G][128])."""
+    n = wl.own_positions(b).shape[0]
+    rng = np.random.default_rng([wl.seed, 1, b])
+    idx = rng.standard_normal((n, wl.D), dtype=np.float32)
+    k = rng.standard_normal((n, wl.G, wl.D), dtype=np.float32)
+    v = rng.standard_normal((n, wl.G, wl.D), dtype=np.float32)
+    return idx, k, v
+
+
+def prefix_rows(wl: Workload):
+    """FP32 N(0,1) rows of the shared prefix (written once, into the shared pages)."""
+    n = wl.prefix_tokens
+    rng = np.random.default_rng([wl.seed, 2])
+    idx = rng.standard_normal((n, wl.D), dtype=np.float32)
+    k = rng.standard_normal((n, wl.G, wl.D), dtype=np.float32)
+    v = rng.standard_normal((n, wl.G, wl.D), dtype=np.float32)
+    return idx, k, v
+
+
+def queries(wl: Workload):
+    """FP32 N(0,1) queries: (q_idx [B][R][G][128], q [B][R][H][128])."""
+    rng = np.random.default_rng([wl.seed, 3])
+    q_idx = rng.standard_normal((wl.B, wl.R, wl.G, wl.D), dtype=np.float32)
+    q = rng.standard_normal((wl.B, wl.R, wl.H, wl.D), dtype=np.float32)
+    return q_idx, q
+
+
+def all_rows(wl: Workload):
+    """Every cached row once, with its slot: (slots [n], idx [n][128], k [n][G][128], v [n][G][128])."""
+    parts = []
+    if wl.prefix_tokens:
+        pos = np.arange(wl.prefix_tokens, dtype=np.int64)
+        parts.append((wl.slots(0, pos),) + prefix_rows(wl))
+    for b in range(wl.B):
+        pos = wl.own_positions(b)
+        if pos.shape[0]:
+            parts.append((wl.slots(b, pos),) + request_rows(wl, b))
+    if not parts:
+        z = np.zeros((0,), np.int64)
+        return z, np.zeros((0, wl.D), np.float32), np.zeros((0, wl.G, wl.D), np.float32), \
+            np.zeros((0, wl.G, wl.D), np.float32)
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))
+
+
+def torch_rows(wl: Workload, b: int, device, prefix: bool = False):
+    """Device-side draw of the same shapes (for the benchmark's large caches).
+    Seeded, N(0,1), but a different stream from the numpy one."""
+    import torch
+
+    n = wl.prefix_tokens if prefix else wl.own_positions(b).shape[0]
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed * 1_000_003 + (0 if prefix else b + 1)) & 0x7FFFFFFF)
+    idx = torch.randn((n, wl.D), generator=gen, device=device, dtype=torch.float32)
+    k = torch.randn((n, wl.G, wl.D), generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn((n, wl.G, wl.D), generator=gen, device=device, dtype=torch.float32)
+    return idx, k, v
