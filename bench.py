@@ -1,0 +1,279 @@
+"""MSA decode benchmark on one MI355X: layer-steps/s and achieved HBM bandwidth.
+
+Workload: one sparse layer at 128K mean context -- 32 requests, one query row
+each, contexts uniform in 64K..192K tokens, NVFP4 K/V and index caches,
+FP8 queries, 4 KV heads x 128, 32 query heads, top-16 of 128-token blocks,
+random physical page order.  Inputs are seeded, synthetic N(0,1) rows drawn
+on the device.
+
+A step is one pass of the whole path over the batch: insert of the B*R new
+tokens (NVFP4 quantisation into the pages), indexer score + block max-pool,
+top-16 selection with the latest block kept, sparse attention + split merge.
+Inputs sit in HBM before timing starts; the caches rotate over replicas so
+that consecutive steps cannot serve the index scan from the 256 MB Infinity
+Cache.
+
+Prints one JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "MSA decode layer-steps/s + achieved HBM GB/s (% of peak), 128K ctx NVFP4 KV"
+CONFIG_ID = 3
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, sel, cnt):
+    """Minimum bytes one step moves (per the method): the whole index of every
+    context (72 B/token), K+V of the selected tokens of each (request, group)
+    (144 B/token: 64+8 B of K, 64+8 B of V), queries, outputs, block table,
+    and the insert of the new rows (FP32 in, NVFP4 out)."""
+    B, R = wl.B, wl.R
+    idx = int(wl.lengths.astype(np.int64).sum()) * 72
+    kv_tokens = 0
+    p = wl.lengths.astype(np.int64)[:, None] - R + np.arange(R)[None, :]
+    for b in range(B):
+        for g in range(4):
+            blocks = set()
+            lim = {}
+            for r in range(R):
+                for j in sel[b, r, g, : cnt[b, r, g]]:
+                    j = int(j)
+                    blocks.add(j)
+                    lim[j] = max(lim.get(j, -1), min(127, int(p[b, r]) - 128 * j))
+            kv_tokens += sum(lim[j] + 1 for j in blocks)
+    kv = kv_tokens * 144
+    q_bytes = B * R * 4 * 128 + B * R * 32 * 128  # FP8 index queries + queries
+    out_bytes = B * R * 32 * 128 * 4
+    table = B * wl.max_pages * 4 + B * 4
+    insert = B * R * (9 * 128 * 4 + 9 * 72)  # FP32 rows in, NVFP4 bytes out
+    return {"index": idx + B * R * 4 * 128 + table, "kv": kv, "total": idx + kv + q_bytes + out_bytes + table + insert,
+            "kv_tokens": kv_tokens}
+
+
+def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
+    """The oracle (plain FP64 C, OpenMP over (request, row, group)) timed on a
+    bounded sample of the same workload: all four steps for `sample_reqs`
+    requests, repeated until min_seconds of work; scaled to whole-batch
+    steps/s by context tokens (work is linear in them)."""
+    import oracle as O
+    import workload as W
+
+    rows = np.asarray(sample_reqs)
+    dt = O.NVFP4
+    ci = O.OracleCache(dt, O.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
+    ck = O.OracleCache(dt, O.TOKEN_MAJOR, 4, wl.num_pages, wl.tensor_scale)
+    cv = O.OracleCache(dt, O.DIM_MAJOR, 4, wl.num_pages, wl.tensor_scale)
+    for b in rows:
+        pos = wl.own_positions(int(b))
+        xi, xk, xv = W.request_rows(wl, int(b))
+        s = wl.slots(int(b), pos)
+        ci.write(s, xi), ck.write(s, xk), cv.write(s, xv)
+    qi32, q32 = W.queries(wl)
+    qi = O.decode_queries(O.quantize_queries(qi32[rows], wl.q_scale), O.FP8_E4M3, wl.q_scale)
+    q = O.decode_queries(O.quantize_queries(q32[rows], wl.q_scale), O.FP8_E4M3, wl.q_scale)
+    bt = O.OracleBatch(wl.block_table[rows], wl.lengths[rows], wl.R)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.decode_step(bt, qi, q, wl.sm_scale, ci, ck, cv, wl.topk)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per_sample = el / reps
+    frac = float(wl.lengths[rows].astype(np.int64).sum()) / float(wl.lengths.astype(np.int64).sum())
+    full_step = per_sample / frac
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": 1.0 / full_step, "unit": "layer-steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.B} requests ({int(wl.lengths[rows].sum())} of "
+                      f"{int(wl.lengths.sum())} context tokens), full step x{reps} in {el:.1f} s, "
+                      f"scaled by context tokens"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the oracle's timed sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the context-parallel indexer design is documented, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_index_amd as M
+    import workload as W
+    from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
+
+    dev = torch.device("cuda:0")
+    wl = W.make_workload(CONFIG_ID, seed=args.seed)
+    log(f"workload {wl.name}: B={wl.B} R={wl.R} tokens={int(wl.lengths.sum())} pages={wl.num_pages}")
+
+    # ---- caches (replica 0 filled by the insert kernel from device-drawn rows)
+    k0, v0, i0 = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
+    table = torch.from_numpy(wl.block_table).to(dev)
+    lens = torch.from_numpy(wl.lengths).to(dev)
+    batch = M.Batch(table, lens, wl.R)
+    for b in range(wl.B):
+        pos = wl.own_positions(b)
+        xi, xk, xv = W.torch_rows(wl, b, dev)
+        slots = torch.from_numpy(wl.slots(b, pos)).to(dev)
+        M.msa_kv_insert(xk, xv, xi, slots, k0, v0, i0)
+        del xi, xk, xv
+    torch.cuda.synchronize()
+    replicas = [(k0, v0, i0)]
+    for _ in range(args.replicas - 1):
+        k, v, i = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
+        k.pages.copy_(k0.pages), v.pages.copy_(v0.pages), i.pages.copy_(i0.pages)
+        replicas.append((k, v, i))
+    decs = [MsaDecoder(batch, k, v, i, wl.topk, dev) for (k, v, i) in replicas]
+    for d in decs[1:]:  # share the output buffers: every replica computes the same step
+        d.block_scores, d.sel, d.cnt, d.out, d.workspace = (decs[0].block_scores, decs[0].sel, decs[0].cnt,
+                                                            decs[0].out, decs[0].workspace)
+
+    # ---- step inputs: new rows of the R latest positions, FP8 queries
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 12345)
+    n_new = wl.B * wl.R
+    new_k = torch.randn((n_new, 4, 128), generator=gen, device=dev)
+    new_v = torch.randn((n_new, 4, 128), generator=gen, device=dev)
+    new_i = torch.randn((n_new, 128), generator=gen, device=dev)
+    new_slots = torch.from_numpy(np.concatenate([wl.slots(b, wl.new_row_positions(b)) for b in range(wl.B)])).to(dev)
+    qi32, q32 = W.queries(wl)
+    q_idx = M.msa_quantize_e4m3(torch.from_numpy(qi32).to(dev), wl.q_scale)
+    q = M.msa_quantize_e4m3(torch.from_numpy(q32).to(dev), wl.q_scale)
+    new = (new_k, new_v, new_i, new_slots)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    use_graph = not args.no_graph
+
+    def run_step(i, s):
+        decs[i % len(decs)].step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new, stream=s)
+
+    graphs = []
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run_step(i, stream)
+        if use_graph:
+            for r in range(len(decs)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    run_step(r, stream)
+                graphs.append(g)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for i in range(args.steps):
+            if use_graph:
+                graphs[i % len(graphs)].replay()
+            else:
+                run_step(i, stream)
+        t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (events), wall {wall / args.steps * 1e6:.1f} us/step")
+
+    # ---- per-kernel durations: for each kernel, a HIP graph of `reps` back-to-back
+    # launches (alternating cache replicas) replayed between two HIP events on
+    # the launch stream; per-launch time = elapsed / (replays * reps)
+    reps, replays = 20, max(1, args.steps // 20)
+    calls = {
+        "insert": lambda d: d.insert(*new, stream=stream),
+        "index": lambda d: d.index(q_idx, wl.q_scale, None, stream),
+        "topk": lambda d: d.select(stream),
+        "decode": lambda d: d.attend(q, wl.q_scale, wl.sm_scale, stream),
+    }
+    us = {}
+    for name, call in calls.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(reps):
+                    call(decs[i % len(decs)])
+            g.replay()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(replays):
+                g.replay()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        us[name] = a_.elapsed_time(b_) * 1e3 / (replays * reps)
+    log("per-kernel us (graph of back-to-back launches): " + ", ".join(f"{k} {v:.1f}" for k, v in us.items()))
+
+    sel = decs[0].sel.cpu().numpy()
+    cnt = decs[0].cnt.cpu().numpy()
+    nbytes = algorithmic_bytes(wl, sel, cnt)
+    steps_per_s = 1e3 / ms_step
+    idx_gbps = nbytes["index"] / (us["index"] * 1e-6) / 1e9
+    step_gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(args.seed)
+        sample = sorted(rng.choice(wl.B, size=min(args.cpu_sample, wl.B), replace=False).tolist())
+        log(f"cpu baseline: oracle on requests {sample}")
+        cpu = cpu_baseline(wl, sample)
+        log(f"cpu baseline: {cpu['value']:.3f} steps/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 kv x fp8 q (fp8xfp4 + f16 mfma, f32 accumulate)",
+        "data": "synthetic N(0,1) rows, seeded, device-generated",
+        "config": {"workload": wl.name, "global_batch": wl.B, "rows_per_req": wl.R,
+                   "ctx_tokens_mean": float(wl.lengths.mean()), "ctx_tokens_min": int(wl.lengths.min()),
+                   "ctx_tokens_max": int(wl.lengths.max()), "kv_cache": "nvfp4", "index_cache": "nvfp4",
+                   "topk_blocks": wl.topk, "block_tokens": 128, "parallelism": "single-gpu",
+                   "cache_replicas": len(decs), "hip_graph": use_graph},
+        "roofline": {"bound": "hbm", "kernel": "index_nvfp4_kernel (steps 1+2)", "achieved": idx_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"]},
+        "step_hbm": {"algorithmic_bytes": nbytes["total"], "achieved_GBps": step_gbps,
+                     "frac_of_peak": step_gbps / PEAK_HBM_GBPS, "kv_tokens_read": nbytes["kv_tokens"]},
+        "kernel_us": us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

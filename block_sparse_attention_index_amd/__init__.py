@@ -1,0 +1,210 @@
+"""Python binding of the MI355X MSA decode library (``libmsa.so``, include/msa.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI.  PyTorch supplies device memory and streams.  Importing
+this package raises if the HIP library has not been built -- there is no
+CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
+MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
+MSA_TOKEN_MAJOR, MSA_DIM_MAJOR = 0, 1
+PAGE_TOKENS = 128
+HEAD_DIM = 128
+HEADS_PER_GROUP = 8
+NVFP4_SLAB_BYTES = 9216
+F32_SLAB_BYTES = 65536
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_text(status)} ({status})")
+        self.status = status
+
+
+class msa_cache(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("layout", C.c_int32), ("num_heads", C.c_int32), ("num_pages", C.c_int32),
+                ("tensor_scale", C.c_float), ("pages", C.c_void_p)]
+
+
+class msa_batch(C.Structure):
+    _fields_ = [("num_reqs", C.c_int32), ("rows_per_req", C.c_int32), ("max_pages_per_req", C.c_int32),
+                ("shared_prefix_pages", C.c_int32), ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+    P = C.POINTER
+    sigs = {
+        "msa_kv_insert": (C.c_int, [vp, vp, vp, vp, i32, P(msa_cache), P(msa_cache), P(msa_cache), vp]),
+        "msa_kv_insert_nvfp4": (C.c_int, [vp, vp, vp, vp, i32, P(msa_cache), P(msa_cache), P(msa_cache), vp]),
+        "msa_quantize_e4m3": (C.c_int, [vp, i64, f32, vp, vp]),
+        "msa_index_score": (C.c_int, [P(msa_batch), vp, i32, f32, P(msa_cache), vp, vp, vp]),
+        "msa_block_maxpool_topk": (C.c_int, [P(msa_batch), vp, i32, i32, vp, vp, vp]),
+        "msa_decode_workspace_bytes": (sz, [P(msa_batch), i32]),
+        "msa_sparse_decode": (C.c_int, [P(msa_batch), vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp, vp, i32,
+                                        vp, vp, sz, vp]),
+        "msa_select_decode": (C.c_int, [P(msa_batch), vp, i32, vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp,
+                                        vp, vp, vp]),
+        "msa_status_str": (C.c_char_p, [C.c_int]),
+        "msa_debug_dequant": (C.c_int, [P(msa_cache), vp, i32, i32, vp, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    return L
+
+
+lib = _load()
+
+
+def status_text(status: int) -> str:
+    return lib.msa_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MSA_OK:
+        raise MsaError(status, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return int(t)
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MSA library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Cache:
+    """A device page pool for one cache tensor (keys, values or index keys)."""
+
+    def __init__(self, pages: torch.Tensor, dtype: int, layout: int, num_heads: int, num_pages: int,
+                 tensor_scale: float = 1.0):
+        self.pages, self.dtype, self.layout = pages, dtype, layout
+        self.num_heads, self.num_pages, self.tensor_scale = num_heads, num_pages, float(tensor_scale)
+        self.struct = msa_cache(dtype, layout, num_heads, num_pages, self.tensor_scale, pages.data_ptr())
+
+    @staticmethod
+    def slab_bytes(dtype: int) -> int:
+        return F32_SLAB_BYTES if dtype == MSA_F32 else NVFP4_SLAB_BYTES
+
+    @classmethod
+    def empty(cls, dtype: int, layout: int, num_heads: int, num_pages: int, tensor_scale: float = 1.0,
+              device="cuda") -> "Cache":
+        nbytes = num_pages * num_heads * cls.slab_bytes(dtype)
+        pages = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return cls(pages, dtype, layout, num_heads, num_pages, tensor_scale)
+
+    def ref(self):
+        return C.byref(self.struct)
+
+
+class Batch:
+    """Block table and context lengths (device int32) of one decode step."""
+
+    def __init__(self, block_table: torch.Tensor, ctx_lens: torch.Tensor, rows_per_req: int,
+                 shared_prefix_pages: int = 0):
+        assert block_table.dtype == torch.int32 and ctx_lens.dtype == torch.int32
+        self.block_table, self.ctx_lens = block_table, ctx_lens
+        B, P = block_table.shape
+        self.struct = msa_batch(B, rows_per_req, P, shared_prefix_pages, _ptr(block_table), _ptr(ctx_lens))
+
+    def ref(self):
+        return C.byref(self.struct)
+
+    @property
+    def B(self):
+        return self.struct.num_reqs
+
+    @property
+    def R(self):
+        return self.struct.rows_per_req
+
+    @property
+    def max_pages(self):
+        return self.struct.max_pages_per_req
+
+
+def _cref(c):
+    return None if c is None else c.ref()
+
+
+def msa_kv_insert(k, v, idx_k, slot_mapping, k_cache, v_cache, idx_cache, stream=None) -> None:
+    n = slot_mapping.shape[0]
+    _check(lib.msa_kv_insert(_ptr(k), _ptr(v), _ptr(idx_k), _ptr(slot_mapping), n, _cref(k_cache), _cref(v_cache),
+                             _cref(idx_cache), _stream(stream)), "msa_kv_insert")
+
+
+def msa_kv_insert_nvfp4(k, v, idx_k, slot_mapping, k_cache, v_cache, idx_cache, stream=None) -> None:
+    n = slot_mapping.shape[0]
+    _check(lib.msa_kv_insert_nvfp4(_ptr(k), _ptr(v), _ptr(idx_k), _ptr(slot_mapping), n, _cref(k_cache),
+                                   _cref(v_cache), _cref(idx_cache), _stream(stream)), "msa_kv_insert_nvfp4")
+
+
+def msa_quantize_e4m3(x: torch.Tensor, scale: float = 1.0, out: torch.Tensor | None = None, stream=None):
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib.msa_quantize_e4m3(_ptr(x), x.numel(), float(scale), _ptr(out), _stream(stream)), "msa_quantize_e4m3")
+    return out
+
+
+def msa_index_score(batch: Batch, q_idx, q_dtype: int, q_scale: float, idx_cache: Cache, block_scores,
+                    token_scores=None, stream=None) -> None:
+    _check(lib.msa_index_score(batch.ref(), _ptr(q_idx), q_dtype, float(q_scale), idx_cache.ref(),
+                               _ptr(block_scores), _ptr(token_scores), _stream(stream)), "msa_index_score")
+
+
+def msa_block_maxpool_topk(batch: Batch, scores, scores_are_token_level: int, topk: int, sel_blocks, sel_count,
+                           stream=None) -> None:
+    _check(lib.msa_block_maxpool_topk(batch.ref(), _ptr(scores), int(scores_are_token_level), int(topk),
+                                      _ptr(sel_blocks), _ptr(sel_count), _stream(stream)), "msa_block_maxpool_topk")
+
+
+def msa_decode_workspace_bytes(batch: Batch, topk: int) -> int:
+    return int(lib.msa_decode_workspace_bytes(batch.ref(), int(topk)))
+
+
+def msa_sparse_decode(batch: Batch, q, q_dtype: int, q_scale: float, sm_scale: float, k_cache: Cache,
+                      v_cache: Cache, sel_blocks, sel_count, topk: int, out, workspace, stream=None) -> None:
+    _check(lib.msa_sparse_decode(batch.ref(), _ptr(q), q_dtype, float(q_scale), float(sm_scale), k_cache.ref(),
+                                 v_cache.ref(), _ptr(sel_blocks), _ptr(sel_count), int(topk), _ptr(out),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "msa_sparse_decode")
+
+
+def msa_select_decode(batch: Batch, block_scores, topk: int, q, q_dtype: int, q_scale: float, sm_scale: float,
+                      k_cache: Cache, v_cache: Cache, sel_blocks, sel_count, out, stream=None) -> None:
+    _check(lib.msa_select_decode(batch.ref(), _ptr(block_scores), int(topk), _ptr(q), q_dtype, float(q_scale),
+                                 float(sm_scale), k_cache.ref(), v_cache.ref(), _ptr(sel_blocks), _ptr(sel_count),
+                                 _ptr(out), _stream(stream)), "msa_select_decode")
+
+
+def msa_status_str(status: int) -> str:
+    return status_text(status)
+
+
+def msa_debug_dequant(cache: Cache, pages, mode: int, out, stream=None) -> None:
+    _check(lib.msa_debug_dequant(cache.ref(), _ptr(pages), pages.shape[0], int(mode), _ptr(out), _stream(stream)),
+           "msa_debug_dequant")

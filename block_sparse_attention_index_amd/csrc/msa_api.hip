@@ -1,0 +1,171 @@
+// msa_api.hip -- the C ABI declared in include/msa.h: host-side validation of
+// every argument the host can see, then one launcher call per step.  No call
+// allocates, frees, synchronises or keeps state.
+#include <math.h>
+
+#include "msa.h"
+#include "msa_kernels.h"
+
+namespace {
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.0f; }
+
+int check_cache(const msa_cache* c, int want_heads, bool allow_dim_major, bool require_dim_major) {
+  if (!c || !c->pages || c->num_pages < 1 || c->num_heads != want_heads) return MSA_ERR_INVALID_ARG;
+  if (c->dtype != MSA_NVFP4 && c->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
+  if (c->layout != MSA_TOKEN_MAJOR && c->layout != MSA_DIM_MAJOR) return MSA_ERR_INVALID_ARG;
+  if (c->dtype == MSA_F32 && c->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
+  if (c->dtype == MSA_NVFP4) {
+    if (require_dim_major && c->layout != MSA_DIM_MAJOR) return MSA_ERR_UNSUPPORTED;
+    if (!allow_dim_major && c->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
+  }
+  if (!finite_pos(c->tensor_scale)) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+int check_batch(const msa_batch* b) {
+  if (!b || !b->block_table || !b->ctx_lens) return MSA_ERR_INVALID_ARG;
+  if (b->num_reqs < 1 || b->rows_per_req < 1 || b->rows_per_req > MSA_MAX_ROWS || b->max_pages_per_req < 1)
+    return MSA_ERR_INVALID_ARG;
+  if (b->shared_prefix_pages < 0 || b->shared_prefix_pages > b->max_pages_per_req) return MSA_ERR_INVALID_ARG;
+  // grid dimensions: y and z are 16-bit on this hardware
+  if (b->num_reqs > 65535) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+int query_dtype_ok(int32_t q_dtype, const msa_cache* c) {
+  if (c->dtype == MSA_NVFP4) return q_dtype == MSA_FP8_E4M3 ? MSA_OK : MSA_ERR_UNSUPPORTED;
+  return q_dtype == MSA_F32 ? MSA_OK : MSA_ERR_UNSUPPORTED;
+}
+
+int insert_impl(const float* k, const float* v, const float* idx_k, const int64_t* slots, int32_t n,
+                const msa_cache* kc, const msa_cache* vc, const msa_cache* ic, hipStream_t stream, bool nvfp4_only) {
+  if (n < 0 || (n > 0 && !slots)) return MSA_ERR_INVALID_ARG;
+  if (!k && !v && !idx_k) return MSA_ERR_INVALID_ARG;
+  if ((k != nullptr) != (kc != nullptr) || (v != nullptr) != (vc != nullptr) || (idx_k != nullptr) != (ic != nullptr))
+    return MSA_ERR_INVALID_ARG;
+  int st;
+  if (kc && (st = check_cache(kc, 4, false, false)) != MSA_OK) return st;
+  if (vc && (st = check_cache(vc, 4, true, vc->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if (ic && (st = check_cache(ic, 1, false, false)) != MSA_OK) return st;
+  if (nvfp4_only)
+    for (const msa_cache* c : {kc, vc, ic})
+      if (c && c->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (n == 0) return MSA_OK;
+  return msa_launch_kv_insert(k, v, idx_k, slots, n, kc, vc, ic, stream) == 0 ? MSA_OK : MSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_kv_insert(const float* k, const float* v, const float* idx_k, const int64_t* slot_mapping, int32_t n,
+                  const msa_cache* k_cache, const msa_cache* v_cache, const msa_cache* idx_cache,
+                  hipStream_t stream) {
+  return insert_impl(k, v, idx_k, slot_mapping, n, k_cache, v_cache, idx_cache, stream, false);
+}
+
+int msa_kv_insert_nvfp4(const float* k, const float* v, const float* idx_k, const int64_t* slot_mapping,
+                        int32_t n, const msa_cache* k_cache, const msa_cache* v_cache,
+                        const msa_cache* idx_cache, hipStream_t stream) {
+  return insert_impl(k, v, idx_k, slot_mapping, n, k_cache, v_cache, idx_cache, stream, true);
+}
+
+int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!x || !out)) || !finite_pos(scale)) return MSA_ERR_INVALID_ARG;
+  if (n == 0) return MSA_OK;
+  return msa_launch_quantize_e4m3(x, n, scale, out, stream) == 0 ? MSA_OK : MSA_ERR_HIP;
+}
+
+int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, float q_scale,
+                    const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_cache(idx_cache, 1, false, false)) != MSA_OK) return st;
+  if (!q_idx || !block_scores) return MSA_ERR_INVALID_ARG;
+  if ((st = query_dtype_ok(q_dtype, idx_cache)) != MSA_OK) return st;
+  if (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
+  return msa_launch_index_score(batch, q_idx, q_dtype, q_scale, idx_cache, block_scores, token_scores, stream) == 0
+             ? MSA_OK
+             : MSA_ERR_HIP;
+}
+
+int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t scores_are_token_level,
+                           int32_t topk, int32_t* sel_blocks, int32_t* sel_count, hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if (!scores || !sel_blocks || !sel_count) return MSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
+  if (scores_are_token_level != 0 && scores_are_token_level != 1) return MSA_ERR_INVALID_ARG;
+  return msa_launch_topk(batch, scores, scores_are_token_level, topk, sel_blocks, sel_count, stream) == 0
+             ? MSA_OK
+             : MSA_ERR_HIP;
+}
+
+size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk) {
+  if (check_batch(batch) != MSA_OK || topk < 1 || topk > MSA_MAX_TOPK) return 0;
+  return msa_decode_partials_bytes(batch, topk);
+}
+
+int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
+                      const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
+                      const int32_t* sel_count, int32_t topk, float* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if (k_cache->dtype != v_cache->dtype || k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
+  if (!q || !sel_blocks || !sel_count || !out || !workspace) return MSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
+  if ((st = query_dtype_ok(q_dtype, k_cache)) != MSA_OK) return st;
+  if (!finite_pos(sm_scale) || (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale))) return MSA_ERR_INVALID_ARG;
+  if (workspace_bytes < msa_decode_workspace_bytes(batch, topk)) return MSA_ERR_WORKSPACE;
+  return msa_launch_sparse_decode(batch, q, q_dtype, q_scale, sm_scale, k_cache, v_cache, sel_blocks, sel_count,
+                                  topk, out, workspace, stream) == 0
+             ? MSA_OK
+             : MSA_ERR_HIP;
+}
+
+int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t topk, const void* q,
+                      int32_t q_dtype, float q_scale, float sm_scale, const msa_cache* k_cache,
+                      const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,
+                      hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if (k_cache->dtype != MSA_NVFP4 || v_cache->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
+  if (!block_scores || !q || !sel_blocks || !sel_count || !out) return MSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
+  if (q_dtype != MSA_FP8_E4M3) return MSA_ERR_UNSUPPORTED;
+  if (!finite_pos(sm_scale) || !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
+  return msa_launch_select_decode(batch, block_scores, topk, q, q_scale, sm_scale, k_cache, v_cache, sel_blocks,
+                                  sel_count, out, stream) == 0
+             ? MSA_OK
+             : MSA_ERR_HIP;
+}
+
+const char* msa_status_str(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported dtype or layout";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int msa_debug_dequant(const msa_cache* cache, const int32_t* pages, int32_t n_pages, int32_t mode, float* out,
+                      hipStream_t stream) {
+  if (!cache || !cache->pages || cache->num_heads < 1 || cache->num_pages < 1) return MSA_ERR_INVALID_ARG;
+  if (cache->dtype != MSA_NVFP4 && cache->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
+  if (cache->dtype == MSA_F32 && cache->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
+  if (n_pages < 0 || (n_pages > 0 && (!pages || !out)) || (mode != 0 && mode != 1)) return MSA_ERR_INVALID_ARG;
+  if (n_pages == 0) return MSA_OK;
+  return msa_launch_debug_dequant(cache, pages, n_pages, mode, out, stream) == 0 ? MSA_OK : MSA_ERR_HIP;
+}
+
+}  // extern "C"

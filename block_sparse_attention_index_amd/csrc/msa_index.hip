@@ -1,0 +1,279 @@
+// msa_index.hip -- steps 1 and 2: indexer scores fused with the 128-token
+// block max-pool (vLLM M3.1 post, "MiniMax 稀疏注意力的工作原理"; "MiniMax
+// goes sparse", section 1 Step 1).
+//
+// NVFP4 path.  Each step streams the whole index cache (72 B per token), so
+// the kernel is an HBM-bound scan; the dot products run on the matrix cores
+// so that the vector ALUs are left with a handful of operations per token.
+// The E2M1 codes are fed to v_mfma_scale_f32_16x16x128_f8f6f4 as they sit in
+// memory (B operand, FP4) against the FP8 index queries (A operand), with
+// the per-16 E4M3 scales applied after the product, once per partial result
+// -- the "scale once per MMA result" idea of the post's Rubin section, which
+// keeps the scores exact in the operands (no FP8 re-rounding of the keys).
+// To keep the sixteen-element groups apart, A row (g, j) holds query g only
+// on group j's sixteen dims and zeros elsewhere; two MFMAs per 16 tokens then
+// give all 8 group partials of 4 queries.  The operand pairing of this
+// instruction (measured on gfx950): the fp4 operand lane group c (lanes
+// 16c..16c+15) carries dims 32c..32c+31 of its column (nibble e = dim
+// 32c + e); the fp8 operand lane group c, byte e pairs with dim
+// 64*(e/16) + 16c + e%16, so each 16-byte half of an A lane is one scale group
+// (j = c for bytes 0..15, j = 4 + c for bytes 16..31).
+// Output lane l holds rows 4*(l/16)+q: with row (g, q) -> group g = l/16 and
+// j = q (first MFMA) or 4 + q (second), and column l%16 = token.  So lane l
+// ends with the complete score of (group l/16, token l%16) after 8 FMAs, and
+// the block max is a 16-lane row reduction.
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+// One page of the index cache as one wave holds it: lane l keeps, for each
+// 16-token chunk c, the 16 code bytes of token 16c + l%16, dims
+// 32*(l/16)..+31 (the fp4 operand), and the 8 scale bytes of that token.
+struct PageRegs {
+  uint4 cw[8];
+  uint2 sw[8];
+};
+
+// NT: non-temporal loads (the index is read once per step; streaming hint).
+template <bool NT>
+__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ slab, int col, int grp) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u4* cp = reinterpret_cast<const u4*>(slab + (16 * c + col) * 64 + 16 * grp);
+    const u2* sp = reinterpret_cast<const u2*>(slab + kScaleOff + (16 * c + col) * 8);
+    const u4 cv = NT ? __builtin_nontemporal_load(cp) : *cp;
+    const u2 sv = NT ? __builtin_nontemporal_load(sp) : *sp;
+    pr.cw[c] = make_uint4(cv.x, cv.y, cv.z, cv.w);
+    pr.sw[c] = make_uint2(sv.x, sv.y);
+  }
+}
+
+// Scores of one resident page for all R rows; returns per-row maxima (unscaled).
+template <int R, bool kTok>
+__device__ __forceinline__ void score_page(const PageRegs& pr, const v8i (&A)[R][2], const int (&pos_lim)[R], int j,
+                                           int b, int grp, int col, float out_scale, int64_t T,
+                                           float* __restrict__ token_scores, float (&m)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) m[r] = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const v8i Bop = v8i{(int)pr.cw[c].x, (int)pr.cw[c].y, (int)pr.cw[c].z, (int)pr.cw[c].w, 0, 0, 0, 0};
+    float s[8];
+    {
+      auto s01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pr.sw[c].x, false);
+      auto s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pr.sw[c].x, true);
+      auto s45 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pr.sw[c].y, false);
+      auto s67 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pr.sw[c].y, true);
+      s[0] = s01[0]; s[1] = s01[1]; s[2] = s23[0]; s[3] = s23[1];
+      s[4] = s45[0]; s[5] = s45[1]; s[6] = s67[0]; s[7] = s67[1];
+    }
+    const int t = j * kPage + 16 * c + col;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      const v4f d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[r][0], Bop, z, 0, 4, 0, 127, 0, 127);
+      const v4f d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[r][1], Bop, z, 0, 4, 0, 127, 0, 127);
+      float sc = s[0] * d0[0];
+      sc = fmaf(s[1], d0[1], sc);
+      sc = fmaf(s[2], d0[2], sc);
+      sc = fmaf(s[3], d0[3], sc);
+      sc = fmaf(s[4], d1[0], sc);
+      sc = fmaf(s[5], d1[1], sc);
+      sc = fmaf(s[6], d1[2], sc);
+      sc = fmaf(s[7], d1[3], sc);
+      const bool vis = t <= pos_lim[r];
+      if (kTok)
+        token_scores[(((int64_t)b * R + r) * kGroups + grp) * T + t] = vis ? sc * out_scale : -__builtin_inff();
+      if (vis) m[r] = fmaxf(m[r], sc);
+    }
+  }
+}
+
+// Pages [j0, j0 + PPW) of request b per wave; with PREFETCH the next page's
+// loads are issued before the current page is scored (register double buffer).
+template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_nvfp4_kernel(const int32_t* __restrict__ table,
+                                                          const int32_t* __restrict__ lens, int32_t max_pages,
+                                                          const uint8_t* __restrict__ q_idx, float out_scale,
+                                                          const uint8_t* __restrict__ pages, int32_t num_pages,
+                                                          float* __restrict__ block_scores,
+                                                          float* __restrict__ token_scores) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int j0 = (blockIdx.x * 4 + wave) * PPW;
+  if (j0 >= max_pages) return;
+  const int L = clamp_len(lens[b], max_pages);
+  const int npb = (L + kPage - 1) / kPage;
+  const int j1 = min(j0 + PPW, max_pages);
+  const int grp = lane >> 4;  // this lane's query group (output) and fp4 lane group
+  const int col = lane & 15;  // token within a 16-token chunk
+  const int64_t T = (int64_t)max_pages * kPage;
+
+  // physical pages of this wave, one per lane, then broadcast
+  int my_phys = -1;
+  if (lane < PPW && j0 + lane < npb) {
+    my_phys = table[(int64_t)b * max_pages + j0 + lane];
+    if (my_phys >= num_pages) my_phys = -1;
+  }
+
+  // A operands: queries of row r masked to one scale group per MFMA row.
+  v8i A[R][2];
+  {
+    const int i = lane & 15;
+    const int gq = i >> 2, jj = i & 3;
+    const bool on = (jj == grp);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* q = q_idx + (((int64_t)b * R + r) * kGroups + gq) * kDim;
+      uint4 lo = on ? *reinterpret_cast<const uint4*>(q + 16 * grp) : make_uint4(0, 0, 0, 0);
+      uint4 hi = on ? *reinterpret_cast<const uint4*>(q + 64 + 16 * grp) : make_uint4(0, 0, 0, 0);
+      A[r][0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+      A[r][1] = v8i{0, 0, 0, 0, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  }
+  int pos_lim[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) pos_lim[r] = L - R + r;
+
+  auto finish = [&](int j, const float (&m)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float mm = wave_max16(m[r]);
+      if (col == 0) block_scores[(((int64_t)b * R + r) * kGroups + grp) * max_pages + j] = mm * out_scale;
+    }
+  };
+  auto empty_page = [&](int j) {
+    float m[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) m[r] = -__builtin_inff();
+    if (kTok)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        for (int c = 0; c < 8; ++c)
+          token_scores[(((int64_t)b * R + r) * kGroups + grp) * T + j * kPage + 16 * c + col] = -__builtin_inff();
+    finish(j, m);
+  };
+
+  PageRegs buf[PREFETCH ? 2 : 1];
+  int phys_cur = __shfl(my_phys, 0);
+  if (PREFETCH && phys_cur >= 0) load_page<NT>(buf[0], pages + (int64_t)phys_cur * kNvSlab, col, grp);
+#pragma unroll
+  for (int k = 0; k < PPW; ++k) {
+    const int j = j0 + k;
+    if (j >= j1) break;
+    PageRegs& cur = buf[PREFETCH ? (k & 1) : 0];
+    const int phys_next = (k + 1 < PPW) ? __shfl(my_phys, k + 1) : -1;
+    if (!PREFETCH && phys_cur >= 0) load_page<NT>(cur, pages + (int64_t)phys_cur * kNvSlab, col, grp);
+    if (PREFETCH && phys_next >= 0 && j + 1 < j1)
+      load_page<NT>(buf[(k + 1) & 1], pages + (int64_t)phys_next * kNvSlab, col, grp);
+    if (phys_cur >= 0) {
+      float m[R];
+      score_page<R, kTok>(cur, A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
+      finish(j, m);
+    } else {
+      empty_page(j);
+    }
+    phys_cur = phys_next;
+  }
+}
+
+// F32 cache, F32 queries: one workgroup per (page, request), one thread per token.
+template <bool kTok>
+__global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restrict__ table,
+                                                        const int32_t* __restrict__ lens, int32_t max_pages,
+                                                        int32_t R, const float* __restrict__ q_idx,
+                                                        const uint8_t* __restrict__ pages, int32_t num_pages,
+                                                        float* __restrict__ block_scores,
+                                                        float* __restrict__ token_scores) {
+  __shared__ float qs[MSA_MAX_ROWS * kGroups * kDim];
+  __shared__ float red[2][MSA_MAX_ROWS * kGroups];
+  const int j = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int L = clamp_len(lens[b], max_pages);
+  const int npb = (L + kPage - 1) / kPage;
+  for (int i = t; i < R * kGroups * kDim; i += 128) qs[i] = q_idx[(int64_t)b * R * kGroups * kDim + i];
+  __syncthreads();
+  const int phys = j < npb ? table[(int64_t)b * max_pages + j] : -1;
+  const bool ok = phys >= 0 && phys < num_pages;
+  const float* krow = ok ? reinterpret_cast<const float*>(pages + (int64_t)phys * kF32Slab) + t * kDim : nullptr;
+  const int64_t T = (int64_t)max_pages * kPage;
+  const int pos = j * kPage + t;
+  for (int rg = 0; rg < R * kGroups; ++rg) {
+    const int r = rg / kGroups;
+    float s = -__builtin_inff();
+    if (ok && pos <= L - R + r) {
+      s = 0.f;
+      const float* q = qs + rg * kDim;
+      for (int d = 0; d < kDim; ++d) s = fmaf(q[d], krow[d], s);
+    }
+    if (kTok) token_scores[((int64_t)b * R * kGroups + rg) * T + pos] = s;
+    float m = s;
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) red[t >> 6][rg] = m;
+  }
+  __syncthreads();
+  for (int rg = t; rg < R * kGroups; rg += 128)
+    block_scores[((int64_t)b * R * kGroups + rg) * max_pages + j] = fmaxf(red[0][rg], red[1][rg]);
+}
+
+template <int R, int PPW, bool PREFETCH, bool NT, int WPE>
+static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                             float* ts, hipStream_t s) {
+  dim3 grid((bt->max_pages_per_req + 4 * PPW - 1) / (4 * PPW), bt->num_reqs);
+  if (ts)
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages,
+                       bs, ts);
+  else
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE>), grid, dim3(256), 0, s,
+                       bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts);
+}
+
+// One page per wave, non-temporal (streaming) loads, and an occupancy target
+// of WPE waves per SIMD: measured best on the 128K-context shapes (the
+// streaming hint alone is worth ~12%; many short waves balance the ragged
+// contexts better than a deeper per-wave pipeline).
+template <int R>
+static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                         float* ts, hipStream_t s) {
+  launch_nvfp4_cfg<R, 1, false, true, (R <= 2 ? 4 : (R <= 4 ? 3 : 2))>(bt, q, out_scale, ic, bs, ts, s);
+}
+
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" int msa_launch_index_score(const msa_batch* bt, const void* q_idx, int32_t q_dtype, float q_scale,
+                                      const msa_cache* ic, float* block_scores, float* token_scores,
+                                      hipStream_t s) {
+  if (ic->dtype == MSA_F32) {
+    dim3 grid(bt->max_pages_per_req, bt->num_reqs);
+    if (token_scores)
+      hipLaunchKernelGGL(index_f32_kernel<true>, grid, dim3(128), 0, s, bt->block_table, bt->ctx_lens,
+                         bt->max_pages_per_req, bt->rows_per_req, (const float*)q_idx, (const uint8_t*)ic->pages,
+                         ic->num_pages, block_scores, token_scores);
+    else
+      hipLaunchKernelGGL(index_f32_kernel<false>, grid, dim3(128), 0, s, bt->block_table, bt->ctx_lens,
+                         bt->max_pages_per_req, bt->rows_per_req, (const float*)q_idx, (const uint8_t*)ic->pages,
+                         ic->num_pages, block_scores, token_scores);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  const float out_scale = ic->tensor_scale * q_scale;
+  const uint8_t* q = (const uint8_t*)q_idx;
+  switch (bt->rows_per_req) {
+    case 1: launch_nvfp4<1>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 2: launch_nvfp4<2>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 3: launch_nvfp4<3>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 4: launch_nvfp4<4>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 5: launch_nvfp4<5>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 6: launch_nvfp4<6>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 7: launch_nvfp4<7>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    case 8: launch_nvfp4<8>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

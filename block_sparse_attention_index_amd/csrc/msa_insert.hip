@@ -1,0 +1,231 @@
+// msa_insert.hip -- step 0 (cache insert with NVFP4 quantisation), the FP8
+// query quantiser and the dequantisation test aid.
+//
+// Insert: one thread per (token, cache head, 16-dim group).  Each thread
+// reads its 16 FP32 values (four 16-byte loads), derives the E4M3 group
+// scale and the sixteen E2M1 codes with the amax recipe below (every step an
+// FP32 operation with round-to-nearest-even, no contraction), and writes
+// them into the page slab of the token's slot.  Token-major slabs take the 8
+// code bytes as one 64-bit store; dim-major (value) slabs hold the codes of 8
+// consecutive tokens of one dim in a dword, so each nibble is replaced with
+// an atomic AND then OR (vector memory atomics, no read round trip) --
+// tokens inserted together may share that dword.
+#pragma clang fp contract(off)
+
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+// Quantise 16 FP32 values: returns the E4M3 scale code, codes packed 2 per
+// byte (element 2i in the low nibble of byte i) in the 64-bit word.
+__device__ __forceinline__ uint32_t nvfp4_group(const float* x, float ts, uint64_t* packed) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  float t1 = amax / 6.0f;
+  float s32 = t1 / ts;
+  uint32_t sc = e4m3_encode(s32);
+  float sv = e4m3_to_f32(sc);
+  uint64_t out = 0;
+  if (sv != 0.0f) {
+    float denom = sv * ts;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float y = x[i] / denom;
+      uint32_t c = e2m1_mag(fabsf(y)) | ((__float_as_uint(x[i]) >> 28) & 0x8u);
+      out |= (uint64_t)c << (4 * i);
+    }
+  }
+  *packed = out;
+  return sc;
+}
+
+// Up to three target caches (keys, values, index keys), passed as scalars so
+// that choosing one per thread is a register select, not a memory load.
+struct InsertArgs {
+  uint8_t* pages0;
+  uint8_t* pages1;
+  uint8_t* pages2;
+  const float* src0;
+  const float* src1;
+  const float* src2;
+  int32_t np0, np1, np2;     // page-pool sizes
+  int32_t h0, h1, h2;        // heads
+  int32_t nv0, nv1, nv2;     // 1 = NVFP4, 0 = F32
+  int32_t dm0, dm1, dm2;     // 1 = dim-major slab
+  float ts0, ts1, ts2;       // tensor scales
+  int32_t u0, u1, u2;        // 16-dim groups per token (heads * 8), 0 if absent
+};
+
+__global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int64_t* __restrict__ slots, int32_t n) {
+  const int32_t units = A.u0 + A.u1 + A.u2;  // 16-dim groups per token over all caches
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)n * units) return;
+  const int32_t tok = (int32_t)(gid / units);
+  int32_t u = (int32_t)(gid - (int64_t)tok * units);
+  const int c = u < A.u0 ? 0 : (u < A.u0 + A.u1 ? 1 : 2);
+  u -= c == 0 ? 0 : (c == 1 ? A.u0 : A.u0 + A.u1);
+  uint8_t* pages = c == 0 ? A.pages0 : (c == 1 ? A.pages1 : A.pages2);
+  const float* src = c == 0 ? A.src0 : (c == 1 ? A.src1 : A.src2);
+  const int32_t num_pages = c == 0 ? A.np0 : (c == 1 ? A.np1 : A.np2);
+  const int32_t heads = c == 0 ? A.h0 : (c == 1 ? A.h1 : A.h2);
+  const int32_t nvfp4 = c == 0 ? A.nv0 : (c == 1 ? A.nv1 : A.nv2);
+  const int32_t dim_major = c == 0 ? A.dm0 : (c == 1 ? A.dm1 : A.dm2);
+  const float ts = c == 0 ? A.ts0 : (c == 1 ? A.ts1 : A.ts2);
+  const int head = u >> 3, grp = u & 7;
+
+  // Both loads go out before anything waits on them: an invalid slot only
+  // predicates the stores (an early return would let the compiler sink the
+  // row loads behind the slot load).
+  const int64_t slot = slots[tok];
+  const float4* src4 = reinterpret_cast<const float4*>(src + ((int64_t)tok * heads + head) * kDim + grp * 16);
+  float4 f[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = src4[i];
+  const bool valid = slot >= 0 && slot < (int64_t)num_pages * kPage;
+  const int64_t page = valid ? slot >> 7 : 0;
+  const int off = (int)(slot & 127);
+  if (!nvfp4) {
+    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(pages + (page * heads + head) * (int64_t)kF32Slab) +
+                                            off * kDim + grp * 16);
+    if (valid)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = f[i];
+    return;
+  }
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[4 * i] = f[i].x;
+    x[4 * i + 1] = f[i].y;
+    x[4 * i + 2] = f[i].z;
+    x[4 * i + 3] = f[i].w;
+  }
+  uint64_t packed;
+  const uint32_t sc = nvfp4_group(x, ts, &packed);
+  uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
+  if (!valid) return;
+  if (!dim_major) {
+    *reinterpret_cast<uint64_t*>(slab + off * 64 + grp * 8) = packed;
+    slab[kScaleOff + off * 8 + grp] = (uint8_t)sc;
+  } else {
+    // Clear this token's nibble, then set it: atomic AND / OR on the dword
+    // (fire-and-forget); the other 7 tokens of the dword may be written by
+    // other threads at the same time.
+    const unsigned int sh = 4u * (unsigned)(off & 7);
+    const unsigned int keep = ~(0xFu << sh);
+    unsigned int* words = reinterpret_cast<unsigned int*>(slab + grp * 16 * 64 + (off >> 3) * 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const unsigned int cd = (unsigned int)(packed >> (4 * i)) & 0xFu;
+      atomicAnd(words + i * 16, keep);
+      atomicOr(words + i * 16, cd << sh);
+    }
+    slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
+  }
+}
+
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* __restrict__ x, int64_t n, float scale,
+                                                            uint8_t* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)e4m3_encode(x[i] / scale);
+}
+
+// One thread per (page, head, token, 8-dim chunk): decodes 8 elements.
+__global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __restrict__ pages, int32_t num_pages,
+                                                            int32_t heads, int32_t nvfp4, int32_t dim_major,
+                                                            float ts, const int32_t* __restrict__ page_ids,
+                                                            int32_t n_pages, int32_t mode, float* __restrict__ out) {
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t total = (int64_t)n_pages * heads * kPage * (kDim / 8);
+  if (gid >= total) return;
+  int chunk = (int)(gid % (kDim / 8));
+  int t = (int)((gid / (kDim / 8)) % kPage);
+  int head = (int)((gid / (kDim / 8 * kPage)) % heads);
+  int i = (int)(gid / ((int64_t)kDim / 8 * kPage * heads));
+  int64_t page = page_ids[i];
+  float* o = out + (((int64_t)i * heads + head) * kPage + t) * kDim + chunk * 8;
+  if (page < 0 || page >= num_pages) {
+    for (int e = 0; e < 8; ++e) o[e] = __builtin_nanf("");
+    return;
+  }
+  if (!nvfp4) {
+    const float* s = reinterpret_cast<const float*>(pages + (page * heads + head) * (int64_t)kF32Slab) + t * kDim;
+    for (int e = 0; e < 8; ++e) o[e] = s[chunk * 8 + e];
+    return;
+  }
+  const uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
+  uint32_t codes = 0;  // 8 nibbles, dim chunk*8 + e at nibble e
+  uint8_t sc;
+  if (!dim_major) {
+    codes = *reinterpret_cast<const uint32_t*>(slab + t * 64 + chunk * 4);
+    sc = slab[kScaleOff + t * 8 + chunk / 2];
+  } else {
+    for (int e = 0; e < 8; ++e) {
+      int d = chunk * 8 + e;
+      uint32_t byte = slab[d * 64 + t / 2];
+      codes |= ((byte >> (4 * (t & 1))) & 0xFu) << (4 * e);
+    }
+    sc = slab[kScaleOff + (chunk / 2) * 128 + t];
+  }
+  h8 c = e2m1x8_to_h8(codes);
+  if (mode == 0) {
+    float s = e4m3_to_f32(sc);
+    for (int e = 0; e < 8; ++e) o[e] = ((float)c[e] * s) * ts;
+  } else {
+    h2 s2 = e4m3x2_to_h2<false>((uint32_t)sc | ((uint32_t)sc << 8));
+    for (int e = 0; e < 8; ++e) {
+      _Float16 v = c[e] * s2[0];  // exact in FP16
+      o[e] = (float)v * ts;
+    }
+  }
+}
+
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" int msa_launch_kv_insert(const float* k, const float* v, const float* idx_k, const int64_t* slots,
+                                    int32_t n, const msa_cache* kc, const msa_cache* vc, const msa_cache* ic,
+                                    hipStream_t stream) {
+  InsertArgs A{};
+  auto fill = [](const msa_cache* c, const float* src, uint8_t*& pg, const float*& s, int32_t& np, int32_t& h,
+                 int32_t& nv, int32_t& dm, float& ts, int32_t& u) {
+    if (!c || !src) return;
+    pg = (uint8_t*)c->pages;
+    s = src;
+    np = c->num_pages;
+    h = c->num_heads;
+    nv = c->dtype == MSA_NVFP4;
+    dm = c->layout == MSA_DIM_MAJOR;
+    ts = c->tensor_scale;
+    u = c->num_heads * 8;
+  };
+  fill(kc, k, A.pages0, A.src0, A.np0, A.h0, A.nv0, A.dm0, A.ts0, A.u0);
+  fill(vc, v, A.pages1, A.src1, A.np1, A.h1, A.nv1, A.dm1, A.ts1, A.u1);
+  fill(ic, idx_k, A.pages2, A.src2, A.np2, A.h2, A.nv2, A.dm2, A.ts2, A.u2);
+  const int64_t total = (int64_t)n * (A.u0 + A.u1 + A.u2);
+  if (total == 0) return 0;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(kv_insert_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A, slots, n);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+extern "C" int msa_launch_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream) {
+  if (n == 0) return 0;
+  int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(quantize_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, scale, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+extern "C" int msa_launch_debug_dequant(const msa_cache* c, const int32_t* pages, int32_t n_pages, int32_t mode,
+                                        float* out, hipStream_t stream) {
+  int64_t total = (int64_t)n_pages * c->num_heads * kPage * (kDim / 8);
+  if (total == 0) return 0;
+  int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint8_t*)c->pages,
+                     c->num_pages, c->num_heads, (int32_t)(c->dtype == MSA_NVFP4),
+                     (int32_t)(c->layout == MSA_DIM_MAJOR), c->tensor_scale, pages, n_pages, mode, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

@@ -1,0 +1,132 @@
+// msa_select.h -- step 3 on one wave: top-k block selection with the latest
+// block kept (vLLM M3.1 post, "MiniMax 稀疏注意力的工作原理"; "MiniMax goes
+// sparse", section 1 Step 1, TopK per layer and GQA group).  Used by the
+// selection kernel and by the fused selection + attention kernel.
+//
+// Each candidate block becomes a 64-bit key: the order-preserving image of
+// its FP32 score in the high word (-0 folded onto +0, NaN below every
+// number) and 0xFFFFFFFF - j in the low word, so the larger key is the better
+// block and equal scores go to the lower block index.  topk-1 rounds of a
+// wave-wide argmax pick the best blocks other than the latest.
+//
+// Each lane keeps its candidates' keys in registers (KMAX per lane, blocks
+// lane, lane+64, ...; KMAX = 0 reads them from memory when needed, for very
+// long contexts) and a sorted list of its own best 3.  A round takes the
+// wave-wide max of the list heads -- one 32-bit DPP max of the score words
+// and a ballot; a second reduction of the index words runs only when several
+// heads carry the same score -- and the winning lane pops its head.  A lane
+// whose list runs dry refills it from its keys below the key it just gave up
+// (keys are distinct, so "below the last winner" is exactly "not yet
+// selected").
+#pragma once
+
+#include "msa_device.h"
+
+namespace msa {
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (f == f) ? k : 0u;  // NaN ranks below -inf
+}
+
+template <bool kTok>
+__device__ __forceinline__ float block_score(const float* __restrict__ row, int j, int pos_lim) {
+  if (!kTok) return row[j];
+  float m = -__builtin_inff();
+  const int hi = min(kPage - 1, pos_lim - j * kPage);
+  for (int t = 0; t <= hi; ++t) m = fmaxf(m, row[j * kPage + t]);
+  return m;
+}
+
+// Insert key k into a descending top-3 list (0 = empty slot).
+__device__ __forceinline__ void top3_insert(uint64_t k, uint64_t& t0, uint64_t& t1, uint64_t& t2) {
+  const bool g0 = k > t0, g1 = k > t1, g2 = k > t2;
+  t2 = g1 ? t1 : (g2 ? k : t2);
+  t1 = g0 ? t0 : (g1 ? k : t1);
+  t0 = g0 ? k : t0;
+}
+
+// Selection of one (request, row, group) by one whole wave.  `row` holds the
+// block scores (or token scores when kTok) of the row; p is the row's
+// position; n = number of blocks it sees.  Calls emit(rank, id) once for each
+// selected block (rank = position in ascending order) from the lane that
+// holds it, and returns the count.
+template <bool kTok, int KMAX, typename Emit>
+__device__ __forceinline__ int select_row(const float* __restrict__ row, int n, int p, int topk, int lane,
+                                          Emit emit) {
+  if (n <= topk) {
+    if (lane < n) emit(lane, lane);
+    return n;
+  }
+  const int latest = n - 1;
+  auto key_of = [&](int j, float sc) {
+    return ((uint64_t)order_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+  };
+  uint64_t keys[KMAX > 0 ? KMAX : 1];
+  uint64_t t0 = 0, t1 = 0, t2 = 0;
+  if (KMAX > 0) {
+    // all loads unconditional (index clamped into the row) so they issue back to back;
+    // candidates past the latest block are masked to key 0 afterwards
+    float sc[KMAX > 0 ? KMAX : 1];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) sc[i] = block_score<kTok>(row, min(lane + 64 * i, latest - 1), p);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      const int j = lane + 64 * i;
+      keys[i] = j < latest ? key_of(j, sc[i]) : 0ull;
+      top3_insert(keys[i], t0, t1, t2);
+    }
+  } else {
+    for (int j = lane; j < latest; j += 64) top3_insert(key_of(j, block_score<kTok>(row, j, p)), t0, t1, t2);
+  }
+  int mine = -1;  // the block this lane ends up holding in the output set
+  for (int k = 0; k < topk - 1; ++k) {
+    const uint32_t hi = (uint32_t)(t0 >> 32);
+    const uint32_t H = wave_umax(hi);
+    const uint64_t tied = __ballot(hi == H);
+    int wl;
+    if (__popcll(tied) == 1) {
+      wl = __ffsll((unsigned long long)tied) - 1;
+    } else {  // equal scores: the lower block index (larger low word) wins
+      const uint32_t Lo = wave_umax(hi == H ? (uint32_t)t0 : 0u);
+      wl = (int)((0xFFFFFFFFu - Lo) & 63u);
+    }
+    const uint64_t W = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(t0 >> 32), wl) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)t0, wl);
+    if (lane == k) mine = (int)(0xFFFFFFFFu - (uint32_t)W);
+    if (lane == wl) {
+      t0 = t1;
+      t1 = t2;
+      t2 = 0;
+      if (t0 == 0) {  // list ran dry: refill from this lane's keys below W
+        if (KMAX > 0) {
+#pragma unroll
+          for (int i = 0; i < KMAX; ++i)
+            if (keys[i] < W) top3_insert(keys[i], t0, t1, t2);
+        } else {
+          for (int j = lane; j < latest; j += 64) {
+            const uint64_t kk = key_of(j, block_score<kTok>(row, j, p));
+            if (kk < W) top3_insert(kk, t0, t1, t2);
+          }
+        }
+      }
+    }
+  }
+  if (lane == topk - 1) mine = latest;
+  // rank of each held id among the held ids (ids are distinct)
+  int rank = 0;
+  for (int i = 0; i < topk; ++i) {
+    const int other = __builtin_amdgcn_readlane(mine, i);
+    rank += (lane < topk && other < mine) ? 1 : 0;
+  }
+  if (lane < topk) emit(rank, mine);
+  return topk;
+}
+
+// Register capacity (candidates per lane) for a block-table width.
+__host__ __device__ constexpr int select_kmax(int max_pages) {
+  return max_pages <= 64 * 8 ? 8 : (max_pages <= 64 * 24 ? 24 : (max_pages <= 64 * 48 ? 48 : 0));
+}
+
+}  // namespace msa

@@ -1,0 +1,208 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MiniMax Sparse Attention decode path.
+ *
+ * The method (cited by page title and section):
+ *  - vLLM's MiniMax-M3.1-Flash day-0 post, Chinese edition (agentlenshq.com),
+ *    section "MiniMax 稀疏注意力的工作原理" (how MSA works): the KV cache is cut
+ *    into 128-token blocks; a lightweight indexer scores every cached key
+ *    with one index query per GQA group against a single shared index-key
+ *    head; scores are max-pooled to one per block; exact attention runs only
+ *    over the top-16 blocks, the latest block always kept, so each query
+ *    sees at most 2,048 keys.
+ *  - the same post, "MiniMax-M3.1 架构的变化": the KV cache (keys, values and
+ *    index keys) is NVFP4; "NVIDIA Blackwell MSA 内核优化": queries stay FP8;
+ *    "通过查表实现的 NVFP4 MSA 内核": E4M3 scales and E2M1 magnitudes.
+ *  - "MiniMax goes sparse" (atlascloud.ai), section 1, Step 1 (index branch,
+ *    block max pool, TopK per layer and GQA group) and Step 2 (every query
+ *    head of a group attends to the group's blocks).
+ *  - The spke.com Japanese rendering of the vLLM post, section "MSA入門", says
+ *    the same as the first bullet.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns
+ *    every buffer (inputs, outputs, workspaces); the library keeps no state,
+ *    allocates nothing and never synchronises.  Calls are asynchronous on
+ *    `stream` and may be captured into a HIP graph (no memset nodes).
+ *  - Host-side argument errors return a negative msa_status synchronously
+ *    and launch nothing.  A failed launch returns MSA_ERR_HIP.
+ *  - Device data the host cannot see (block tables, context lengths, slot
+ *    mappings) is read defensively: a context length above
+ *    max_pages_per_req*128 is clamped, a page id outside [0, num_pages) makes
+ *    that page read as masked and a slot outside the pool is skipped.  Results
+ *    for such inputs are unspecified but no access leaves the buffers.
+ *  - Batch semantics: request b has ctx_lens[b] = L_b cached tokens, its R
+ *    new query rows included; row r sits at position p = L_b - R + r and
+ *    sees tokens 0..p.  Logical block j of request b is the physical page
+ *    block_table[b * max_pages_per_req + j]; page = selection block = 128
+ *    tokens.  Rows with p < 0 see nothing.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape           */
+  MSA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, layout)  */
+  MSA_ERR_WORKSPACE = -3,   /* workspace smaller than the size query says */
+  MSA_ERR_HIP = -4          /* a HIP launch or runtime call failed        */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_FP8_E4M3 = 1, MSA_NVFP4 = 2 } msa_dtype;
+
+typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1 } msa_layout;
+
+#define MSA_PAGE_TOKENS 128
+#define MSA_HEAD_DIM 128
+#define MSA_HEADS_PER_GROUP 8
+#define MSA_MAX_ROWS 8
+#define MSA_MAX_TOPK 64
+#define MSA_NVFP4_GROUP 16
+#define MSA_NVFP4_SLAB_BYTES 9216
+#define MSA_F32_SLAB_BYTES 65536
+
+/*
+ * One paged cache tensor of one layer.  Page p, head h is the slab at
+ * pages + (p * num_heads + h) * slab_bytes.  Slab layouts:
+ *   MSA_F32 (token-major only): float [128 tokens][128 dims], 65,536 B.
+ *   MSA_NVFP4, 9,216 B per slab.  Element value = (e2m1 * e4m3_scale) *
+ *   tensor_scale; one E4M3 scale per 16 consecutive dims of a token (the
+ *   block size that the pages' 34,560-vs-61,440 B per token fixes).
+ *     MSA_TOKEN_MAJOR (keys, index keys): codes [128 tokens][64 B] (byte i of
+ *       a token holds dim 2i in its low nibble, 2i+1 in its high nibble),
+ *       then scales [128 tokens][8 B] (byte j: dims 16j..16j+15).
+ *     MSA_DIM_MAJOR (values): codes [128 dims][64 B] (byte i of a dim holds
+ *       token 2i in its low nibble, 2i+1 in its high nibble), then scales
+ *       [8 groups][128 tokens].  Same quantisation groups as token-major; the
+ *       bytes are placed so that the attention kernel's P.V matrix-core
+ *       operand reads 8 consecutive tokens of one dim as one dword.
+ * Keys and index keys must be MSA_TOKEN_MAJOR, values MSA_DIM_MAJOR when
+ * NVFP4 (MSA_TOKEN_MAJOR when F32).  tensor_scale must be finite and > 0.
+ */
+typedef struct {
+  int32_t dtype;      /* msa_dtype: MSA_NVFP4 or MSA_F32                  */
+  int32_t layout;     /* msa_layout                                        */
+  int32_t num_heads;  /* 4 for keys and values, 1 for index keys           */
+  int32_t num_pages;  /* physical page pool size (>= 1)                    */
+  float tensor_scale; /* per-tensor FP32 scale of an NVFP4 cache; 1 for F32 */
+  void* pages;        /* device, num_pages * num_heads * slab bytes        */
+} msa_cache;
+
+/* One decode step's batch (the struct itself is host memory). */
+typedef struct {
+  int32_t num_reqs;            /* B >= 1                                        */
+  int32_t rows_per_req;        /* R in 1..MSA_MAX_ROWS (speculative rows)       */
+  int32_t max_pages_per_req;   /* row stride of block_table (>= 1)              */
+  int32_t shared_prefix_pages; /* leading pages identical in every row (hint), 0 if none */
+  const int32_t* block_table;  /* device [B][max_pages_per_req] physical page ids */
+  const int32_t* ctx_lens;     /* device [B] L_b, new rows included              */
+} msa_batch;
+
+/*
+ * Step 0: write n new tokens into the caches.  k, v: [n][4][128] FP32,
+ * idx_k: [n][128] FP32, slot_mapping: [n] slot = page * 128 + offset, slots
+ * distinct.  Any of k / v / idx_k may be NULL (with its cache NULL) to skip
+ * that cache.  NVFP4 quantisation of each 16-dim group, FP32 round-to-
+ * nearest-even at every step (the pages state no recipe; this amax recipe is
+ * the reading taken): s = E4M3_sat((amax/6)/tensor_scale); s == 0 -> all
+ * codes +0; else code_i = sign(x_i) | E2M1_sat(|x_i / (s*tensor_scale)|).
+ * F32 caches store the values unchanged.  The pages fuse this into the QKV
+ * GEMM epilogue (vLLM post, "QKV GEMM + norm + RoPE + KV 插入融合"); here it
+ * is a kernel of its own.
+ */
+int msa_kv_insert(const float* k, const float* v, const float* idx_k, const int64_t* slot_mapping, int32_t n,
+                  const msa_cache* k_cache, const msa_cache* v_cache, const msa_cache* idx_cache,
+                  hipStream_t stream);
+
+/* Same as msa_kv_insert, restricted to NVFP4 caches (MSA_ERR_UNSUPPORTED otherwise). */
+int msa_kv_insert_nvfp4(const float* k, const float* v, const float* idx_k, const int64_t* slot_mapping,
+                        int32_t n, const msa_cache* k_cache, const msa_cache* v_cache,
+                        const msa_cache* idx_cache, hipStream_t stream);
+
+/* FP32 -> FP8 E4M3 (OCP) query bytes: out[i] = E4M3_sat_RNE(x[i] / scale), NaN -> 0x7F|sign.
+ * Queries stay FP8 while the cache is NVFP4 (vLLM post, Blackwell section). scale > 0. */
+int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream);
+
+/*
+ * Steps 1+2: indexer scores and 128-token block max-pool (vLLM post, "how
+ * MSA works"; "MiniMax goes sparse", Step 1).  For every row (b, r), group
+ * g in 0..3 and block j: block_scores[((b*R + r)*4 + g)*max_pages + j] =
+ * max over tokens t <= p of block j of q_idx[b][r][g] . K_idx[t], or -inf
+ * where the block holds no visible token (also for j beyond the context).
+ * q_idx: [B][R][4][128], FP8 E4M3 bytes (times q_scale) with an NVFP4 index
+ * cache, or FP32 with an F32 cache.  token_scores (may be NULL; a test aid):
+ * [B][R][4][max_pages*128] per-token scores, -inf for invisible tokens.
+ */
+int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, float q_scale,
+                    const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream);
+
+/*
+ * Step 3: block selection (vLLM post, "how MSA works").  For each (b, r, g)
+ * with n visible blocks: all blocks if n <= topk; otherwise the latest block
+ * n-1 plus the topk-1 best of the others by score, ties to the lower block
+ * index, NaN below every number.  sel_blocks [B][R][4][topk] ascending
+ * logical block ids, -1 padded; sel_count [B][R][4].  scores are block
+ * scores [B][R][4][max_pages] (scores_are_token_level = 0) or token scores
+ * [B][R][4][max_pages*128] that are max-pooled first (= 1).  1 <= topk <= 64.
+ */
+int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t scores_are_token_level,
+                           int32_t topk, int32_t* sel_blocks, int32_t* sel_count, hipStream_t stream);
+
+/* Workspace bytes msa_sparse_decode needs for this batch and topk (host call). */
+size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk);
+
+/*
+ * Step 4: exact GQA softmax attention over the selected blocks (vLLM post,
+ * "how MSA works"; spke.com "MSA入門" Fig. 1 caption; "MiniMax goes sparse",
+ * Step 2).  Query head h belongs to group g = h / 8 and attends, for row r,
+ * to the tokens t <= p of the blocks sel_blocks[b][r][g][0..sel_count):
+ *   out[b][r][h] = sum_t softmax_t(sm_scale * q_h . K_g[t]) V_g[t].
+ * q: [B][R][4*8][128], FP8 E4M3 bytes (times q_scale) with NVFP4 caches or
+ * FP32 with F32 caches.  out: [B][R][32][128] FP32; rows with no selected
+ * block get zeros.  workspace: device, >= msa_decode_workspace_bytes() (used
+ * by the F32 route for per-block partial results; no initial contents
+ * needed).  Two calls that share a workspace must not run concurrently.
+ */
+int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
+                      const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
+                      const int32_t* sel_count, int32_t topk, float* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Steps 3+4 in one launch (NVFP4 caches, FP8 queries): the selection of
+ * msa_block_maxpool_topk (from block scores) and the attention of
+ * msa_sparse_decode, per (request, group) in one workgroup, so the selected
+ * sets never make a round trip through memory between the two steps.
+ * sel_blocks / sel_count are written as msa_block_maxpool_topk writes them;
+ * out as msa_sparse_decode writes it.  No workspace.
+ */
+int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t topk, const void* q,
+                      int32_t q_dtype, float q_scale, float sm_scale, const msa_cache* k_cache,
+                      const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,
+                      hipStream_t stream);
+
+/* Static text for a status code (host call). */
+const char* msa_status_str(int status);
+
+/*
+ * Test aid: dequantise whole pages to FP32, out [n_pages][num_heads][128
+ * tokens][128 dims], each element the single FP32 rounding of (e2m1 * scale)
+ * * tensor_scale.  mode 0 decodes as the indexer does (FP32 scale), mode 1
+ * as the attention kernel does (E2M1 and scale in FP16, product in FP16).
+ */
+int msa_debug_dequant(const msa_cache* cache, const int32_t* pages, int32_t n_pages, int32_t mode, float* out,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

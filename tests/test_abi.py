@@ -1,0 +1,106 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point the
+header declares, and rejects bad host-side arguments without touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_index_amd", "libmsa.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("msa_kv_insert_nvfp4", "msa_index_score", "msa_block_maxpool_topk", "msa_sparse_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+class Cache(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("layout", C.c_int32), ("num_heads", C.c_int32), ("num_pages", C.c_int32),
+                ("tensor_scale", C.c_float), ("pages", C.c_void_p)]
+
+
+class Batch(C.Structure):
+    _fields_ = [("num_reqs", C.c_int32), ("rows_per_req", C.c_int32), ("max_pages_per_req", C.c_int32),
+                ("shared_prefix_pages", C.c_int32), ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p)]
+
+
+def test_status_strings(lib):
+    lib.msa_status_str.restype = C.c_char_p
+    assert lib.msa_status_str(0) == b"ok"
+    assert lib.msa_status_str(-3) == b"workspace too small"
+    assert lib.msa_status_str(7) == b"unknown status"
+
+
+def test_host_validation_without_gpu(lib):
+    fake = C.c_void_p(0x1000)  # never dereferenced: validation fails first
+    good = Batch(2, 1, 8, 0, fake, fake)
+    idx = Cache(2, 0, 1, 16, 0.01, fake)
+    lib.msa_index_score.restype = C.c_int
+    # null batch / null outputs
+    assert lib.msa_index_score(None, fake, 1, C.c_float(1.0), C.byref(idx), fake, None, None) == -1
+    assert lib.msa_index_score(C.byref(good), fake, 1, C.c_float(1.0), C.byref(idx), None, None, None) == -1
+    # too many rows, bad tensor scale, FP32 queries against an NVFP4 cache
+    bad_rows = Batch(2, 9, 8, 0, fake, fake)
+    assert lib.msa_index_score(C.byref(bad_rows), fake, 1, C.c_float(1.0), C.byref(idx), fake, None, None) == -1
+    bad_ts = Cache(2, 0, 1, 16, 0.0, fake)
+    assert lib.msa_index_score(C.byref(good), fake, 1, C.c_float(1.0), C.byref(bad_ts), fake, None, None) == -1
+    assert lib.msa_index_score(C.byref(good), fake, 0, C.c_float(1.0), C.byref(idx), fake, None, None) == -2
+    # index cache must be token-major and single-head
+    dm = Cache(2, 1, 1, 16, 0.01, fake)
+    assert lib.msa_index_score(C.byref(good), fake, 1, C.c_float(1.0), C.byref(dm), fake, None, None) == -2
+    # topk out of range
+    assert lib.msa_block_maxpool_topk(C.byref(good), fake, 0, 0, fake, fake, None) == -1
+    assert lib.msa_block_maxpool_topk(C.byref(good), fake, 0, 65, fake, fake, None) == -1
+    # workspace too small; value cache must be dim-major when NVFP4
+    k = Cache(2, 0, 4, 16, 0.01, fake)
+    v = Cache(2, 1, 4, 16, 0.01, fake)
+    lib.msa_decode_workspace_bytes.restype = C.c_size_t
+    need = lib.msa_decode_workspace_bytes(C.byref(good), 16)
+    assert need > 0
+    assert lib.msa_sparse_decode(C.byref(good), fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k), C.byref(v),
+                                 fake, fake, 16, fake, fake, C.c_size_t(need - 1), None) == -3
+    assert lib.msa_sparse_decode(C.byref(good), fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k), C.byref(k),
+                                 fake, fake, 16, fake, fake, C.c_size_t(need), None) == -2
+    # insert: pointer/cache pairing and dtype restriction
+    f32k = Cache(0, 0, 4, 16, 1.0, fake)
+    assert lib.msa_kv_insert(fake, None, None, fake, 4, C.byref(k), C.byref(v), None, None) == -1
+    assert lib.msa_kv_insert_nvfp4(fake, None, None, fake, 4, C.byref(f32k), None, None, None) == -2
+    assert lib.msa_quantize_e4m3(fake, C.c_int64(4), C.c_float(0.0), fake, None) == -1
+    # fused selection + attention: NVFP4 only, topk range, null outputs
+    assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(f32k),
+                                 C.byref(f32k), fake, fake, fake, None) == -2
+    assert lib.msa_select_decode(C.byref(good), fake, 65, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k),
+                                 C.byref(v), fake, fake, fake, None) == -1
+    assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k),
+                                 C.byref(v), fake, fake, None, None) == -1
+
+
+def test_workspace_size_formula(lib):
+    lib.msa_decode_workspace_bytes.restype = C.c_size_t
+    fake = C.c_void_p(0x1000)
+    b = Batch(32, 1, 1536, 0, fake, fake)
+    # 4 splits of 4 blocks for top-16; FP32 route needs 16 splits of 1 block: the larger is reserved
+    assert lib.msa_decode_workspace_bytes(C.byref(b), 16) == 32 * 4 * 16 * 8 * 130 * 4

@@ -1,0 +1,430 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+seeded inputs.
+
+Bars (spec criteria, restated in each test):
+  * cache bytes, FP8 query bytes and dequantised values: bit-exact;
+  * selected block sets: identical wherever the oracle's (topk-1)-th and
+    topk-th candidate scores differ by more than 1e-3 relative; inside that
+    band the GPU set must be a valid top set of the band (tests/helpers.py);
+  * attention output: per (request, row, head) vector, max |o - o_ref| /
+    max |o_ref| <= 2e-3;
+  * index scores (no bar is stated; derived): |s - s_ref| <= 2e-4 *
+    sum_k |q_k K_k|.  The matrix-core FP8 x FP4 product accumulates its 16
+    products with fewer than FP32's bits (measured on gfx950 at up to
+    8e-5 of the sum of |terms| for wide exponent ranges); the E4M3 scales
+    and FP32 sums add about 1e-7.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workload as W
+from helpers import (decode_pages_f64, oracle_batch, oracle_caches, oracle_queries, row_positions,
+                     selection_guard_ok)
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 2e-4
+OUT_TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def M():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_attention_index_amd as M
+
+    return M
+
+
+def _dev(x, dt=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t if dt is None else t.to(dt)
+
+
+def gpu_setup(M, wl):
+    from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
+
+    k, v, idx = make_caches(wl.cache == "nvfp4", wl.num_pages, wl.tensor_scale)
+    batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R)
+    dec = MsaDecoder(batch, k, v, idx, wl.topk)
+    # one request at a time, so that full-size caches never sit in host memory at once
+    if wl.prefix_tokens:
+        pos = np.arange(wl.prefix_tokens, dtype=np.int64)
+        xi, xk, xv = W.prefix_rows(wl)
+        dec.insert(_dev(xk), _dev(xv), _dev(xi), _dev(wl.slots(0, pos)))
+    for b in range(wl.B):
+        pos = wl.own_positions(b)
+        if pos.shape[0]:
+            xi, xk, xv = W.request_rows(wl, b)
+            dec.insert(_dev(xk), _dev(xv), _dev(xi), _dev(wl.slots(b, pos)))
+        if wl.num_pages > 4096 and b % 8 == 7:
+            print(f"  inserted requests 0..{b}", flush=True)
+    qi32, q32 = W.queries(wl)
+    if wl.cache == "nvfp4":
+        q_idx = M.msa_quantize_e4m3(_dev(qi32), wl.q_scale)
+        q = M.msa_quantize_e4m3(_dev(q32), wl.q_scale)
+    else:
+        q_idx, q = _dev(qi32), _dev(q32)
+    torch.cuda.synchronize()
+    return dec, q_idx, q
+
+
+def _print_case(name, wl):
+    print(f"[case] {name}: {wl.name} B={wl.B} R={wl.R} lens={wl.lengths.tolist()[:6]} pages={wl.num_pages}",
+          flush=True)
+
+
+CASES = {
+    "cfg1_f32": lambda: W.make_workload(1, seed=0),
+    "cfg2_small": lambda: W.make_workload(2, seed=1, B=3, len_div=16),
+    "cfg3_small": lambda: W.make_workload(3, seed=2, B=4, len_div=48),
+    "cfg4_small": lambda: W.make_workload(4, seed=3, B=3, len_div=64),
+    "cfg5_small": lambda: W.make_workload(5, seed=4, B=4, len_div=64),
+    "ragged": lambda: W.make_workload(3, seed=5, lengths=[1, 127, 128, 129, 2047, 2048, 2049, 5000], R=1),
+    "ragged_r4": lambda: W.make_workload(4, seed=6, lengths=[0, 2, 3, 4, 131, 2051, 2052, 7000], R=4),
+    "r3": lambda: W.make_workload(4, seed=7, B=2, len_div=64, R=3),
+    "r8": lambda: W.make_workload(4, seed=8, B=2, len_div=64, R=8),
+}
+
+
+# ---------------------------------------------------------------- step 0 / codecs
+@pytest.mark.parametrize("case", ["cfg2_small", "cfg4_small", "cfg5_small", "cfg1_f32"])
+def test_insert_bytes_bitexact(M, oracle, case):
+    wl = CASES[case]()
+    _print_case(case, wl)
+    dec, _, _ = gpu_setup(M, wl)
+    ci, ck, cv = oracle_caches(oracle, wl)
+    assert np.array_equal(dec.idx.pages.cpu().numpy(), ci.bytes)
+    assert np.array_equal(dec.k.pages.cpu().numpy(), ck.bytes)
+    assert np.array_equal(dec.v.pages.cpu().numpy(), cv.bytes)
+
+
+def test_insert_special_values_bitexact(M, oracle):
+    """Groups spanning subnormal scales, saturation, exact zeros, -0 and E2M1 ties."""
+    print("[case] insert special values", flush=True)
+    rng = np.random.default_rng(11)
+    n = 512
+    x = rng.standard_normal((n, 4, 128)).astype(np.float32)
+    x *= (2.0 ** rng.integers(-24, 14, size=(n, 4, 8, 1))).repeat(16, -1).reshape(n, 4, 128).astype(np.float32)
+    x[::7, :, :16] = 0.0
+    x[1::7, :, 16:32] = -0.0
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    x[2::7, :, 32:48] = np.tile(np.concatenate([ties, -ties]), 1)  # amax 6 -> scale = E4M3(1/ts)
+    xi = x[:, 0, :].copy()
+    ts = float(np.float32(1.0))
+    from block_sparse_attention_index_amd.decoder import make_caches
+
+    npg = n // 128 + 1
+    k, v, idx = make_caches(True, npg, ts)
+    slots = rng.permutation(npg * 128)[:n].astype(np.int64)
+    M.msa_kv_insert(_dev(x), _dev(x), _dev(xi), _dev(slots), k, v, idx)
+    torch.cuda.synchronize()
+    ok = O.OracleCache(O.NVFP4, O.TOKEN_MAJOR, 4, npg, ts)
+    ov = O.OracleCache(O.NVFP4, O.DIM_MAJOR, 4, npg, ts)
+    oi = O.OracleCache(O.NVFP4, O.TOKEN_MAJOR, 1, npg, ts)
+    ok.write(slots, x), ov.write(slots, x), oi.write(slots, xi)
+    assert np.array_equal(k.pages.cpu().numpy(), ok.bytes)
+    assert np.array_equal(v.pages.cpu().numpy(), ov.bytes)
+    assert np.array_equal(idx.pages.cpu().numpy(), oi.bytes)
+
+
+def test_quantize_e4m3_bitexact(M, oracle):
+    print("[case] e4m3 query quantiser", flush=True)
+    vals = O.e4m3_value(np.arange(127))
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(3)
+    x = np.concatenate([vals, mids, rng.standard_normal(20000) * 4, np.exp(rng.uniform(-18, 7, 5000)),
+                        [448, 463.9, 464, 464.1, 500, 1e30, np.inf, 0.0, -0.0, 2.0 ** -10, 2.0 ** -11 * 3]])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    for scale in (1.0, 0.37):
+        got = M.msa_quantize_e4m3(_dev(x), scale).cpu().numpy()
+        want = O.quantize_queries(x, scale)
+        assert np.array_equal(got, want), scale
+    xn = np.array([np.nan], np.float32)
+    assert M.msa_quantize_e4m3(_dev(xn), 1.0).cpu().numpy()[0] & 0x7F == 0x7F
+
+
+@pytest.mark.parametrize("layout", ["token_major", "dim_major"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_debug_dequant_exhaustive(M, oracle, layout, mode):
+    """Every E4M3 scale code against every E2M1 code, bit-exact (NaN scales give NaN)."""
+    print(f"[case] dequant {layout} mode {mode}", flush=True)
+    rng = np.random.default_rng(1)
+    npg = 4
+    raw = rng.integers(0, 256, size=npg * 9216, dtype=np.uint8)
+    slabs = raw.reshape(npg, 9216)
+    # scales: page p uses codes (p*1024 + i) % 256 -> all 256 codes appear in every page
+    slabs[:, 8192:] = (np.arange(npg * 1024).reshape(npg, 1024) % 256).astype(np.uint8)
+    # codes: row (token or dim) x, element e holds nibble (x + e) % 16, so every 16-element
+    # group holds all 16 E2M1 codes, each next to every scale code over the pages
+    rr, ii = np.meshgrid(np.arange(128), np.arange(64), indexing="ij")
+    codes = ((2 * ii + rr) % 16) | (((2 * ii + 1 + rr) % 16) << 4)
+    slabs[:, :8192] = codes.reshape(-1).astype(np.uint8)[None, :]
+    dm = layout == "dim_major"
+    dev_pages = _dev(raw)
+    c = M.Cache(dev_pages, M.MSA_NVFP4, M.MSA_DIM_MAJOR if dm else M.MSA_TOKEN_MAJOR, 1, npg, 0.3)
+    out = torch.empty((npg, 1, 128, 128), dtype=torch.float32, device="cuda")
+    M.msa_debug_dequant(c, _dev(np.arange(npg, dtype=np.int32)), mode, out)
+    got = out.cpu().numpy()
+    oc = O.OracleCache(O.NVFP4, O.DIM_MAJOR if dm else O.TOKEN_MAJOR, 1, npg, 0.3)
+    oc.bytes[:] = raw
+    want = oc.dequant_pages(np.arange(npg))
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    exact = decode_pages_f64(raw, True, dm, 1, npg, 0.3)
+    assert np.array_equal(np.isnan(exact), nan)
+
+
+# ---------------------------------------------------------------- steps 1+2
+@pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
+                                  "ragged_r4", "r3", "r8"])
+def test_index_scores(M, oracle, case):
+    wl = CASES[case]()
+    _print_case(case, wl)
+    dec, q_idx, _ = gpu_setup(M, wl)
+    T = wl.max_pages * 128
+    tok = torch.empty((wl.B, wl.R, 4, T), dtype=torch.float32, device="cuda")
+    dec.index(q_idx, wl.q_scale, tok)
+    got_tok = tok.cpu().numpy().astype(np.float64)
+    got_blk = dec.block_scores.cpu().numpy().astype(np.float64)
+    ci, _, _ = oracle_caches(oracle, wl)
+    _, _, qi, _ = oracle_queries(oracle, wl)
+    bt = oracle_batch(oracle, wl)
+    ref_tok, ref_abs = oracle.index_scores(bt, qi, ci, with_abs=True)
+    ref_blk = oracle.block_maxpool(bt, ref_tok)
+    inv = np.isneginf(ref_tok)
+    assert np.array_equal(np.isneginf(got_tok), inv)
+    err = np.abs(got_tok[~inv] - ref_tok[~inv])
+    bound = SCORE_TOL * ref_abs[~inv] + 1e-30
+    ratio = float((err / bound).max()) if err.size else 0.0
+    print(f"  token score error / bound max = {ratio:.3f}; max err/sum|terms| = "
+          f"{float((err / (ref_abs[~inv] + 1e-30)).max()) if err.size else 0:.2e}", flush=True)
+    assert ratio <= 1.0
+    # block scores are the max-pool of the token scores
+    binv = np.isneginf(ref_blk)
+    assert np.array_equal(np.isneginf(got_blk), binv)
+    pooled = got_tok.reshape(got_tok.shape[:3] + (wl.max_pages, 128)).max(-1)
+    assert np.array_equal(got_blk, pooled)
+    # same kernel without the token-score output
+    dec.index(q_idx, wl.q_scale, None)
+    assert np.array_equal(dec.block_scores.cpu().numpy().astype(np.float64), got_blk)
+
+
+# ---------------------------------------------------------------- step 3
+@pytest.mark.parametrize("topk,P", [(1, 300), (4, 300), (16, 300), (64, 300), (16, 1400), (16, 2500), (16, 4000)])
+def test_topk_exact_on_shared_scores(M, oracle, topk, P):
+    """Same FP32 scores on both sides: the selection must be identical, ties and NaN included.
+    P covers each register-capacity variant of the kernel and the rescan-from-memory one."""
+    print(f"[case] topk={topk} P={P}", flush=True)
+    rng = np.random.default_rng(topk + P)
+    B, R = 6, 2
+    lens = np.array([0, 1, 128, 129, P * 128, 20000], np.int32)
+    table = np.zeros((B, P), np.int32)
+    scores = rng.integers(-4, 5, size=(B, R, 4, P)).astype(np.float32)
+    scores[4, 0, 1, :40] = rng.standard_normal(40).astype(np.float32)
+    scores[4, 1, 2, :8] = [-0.0, 0.0, -0.0, 0.0, np.nan, np.nan, -np.inf, np.inf]
+    scores[5, 1, 3, 100:150] = np.nan
+    batch = M.Batch(_dev(table), _dev(lens), R)
+    sel = torch.empty((B, R, 4, topk), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, R, 4), dtype=torch.int32, device="cuda")
+    M.msa_block_maxpool_topk(batch, _dev(scores), 0, topk, sel, cnt)
+    bt = oracle.OracleBatch(table, lens, R)
+    rs, rc = oracle.select(bt, scores.astype(np.float64), topk)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(sel.cpu().numpy(), rs)
+    # token-level route: max-pool first
+    tok = np.repeat(scores, 128, axis=-1) - rng.integers(0, 3, size=(B, R, 4, P * 128)).astype(np.float32)
+    M.msa_block_maxpool_topk(batch, _dev(tok), 1, topk, sel, cnt)
+    rs2, rc2 = oracle.select(bt, oracle.block_maxpool(bt, tok.astype(np.float64)), topk)
+    assert np.array_equal(cnt.cpu().numpy(), rc2)
+    assert np.array_equal(sel.cpu().numpy(), rs2)
+
+
+# ---------------------------------------------------------------- step 4
+def _out_err(got, ref):
+    return np.abs(got - ref).max(-1) / np.maximum(np.abs(ref).max(-1), 1e-30)
+
+
+@pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small",
+                                  "ragged", "ragged_r4", "r3", "r8"])
+def test_sparse_decode_on_oracle_selection(M, oracle, case):
+    wl = CASES[case]()
+    _print_case(case, wl)
+    dec, q_idx, q = gpu_setup(M, wl)
+    ci, ck, cv = oracle_caches(oracle, wl)
+    _, _, qi, qd = oracle_queries(oracle, wl)
+    bt = oracle_batch(oracle, wl)
+    sel, cnt = oracle.select(bt, oracle.block_maxpool(bt, oracle.index_scores(bt, qi, ci)), wl.topk)
+    dec.sel.copy_(_dev(sel))
+    dec.cnt.copy_(_dev(cnt))
+    dec.attend(q, wl.q_scale, wl.sm_scale)
+    got = dec.out.cpu().numpy().astype(np.float64)
+    ref = oracle.attention(bt, qd, wl.sm_scale, ck, cv, sel, cnt)
+    err = _out_err(got, ref)
+    empty = np.repeat(cnt == 0, 8, axis=2)
+    assert (got[empty] == 0).all()
+    print(f"  max per-vector relative error {err[~empty].max() if (~empty).any() else 0:.3e}", flush=True)
+    assert err[~empty].max(initial=0.0) <= OUT_TOL
+
+
+# ---------------------------------------------------------------- whole step
+def _check_full_step(M, oracle, wl, sample=None, fused=True):
+    dec, q_idx, q = gpu_setup(M, wl)
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale, fused=fused)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = dec.sel.cpu().numpy(), dec.cnt.cpu().numpy()
+    g_out = dec.out.cpu().numpy().astype(np.float64)
+    g_bs = dec.block_scores.cpu().numpy().astype(np.float64)
+    rows = np.arange(wl.B) if sample is None else np.asarray(sample)
+    ci, ck, cv = oracle_caches(oracle, wl) if sample is None else _sampled_caches(oracle, wl, rows)
+    _, _, qi, qd = oracle_queries(oracle, wl)
+    bt = oracle.OracleBatch(wl.block_table[rows], wl.lengths[rows], wl.R)
+    res = oracle.decode_step(bt, qi[rows], qd[rows], wl.sm_scale, ci, ck, cv, wl.topk)
+    # block scores (max-pooled) against the oracle's, with the derived bound
+    ts, ab = oracle.index_scores(bt, qi[rows], ci, with_abs=True)
+    absmax = ab.reshape(ab.shape[:3] + (wl.max_pages, 128)).max(-1)
+    fin = np.isfinite(res["block_scores"])
+    assert np.array_equal(np.isfinite(g_bs[rows]), fin)
+    assert (np.abs(g_bs[rows][fin] - res["block_scores"][fin]) <= SCORE_TOL * absmax[fin] + 1e-30).all()
+    p = row_positions(wl)[rows]
+    guarded = mism = 0
+    for bi_, b in enumerate(rows):
+        for r in range(wl.R):
+            for g in range(4):
+                ok, gd = selection_guard_ok(res["block_scores"][bi_, r, g], res["sel"][bi_, r, g],
+                                            res["cnt"][bi_, r, g], g_sel[b, r, g], g_cnt[b, r, g], p[bi_, r],
+                                            wl.topk)
+                guarded += gd
+                mism += not ok
+    print(f"  selections: {rows.size * wl.R * 4} compared, {guarded} inside the 1e-3 guard band, "
+          f"{mism} invalid", flush=True)
+    assert mism == 0
+    # outputs: against oracle attention on the GPU's (validated) selection, and on the oracle's where equal
+    ref_own = oracle.attention(bt, qd[rows], wl.sm_scale, ck, cv, g_sel[rows], g_cnt[rows])
+    err = _out_err(g_out[rows], ref_own)
+    print(f"  max per-vector relative error {err.max():.3e}", flush=True)
+    assert err.max() <= OUT_TOL
+    same = np.array([[[set(g_sel[b, r, g, :g_cnt[b, r, g]]) == set(res["sel"][i, r, g, :res["cnt"][i, r, g]])
+                       for g in range(4)] for r in range(wl.R)] for i, b in enumerate(rows)])
+    same_h = np.repeat(same, 8, axis=2)
+    err2 = _out_err(g_out[rows], res["out"])
+    assert err2[same_h].max(initial=0.0) <= OUT_TOL
+    return dec
+
+
+def _sampled_caches(oracle, wl, rows):
+    """Oracle caches holding only the pages of the sampled requests (and the shared prefix)."""
+    dt = oracle.F32 if wl.cache == "f32" else oracle.NVFP4
+    ci = oracle.OracleCache(dt, oracle.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
+    ck = oracle.OracleCache(dt, oracle.TOKEN_MAJOR, 4, wl.num_pages, wl.tensor_scale)
+    cv = oracle.OracleCache(dt, oracle.DIM_MAJOR if dt == oracle.NVFP4 else oracle.TOKEN_MAJOR, 4, wl.num_pages,
+                            wl.tensor_scale)
+    if wl.prefix_tokens:
+        pos = np.arange(wl.prefix_tokens, dtype=np.int64)
+        xi, xk, xv = W.prefix_rows(wl)
+        s = wl.slots(0, pos)
+        ci.write(s, xi), ck.write(s, xk), cv.write(s, xv)
+    for b in rows:
+        pos = wl.own_positions(b)
+        xi, xk, xv = W.request_rows(wl, b)
+        s = wl.slots(b, pos)
+        ci.write(s, xi), ck.write(s, xk), cv.write(s, xv)
+    return ci, ck, cv
+
+
+@pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
+                                  "ragged_r4", "r3", "r8"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_full_step(M, oracle, case, fused):
+    """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
+    wl = CASES[case]()
+    _print_case(f"{case} fused={fused}", wl)
+    _check_full_step(M, oracle, wl, fused=fused)
+
+
+@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8"])
+def test_select_decode_equals_separate_calls(M, oracle, case):
+    """msa_select_decode: same selection as msa_block_maxpool_topk and bitwise the same
+    output as msa_sparse_decode on that selection."""
+    wl = CASES[case]()
+    _print_case(case, wl)
+    dec, q_idx, q = gpu_setup(M, wl)
+    dec.index(q_idx, wl.q_scale)
+    dec.select()
+    dec.attend(q, wl.q_scale, wl.sm_scale)
+    sel_a, cnt_a, out_a = dec.sel.clone(), dec.cnt.clone(), dec.out.clone()
+    dec.sel.fill_(-5), dec.cnt.fill_(-5), dec.out.fill_(7.0)
+    dec.select_attend(q, wl.q_scale, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dec.cnt, cnt_a) and torch.equal(dec.sel, sel_a)
+    assert torch.equal(dec.out.view(torch.int32), out_a.view(torch.int32))
+
+
+def test_full_step_deterministic(M, oracle):
+    wl = CASES["cfg4_small"]()
+    _print_case("determinism", wl)
+    dec, q_idx, q = gpu_setup(M, wl)
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale)
+    a = (dec.block_scores.clone(), dec.sel.clone(), dec.out.clone())
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale)
+    assert torch.equal(a[0], dec.block_scores) and torch.equal(a[1], dec.sel)
+    assert torch.equal(a[2].view(torch.int32), dec.out.view(torch.int32))
+
+
+def test_graph_replay_matches_eager(M, oracle):
+    """The step has no memset nodes and no host sync: capture it and replay it several times."""
+    wl = CASES["cfg3_small"]()
+    _print_case("graph replay", wl)
+    dec, q_idx, q = gpu_setup(M, wl)
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale)
+    torch.cuda.synchronize()
+    eager = dec.out.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dec.step(q_idx, q, wl.q_scale, wl.sm_scale)
+    for _ in range(3):
+        dec.out.zero_()
+        dec.sel.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out.view(torch.int32), eager.view(torch.int32))
+        x = torch.randn(1000, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del x
+
+
+def test_full_size_config3_sampled(M, oracle):
+    """Configuration 3 at full size (B=32, 64K-192K tokens), in the bench's launch
+    configuration; the oracle checks three sampled requests end to end."""
+    wl = W.make_workload(3, seed=0)
+    _print_case("config 3 full size", wl)
+    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 7]
+    _check_full_step(M, oracle, wl, sample=rows)
+
+
+def test_full_size_config4_sampled(M, oracle):
+    wl = W.make_workload(4, seed=0)
+    _print_case("config 4 full size", wl)
+    _check_full_step(M, oracle, wl, sample=[0, 5])
+
+
+def test_abi_errors_on_device(M):
+    print("[case] abi errors", flush=True)
+    wl = CASES["cfg2_small"]()
+    dec, q_idx, q = gpu_setup(M, wl)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(M.MsaError) as e:
+        M.msa_sparse_decode(dec.batch, q, M.MSA_FP8_E4M3, 1.0, wl.sm_scale, dec.k, dec.v, dec.sel, dec.cnt,
+                            wl.topk, dec.out, small)
+    assert e.value.status == M.MSA_ERR_WORKSPACE
+    with pytest.raises(M.MsaError) as e:
+        M.msa_block_maxpool_topk(dec.batch, dec.block_scores, 0, 0, dec.sel, dec.cnt)
+    assert e.value.status == M.MSA_ERR_INVALID_ARG
+    f32 = W.make_workload(1, seed=0)
+    dec32, _, q32 = gpu_setup(M, f32)
+    with pytest.raises(M.MsaError) as e:
+        dec32.select_attend(q32, 1.0, f32.sm_scale)
+    assert e.value.status == M.MSA_ERR_UNSUPPORTED
