@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+from types import SimpleNamespace
 import os
 import sys
 import time
@@ -104,6 +105,58 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
                       f"scaled by context tokens"}
 
 
+def setup(seed=0, n_replicas=2):
+    """Device state of the benchmark workload: filled caches (``n_replicas`` copies),
+    decoders, the step's new rows and quantised queries."""
+    import torch
+
+    import block_sparse_attention_index_amd as M
+    import workload as W
+    from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
+
+    dev = torch.device("cuda:0")
+    wl = W.make_workload(CONFIG_ID, seed=seed)
+    log(f"workload {wl.name}: B={wl.B} R={wl.R} tokens={int(wl.lengths.sum())} pages={wl.num_pages}")
+
+    # ---- caches (replica 0 filled by the insert kernel from device-drawn rows)
+    k0, v0, i0 = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
+    table = torch.from_numpy(wl.block_table).to(dev)
+    lens = torch.from_numpy(wl.lengths).to(dev)
+    batch = M.Batch(table, lens, wl.R)
+    for b in range(wl.B):
+        pos = wl.own_positions(b)
+        xi, xk, xv = W.torch_rows(wl, b, dev)
+        slots = torch.from_numpy(wl.slots(b, pos)).to(dev)
+        M.msa_kv_insert(xk, xv, xi, slots, k0, v0, i0)
+        del xi, xk, xv
+    torch.cuda.synchronize()
+    replicas = [(k0, v0, i0)]
+    for _ in range(n_replicas - 1):
+        k, v, i = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
+        k.pages.copy_(k0.pages), v.pages.copy_(v0.pages), i.pages.copy_(i0.pages)
+        replicas.append((k, v, i))
+    decs = [MsaDecoder(batch, k, v, i, wl.topk, dev) for (k, v, i) in replicas]
+    for d in decs[1:]:  # share the output buffers: every replica computes the same step
+        d.block_scores, d.sel, d.cnt, d.out, d.workspace = (decs[0].block_scores, decs[0].sel, decs[0].cnt,
+                                                            decs[0].out, decs[0].workspace)
+
+    # ---- step inputs: new rows of the R latest positions, FP8 queries
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 12345)
+    n_new = wl.B * wl.R
+    new_k = torch.randn((n_new, 4, 128), generator=gen, device=dev)
+    new_v = torch.randn((n_new, 4, 128), generator=gen, device=dev)
+    new_i = torch.randn((n_new, 128), generator=gen, device=dev)
+    new_slots = torch.from_numpy(np.concatenate([wl.slots(b, wl.new_row_positions(b)) for b in range(wl.B)])).to(dev)
+    qi32, q32 = W.queries(wl)
+    q_idx = M.msa_quantize_e4m3(torch.from_numpy(qi32).to(dev), wl.q_scale)
+    q = M.msa_quantize_e4m3(torch.from_numpy(q32).to(dev), wl.q_scale)
+    new = (new_k, new_v, new_i, new_slots)
+    torch.cuda.synchronize()
+
+    return SimpleNamespace(torch=torch, M=M, W=W, wl=wl, decs=decs, q_idx=q_idx, q=q, new=new, batch=batch)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,51 +174,8 @@ def main():
               "(the context-parallel indexer design is documented, not built).", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
-    import block_sparse_attention_index_amd as M
-    import workload as W
-    from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
-
-    dev = torch.device("cuda:0")
-    wl = W.make_workload(CONFIG_ID, seed=args.seed)
-    log(f"workload {wl.name}: B={wl.B} R={wl.R} tokens={int(wl.lengths.sum())} pages={wl.num_pages}")
-
-    # ---- caches (replica 0 filled by the insert kernel from device-drawn rows)
-    k0, v0, i0 = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
-    table = torch.from_numpy(wl.block_table).to(dev)
-    lens = torch.from_numpy(wl.lengths).to(dev)
-    batch = M.Batch(table, lens, wl.R)
-    for b in range(wl.B):
-        pos = wl.own_positions(b)
-        xi, xk, xv = W.torch_rows(wl, b, dev)
-        slots = torch.from_numpy(wl.slots(b, pos)).to(dev)
-        M.msa_kv_insert(xk, xv, xi, slots, k0, v0, i0)
-        del xi, xk, xv
-    torch.cuda.synchronize()
-    replicas = [(k0, v0, i0)]
-    for _ in range(args.replicas - 1):
-        k, v, i = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
-        k.pages.copy_(k0.pages), v.pages.copy_(v0.pages), i.pages.copy_(i0.pages)
-        replicas.append((k, v, i))
-    decs = [MsaDecoder(batch, k, v, i, wl.topk, dev) for (k, v, i) in replicas]
-    for d in decs[1:]:  # share the output buffers: every replica computes the same step
-        d.block_scores, d.sel, d.cnt, d.out, d.workspace = (decs[0].block_scores, decs[0].sel, decs[0].cnt,
-                                                            decs[0].out, decs[0].workspace)
-
-    # ---- step inputs: new rows of the R latest positions, FP8 queries
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(args.seed + 12345)
-    n_new = wl.B * wl.R
-    new_k = torch.randn((n_new, 4, 128), generator=gen, device=dev)
-    new_v = torch.randn((n_new, 4, 128), generator=gen, device=dev)
-    new_i = torch.randn((n_new, 128), generator=gen, device=dev)
-    new_slots = torch.from_numpy(np.concatenate([wl.slots(b, wl.new_row_positions(b)) for b in range(wl.B)])).to(dev)
-    qi32, q32 = W.queries(wl)
-    q_idx = M.msa_quantize_e4m3(torch.from_numpy(qi32).to(dev), wl.q_scale)
-    q = M.msa_quantize_e4m3(torch.from_numpy(q32).to(dev), wl.q_scale)
-    new = (new_k, new_v, new_i, new_slots)
-    torch.cuda.synchronize()
+    st = setup(args.seed, args.replicas)
+    torch, M, W, wl, decs, q_idx, q, new = st.torch, st.M, st.W, st.wl, st.decs, st.q_idx, st.q, st.new
 
     stream = torch.cuda.Stream()
     use_graph = not args.no_graph
@@ -213,6 +223,7 @@ def main():
         "index": lambda d: d.index(q_idx, wl.q_scale, None, stream),
         "topk": lambda d: d.select(stream),
         "decode": lambda d: d.attend(q, wl.q_scale, wl.sm_scale, stream),
+        "select_decode": lambda d: d.select_attend(q, wl.q_scale, wl.sm_scale, stream),
     }
     us = {}
     for name, call in calls.items():

@@ -5,31 +5,36 @@
 // step 3 (the selection) in one launch.
 //
 // Work split (NVFP4): one workgroup of 8 waves (4 with two query tiles) per
-// (request, group, group of up to 4 rows).  The waves walk the union of the rows' selected blocks,
-// one 128-token block at a time, each keeping an online softmax (running
-// max, denominator, unnormalised output); the waves merge through LDS and the
-// workgroup writes the normalised output -- no partial results leave the
+// (request, group, group of up to 4 rows).  The waves walk the union of the
+// rows' selected blocks, two 128-token blocks at a time with both blocks'
+// loads in flight, each wave keeping an online softmax (running max,
+// denominator, unnormalised output); the waves then merge through LDS and
+// the workgroup writes the normalised output -- no partial results leave the
 // chip and no second launch merges them.  With the selection fused in, waves
 // 0..nr-1 first run the top-k of one row each (msa_select.h) from the block
-// scores.  With one row per request, the 8 heads of a group share each
-// dequantised K/V element (GQA); with 4 speculative rows the 32 query vectors
-// of a group fill two 16-column query tiles.
+// scores, while the block-table row and the queries load.  With one row per
+// request, the 8 heads of a group share each dequantised K/V element (GQA);
+// with 4 speculative rows the 32 query vectors of a group fill two 16-column
+// query tiles.
 //
 // Per block and wave:
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16.  K codes go through the exact
 //    E2M1->FP16 conversion and one packed FP16 multiply by their E4M3 scale
 //    (E2M1 x E4M3 has at most 6 significant bits, so the product is exact);
-//    the K tensor scale, the query scale and sm_scale are applied to the FP32
-//    accumulators.  Queries (E4M3) are exact in FP16 as well.
-//  * The 16 rows of M-tile m are tokens 32*(m/2) + 8*(i/4) + 4*(m%2) + i%4,
-//    so that the accumulator rows a lane holds are 8 consecutive tokens per
-//    32-token step: they are then already the P operand of the P.V product,
-//    with no shuffle through LDS.
-//  * P is rounded to FP16 (FP32 accumulation); V comes from the dim-major
-//    value slab, where the 8 tokens of one dim that a P.V operand lane needs
-//    are one dword, scaled per token by the E4M3 group scale in FP16.
-//  * K and V are read with non-temporal loads (each selected block is read
-//    once per step).
+//    the K tensor scale, the query scale, sm_scale and log2(e) are applied to
+//    the FP32 accumulators.  Queries (E4M3) are exact in FP16 as well.
+//  * Row i of M-tile m is token 32*(i/4) + 8*(m/2) + 4*(m%2) + i%4: a lane
+//    (column n, quad a) then holds, for the 32-token step kk of the P.V
+//    product, tokens 32a + 8kk + 0..7 -- already the P operand, with no
+//    shuffle -- and the value codes of those tokens for one dim are 4
+//    consecutive bytes, so a lane loads the codes of all four steps of a
+//    16-dim tile as one 16-byte word of the dim-major value slab.
+//  * P is rounded to FP16 (FP32 accumulation); its row sums come from one
+//    more MFMA against a ones operand, so the denominator adds exactly the P
+//    that the numerator uses.  V codes are scaled per token by their E4M3
+//    group scale in FP16 (converted once per block into LDS).
+//  * K and V are read with non-temporal 16-byte loads (each selected block is
+//    read once per step).
 #include <algorithm>
 
 #include "msa_device.h"
@@ -40,16 +45,19 @@ namespace msa {
 
 
 // Sorted union of the sets already in s_rowsel (nr rows of topk ids, -1 padded).
+// One row: the ids are already sorted; the valid ones are compacted by a
+// ballot of the first wave.
 __device__ int union_of_rows(const int* s_rowsel, int nr, int topk, int* s_first, int* s_union, int* s_nu) {
   const int tid = threadIdx.x;
   const int N = nr * topk;
   if (nr == 1) {
-    if (tid == 0) {
-      int n = 0;
-      while (n < topk && s_rowsel[n] >= 0) ++n;
-      *s_nu = n;
+    if (tid < 64) {
+      const int v = tid < topk ? s_rowsel[tid] : -1;
+      const uint64_t m = __ballot(v >= 0);
+      const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (v >= 0) s_union[before] = v;
+      if (tid == 0) *s_nu = __popcll(m);
     }
-    for (int i = tid; i < topk; i += blockDim.x) s_union[i] = s_rowsel[i];
     __syncthreads();
     return *s_nu;
   }
@@ -74,7 +82,8 @@ __device__ int union_of_rows(const int* s_rowsel, int nr, int topk, int* s_first
 }
 
 // Rows [r0, r0 + nr) of (b, g): load their selected sets into s_rowsel and
-// form the sorted union in LDS.  Returns the union size.
+// form the sorted union in LDS.  Returns the union size.  Entries past a
+// row's count, or naming a block beyond the table, read as absent (-1).
 __device__ int build_union(const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int b, int g, int R,
                            int r0, int nr, int topk, int max_pages, int* s_rowsel, int* s_first, int* s_union,
                            int* s_nu) {
@@ -82,9 +91,9 @@ __device__ int build_union(const int32_t* __restrict__ sel, const int32_t* __res
   for (int i = threadIdx.x; i < N; i += blockDim.x) {
     const int r = r0 + i / topk, k = i % topk;
     const int64_t row = ((int64_t)b * R + r) * kGroups + g;
-    int v = k < cnt[row] ? sel[row * topk + k] : -1;
-    if (v >= max_pages) v = -1;
-    s_rowsel[i] = v;
+    const int c = cnt[row];
+    const int v = sel[row * topk + k];
+    s_rowsel[i] = (k < c && v < max_pages) ? v : -1;
   }
   __syncthreads();
   return union_of_rows(s_rowsel, nr, topk, s_first, s_union, s_nu);
@@ -96,23 +105,20 @@ __device__ __forceinline__ bool row_has_block(const int* s_rowsel, int rl, int t
   return false;
 }
 
-// Running softmax state of one wave over QT query tiles of 16 columns.
+// Running softmax state of one wave over QT query tiles of 16 columns, in the
+// base-2 domain (scores pre-multiplied by log2 e).
 template <int QT>
 struct AttnState {
   float m[QT];   // running max of query column n = lane%16 (same in its 4 lanes)
-  float l[QT];   // running denominator, same layout
+  v4f L[QT];     // running denominator of queries 4*(lane/16)+q (every column holds it)
   v4f O[QT][8];  // unnormalised output: rows 4*(lane/16)+q (queries), dims 16*nt + lane%16
 };
 
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 nt_load4(const uint8_t* p) {
   const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t nt_load1(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(p));
 }
 
 // Query operands: column n of tile qt = query qi = 16qt + n -> (row qi/8, head qi%8 of group g),
@@ -129,7 +135,8 @@ __device__ __forceinline__ void load_q(const uint8_t* __restrict__ q, int b, int
     const uint8_t* qrow = q + ((((int64_t)b * R + r0 + (ok ? rl : 0)) * kGroups + g) * kHpg + hh) * kDim;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint2 w = ok ? *reinterpret_cast<const uint2*>(qrow + 32 * a + 8 * ks) : make_uint2(0, 0);
+      uint2 w = *reinterpret_cast<const uint2*>(qrow + 32 * a + 8 * ks);
+      w = ok ? w : make_uint2(0, 0);
       const h2 x0 = e4m3x2_to_h2<false>(w.x), x1 = e4m3x2_to_h2<true>(w.x);
       const h2 x2 = e4m3x2_to_h2<false>(w.y), x3 = e4m3x2_to_h2<true>(w.y);
       Q[qt][ks] = h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
@@ -137,123 +144,165 @@ __device__ __forceinline__ void load_q(const uint8_t* __restrict__ q, int b, int
   }
 }
 
-// One 128-token block: S^T = K Q^T, online-softmax update of `st`, O += P V.
-// lim[qt]: last visible token of the block for this lane's query column (-1: none).
-template <int QT>
-__device__ __forceinline__ void attend_block(const uint8_t* __restrict__ ks_, const uint8_t* __restrict__ vs_,
-                                             const h8 (&Q)[QT][4], const int (&lim)[QT], float qk_scale, int lane,
-                                             uint4* vsc_slot, AttnState<QT>& st) {
-  const int n = lane & 15, a = lane >> 4;
-  // ---- every load of the block up front: K codes + scales, V codes, V scales
-  uint4 kc[8];
-  uint32_t ksc[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int tok = 32 * (m >> 1) + 8 * (n >> 2) + 4 * (m & 1) + (n & 3);
-    kc[m] = nt_load4(ks_ + tok * 64 + 16 * a);
-    ksc[m] = *reinterpret_cast<const uint16_t*>(ks_ + kScaleOff + tok * 8 + 2 * a);
-  }
-  uint32_t vw[8][4];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) vw[nt][kk] = nt_load1(vs_ + (16 * nt + n) * 64 + 16 * kk + 4 * a);
-  const uint4 vsc_regs = nt_load4(vs_ + kScaleOff + 16 * lane);
+// What one wave reads of one 128-token block: the key part, then the value
+// part.  Every load is 16 bytes per lane.
+struct KRegs {
+  uint4 kc[8];  // K codes of token tok(m): dims 32a .. 32a+31
+  uint4 ksc;    // K scales of tokens 2 lane, 2 lane + 1 (8 bytes each)
+};
+struct VRegs {
+  uint4 vw[8];  // V codes of dim 16nt + n: tokens 32a .. 32a+31 (dword kk = tokens 32a + 8kk ..)
+  uint4 vsc;    // V scales, bytes 16 lane .. 16 lane + 15 of the block's 1 KB ([group][token])
+};
 
-  // ---- S^T = K Q^T
+// token held in row i of M-tile m (see the file comment)
+__device__ __forceinline__ constexpr int tile_token(int m, int i) {
+  return 32 * (i >> 2) + 8 * (m >> 1) + 4 * (m & 1) + (i & 3);
+}
+
+__device__ __forceinline__ void load_k(const uint8_t* __restrict__ ks_, int lane, KRegs& r) {
+  const int n = lane & 15, a = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) r.kc[m] = nt_load4(ks_ + tile_token(m, n) * 64 + 16 * a);
+  r.ksc = nt_load4(ks_ + kScaleOff + 16 * lane);
+}
+
+__device__ __forceinline__ void load_v(const uint8_t* __restrict__ vs_, int lane, VRegs& r) {
+  const int n = lane & 15, a = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) r.vw[nt] = nt_load4(vs_ + (16 * nt + n) * 64 + 16 * a);
+  r.vsc = nt_load4(vs_ + kScaleOff + 16 * lane);
+}
+
+// Per-wave LDS slots of one block's scales.
+struct ScaleSlot {
+  uint4 k[64];  // raw K scale bytes, [token][group]
+  h8 v[128];    // V scales in FP16, [group][token]
+};
+
+// One 128-token block: S^T = K Q^T, online-softmax update of `st`, O += P V.
+// lim[qt]: last visible token of the block for this lane's query column (-1:
+// none); `partial` (wave-uniform) says whether any lim is below 127; `first`
+// (wave-uniform) says the state is still empty, so nothing needs rescaling.
+// after_qk() runs once the key registers are consumed (the caller issues the
+// next block's loads there).
+template <int QT, typename AfterQK>
+__device__ __forceinline__ void attend_block(const KRegs& kr, const VRegs& vr, const h8 (&Q)[QT][4],
+                                             const int (&lim)[QT], bool partial, bool first, float qk2, int lane,
+                                             ScaleSlot* slot, AttnState<QT>& st, AfterQK after_qk) {
+  const int n = lane & 15, a = lane >> 4;
+  // ---- scales through LDS: each lane needs scales that other lanes of this wave loaded
+  slot->k[lane] = kr.ksc;
+  {
+    const uint32_t w[4] = {vr.vsc.x, vr.vsc.y, vr.vsc.z, vr.vsc.w};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const h2 s0 = e4m3x2_to_h2<false>(w[2 * i]), s1 = e4m3x2_to_h2<true>(w[2 * i]);
+      const h2 s2 = e4m3x2_to_h2<false>(w[2 * i + 1]), s3 = e4m3x2_to_h2<true>(w[2 * i + 1]);
+      slot->v[2 * lane + i] = h8{s0[0], s0[1], s1[0], s1[1], s2[0], s2[1], s3[0], s3[1]};
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint8_t* kraw = reinterpret_cast<const uint8_t*>(slot->k);
+
+  // ---- S^T = K Q^T (k-steps outermost: the 8 accumulators are independent)
+  h2 ksc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    ksc[m] = e4m3x2_to_h2<false>(*reinterpret_cast<const uint16_t*>(kraw + tile_token(m, n) * 8 + 2 * a));
   v4f Sacc[QT][8];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int m = 0; m < 8; ++m) Sacc[qt][m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const h2 sc = e4m3x2_to_h2<false>(ksc[m]);
-    const uint32_t words[4] = {kc[m].x, kc[m].y, kc[m].z, kc[m].w};
+  for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const _Float16 s = ks < 2 ? sc[0] : sc[1];
-      h8 kv = e2m1x8_to_h8(words[ks]);
-      const h8 sv = h8{s, s, s, s, s, s, s, s};
-      kv = kv * sv;
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t word = ks == 0 ? kr.kc[m].x : ks == 1 ? kr.kc[m].y : ks == 2 ? kr.kc[m].z : kr.kc[m].w;
+      const _Float16 s = ks < 2 ? ksc[m][0] : ksc[m][1];
+      h8 kv = e2m1x8_to_h8(word);
+      kv = kv * h8{s, s, s, s, s, s, s, s};
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
         Sacc[qt][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, Q[qt][ks], Sacc[qt][m], 0, 0, 0);
     }
   }
+  after_qk();
 
-  // ---- online softmax (token of Sacc[qt][m][q] = 32(m/2) + 8a + 4(m%2) + q)
+  // ---- online softmax, base 2 (token of Sacc[qt][m][q] = 32a + 8(m/2) + 4(m%2) + q)
   h8 P[QT][4];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) Sacc[qt][m] *= qk2;
+    if (partial) {
+      const int lr = lim[qt] - 32 * a;  // visible iff 8(m/2) + 4(m%2) + q <= lr
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          Sacc[qt][m][qq] = 8 * (m >> 1) + 4 * (m & 1) + qq <= lr ? Sacc[qt][m][qq] : -__builtin_inff();
+    }
     float mx = -__builtin_inff();
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int tok = 32 * (m >> 1) + 8 * a + 4 * (m & 1) + qq;
-        float z = Sacc[qt][m][qq] * qk_scale;
-        z = tok <= lim[qt] ? z : -__builtin_inff();
-        Sacc[qt][m][qq] = z;
-        mx = fmaxf(mx, z);
-      }
+      for (int qq = 0; qq < 4; ++qq) mx = fmaxf(mx, Sacc[qt][m][qq]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m[qt], mx);
-    const float alpha = st.m[qt] == -__builtin_inff() ? 0.f : __expf(st.m[qt] - m_new);
-    float sum = 0.f;
+    // exponent base: a column with nothing visible yet keeps m = -inf and uses 0,
+    // so exp2(-inf - base) = 0 throughout
+    const float base = m_new == -__builtin_inff() ? 0.f : m_new;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       h8 pk;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int m = 2 * kk + (e >> 2), qq = e & 3;
-        const float z = Sacc[qt][m][qq];
-        const float pz = z == -__builtin_inff() ? 0.f : __expf(z - m_new);
-        sum += pz;
-        pk[e] = (_Float16)pz;
-      }
+      for (int e = 0; e < 8; ++e) pk[e] = (_Float16)__builtin_amdgcn_exp2f(Sacc[qt][2 * kk + (e >> 2)][e & 3] - base);
       P[qt][kk] = pk;
     }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    st.l[qt] = alpha * st.l[qt] + sum;
-    st.m[qt] = m_new;
-    // rescale the output rows this lane holds (queries 4a + q live in lanes 4a + q as columns)
+    if (!first) {
+      // rescale the rows this lane holds (query 4a + q is column 4a + q of lane 4a + q)
+      const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - base);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const float aq = __shfl(alpha, 4 * a + qq);
+      for (int qq = 0; qq < 4; ++qq) {
+        const float aq = __shfl(alpha, 4 * a + qq);
+        st.L[qt][qq] *= aq;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) st.O[qt][nt][qq] *= aq;
+        for (int nt = 0; nt < 8; ++nt) st.O[qt][nt][qq] *= aq;
+      }
     }
+    st.m[qt] = m_new;
   }
 
-  // ---- O += P V (dims d = 16 nt + n; V operand: 8 tokens 32kk + 8a.. of dim d).
-  // The block's 1 KB of value scales goes through this wave's LDS slot: each
-  // lane needs 8 scale bytes loaded by another lane of the same wave.
-  vsc_slot[lane] = vsc_regs;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint8_t* vsc = reinterpret_cast<const uint8_t*>(vsc_slot);
+  // ---- denominators: L += P . 1 (row sums of the FP16 P that the numerator uses)
+  const h8 ones = h8{1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      h8 vv = e2m1x8_to_h8(vw[nt][kk]);
-      const uint2 sw = *reinterpret_cast<const uint2*>(vsc + nt * kPage + 32 * kk + 8 * a);
-      const h2 s0 = e4m3x2_to_h2<false>(sw.x), s1 = e4m3x2_to_h2<true>(sw.x);
-      const h2 s2 = e4m3x2_to_h2<false>(sw.y), s3 = e4m3x2_to_h2<true>(sw.y);
-      const h8 sv = h8{s0[0], s0[1], s1[0], s1[1], s2[0], s2[1], s3[0], s3[1]};
-      vv = vv * sv;
+    for (int kk = 0; kk < 4; ++kk) st.L[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[qt][kk], ones, st.L[qt], 0, 0, 0);
+
+  // ---- O += P V (dims d = 16 nt + n; step kk: tokens 32a + 8kk .. of dim d; k-steps outermost)
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const uint32_t word = kk == 0 ? vr.vw[nt].x : kk == 1 ? vr.vw[nt].y : kk == 2 ? vr.vw[nt].z : vr.vw[nt].w;
+      h8 vv = e2m1x8_to_h8(word);
+      vv = vv * slot->v[nt * 16 + 4 * a + kk];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
         st.O[qt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[qt][kk], vv, st.O[qt][nt], 0, 0, 0);
     }
   }
-  // the slot is rewritten by this wave's next block: keep those stores behind these reads
+  // the slot is rewritten for this wave's next block: keep those stores behind these reads
   __builtin_amdgcn_wave_barrier();
 }
+
+constexpr int kTabLds = 2048;  // block-table rows up to this width are staged in LDS
 
 // Steps 3 (when SELECT) and 4 for one (request, group, row group); grid (groups x row groups, requests).
 // WAVES per workgroup: 8 with one query tile; 4 with two, so that each wave can
@@ -261,17 +310,21 @@ __device__ __forceinline__ void attend_block(const uint8_t* __restrict__ ks_, co
 template <int QT, bool SELECT, int KMAX, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t R, int32_t max_pages,
-    const uint8_t* __restrict__ q, float qk_scale, float v_scale, const uint8_t* __restrict__ kpages,
+    const uint8_t* __restrict__ q, float qk2, float v_scale, const uint8_t* __restrict__ kpages,
     const uint8_t* __restrict__ vpages, int32_t num_pages, const float* __restrict__ block_scores,
     int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t topk, float* __restrict__ out) {
+  constexpr int NT = WAVES * 64;
+  constexpr int NQ = QT * 16;  // query columns of the workgroup (rows nq.. are padding)
+  __shared__ int s_tab[kTabLds];
   __shared__ int s_rowsel[4 * MSA_MAX_TOPK];
   __shared__ int s_first[4 * MSA_MAX_TOPK];
   __shared__ int s_union[4 * MSA_MAX_TOPK];
+  __shared__ int s_phys[4 * MSA_MAX_TOPK];
   __shared__ int s_nu;
-  __shared__ float s_m[WAVES][QT * 16];
-  __shared__ float s_l[WAVES][QT * 16];
-  __shared__ float s_o[QT * 16][kDim];
-  __shared__ uint4 s_vsc[WAVES][64];  // value scales of each wave's current block
+  __shared__ float s_m[WAVES][NQ];
+  __shared__ float s_l[WAVES][NQ];
+  __shared__ ScaleSlot s_slot[WAVES];         // scales of each wave's current block
+  __shared__ float s_o[WAVES][NQ / 2][kDim];  // each wave's rescaled output rows (half the columns at a time)
 
   const int RG = (R + 3) / 4;
   const int g = blockIdx.x / RG, rg = blockIdx.x % RG;
@@ -279,6 +332,25 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
   const int r0 = rg * 4, nr = min(4, R - r0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, a = lane >> 4;
+
+  // ---- loads that need no context length go first: this wave's selection
+  // scores, the queries, the block-table row (staged in LDS when it fits)
+  float sc[KMAX > 0 ? KMAX : 1];
+  const int64_t row_id = ((int64_t)b * R + r0 + min(wave, nr - 1)) * kGroups + g;
+  if (SELECT && wave < nr) load_row_scores<KMAX>(block_scores + row_id * max_pages, max_pages, lane, sc);
+  h8 Q[QT][4];
+  load_q<QT>(q, b, R, r0, nr, g, lane, Q);
+  const int32_t* trow = table + (int64_t)b * max_pages;
+  const bool tab_lds = max_pages <= kTabLds;
+  if (tab_lds) {
+    constexpr int PER = kTabLds / NT;
+    int tv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) tv[i] = trow[min(tid + i * NT, max_pages - 1)];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (tid + i * NT < max_pages) s_tab[tid + i * NT] = tv[i];
+  }
   const int L = clamp_len(lens[b], max_pages);
 
   int nu;
@@ -288,14 +360,14 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
       const int r = r0 + wave;
       const int p = L - R + r;
       const int nb = p < 0 ? 0 : p / kPage + 1;
-      const int64_t row_id = ((int64_t)b * R + r) * kGroups + g;
+      const float* srow_scores = block_scores + row_id * max_pages;
       int32_t* o = sel + row_id * topk;
       int* srow = s_rowsel + wave * topk;
-      const int c = select_row<false, KMAX>(block_scores + row_id * max_pages, nb, p, topk, lane,
-                                            [&](int rank, int id) {
-                                              srow[rank] = id;
-                                              o[rank] = id;
-                                            });
+      const int c = select_core<KMAX>(sc, [&](int j) { return srow_scores[j]; }, nb, topk, lane,
+                                      [&](int rank, int id) {
+                                        srow[rank] = id;
+                                        o[rank] = id;
+                                      });
       if (lane >= c && lane < topk) {
         srow[lane] = -1;
         o[lane] = -1;
@@ -307,86 +379,128 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
   } else {
     nu = build_union(sel, cnt, b, g, R, r0, nr, topk, max_pages, s_rowsel, s_first, s_union, &s_nu);
   }
+  // physical pages of the union blocks; -1 when the table entry is out of range
+  for (int ui = tid; ui < nu; ui += NT) {
+    const int j = s_union[ui];
+    const int ph = (j >= 0 && j < max_pages) ? (tab_lds ? s_tab[j] : trow[j]) : -1;
+    s_phys[ui] = (ph >= 0 && ph < num_pages) ? ph : -1;
+  }
+  __syncthreads();
 
   AttnState<QT> st;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     st.m[qt] = -__builtin_inff();
-    st.l[qt] = 0.f;
+    st.L[qt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) st.O[qt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  if (wave < nu) {
-    h8 Q[QT][4];
-    load_q<QT>(q, b, R, r0, nr, g, lane, Q);
-    for (int ui = wave; ui < nu; ui += WAVES) {
-      const int j = s_union[ui];
-      int phys = table[(int64_t)b * max_pages + j];
-      if (phys < 0 || phys >= num_pages) continue;
-      int lim[QT];
+  // visibility of block j to this lane's query columns
+  auto block_lim = [&](int j, int (&lim)[QT]) {
+    bool part = false;
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const int rl = (qt * 16 + n) / kHpg;  // row within the row group
-        int v = -1;
-        if (rl < nr && (nr == 1 || row_has_block(s_rowsel, rl, topk, j))) v = min(kPage - 1, L - R + r0 + rl - j * kPage);
-        lim[qt] = v;
-      }
-      attend_block<QT>(kpages + ((int64_t)phys * kGroups + g) * kNvSlab,
-                       vpages + ((int64_t)phys * kGroups + g) * kNvSlab, Q, lim, qk_scale, lane, &s_vsc[wave][0], st);
+    for (int qt = 0; qt < QT; ++qt) {
+      const int rl = (qt * 16 + n) / kHpg;  // row within the row group
+      int v = kPage - 1;                    // padding columns: never stored, left unmasked
+      if (rl < nr)
+        v = (nr == 1 || row_has_block(s_rowsel, rl, topk, j)) ? min(kPage - 1, L - R + r0 + rl - j * kPage) : -1;
+      lim[qt] = v;
+      part |= v < kPage - 1;
+    }
+    return __any(part) != 0;
+  };
+  auto kslab = [&](int ph) { return kpages + ((int64_t)max(ph, 0) * kGroups + g) * kNvSlab; };
+  auto vslab = [&](int ph) { return vpages + ((int64_t)max(ph, 0) * kGroups + g) * kNvSlab; };
+  bool first = true;
+  // blocks wave, wave + WAVES, ... of the union, two at a time: the second
+  // block's keys load with the first block's, its values once the first
+  // block's keys are consumed (register budget of two waves per SIMD)
+  for (int u0 = wave; u0 < nu; u0 += 2 * WAVES) {
+    const int u1 = u0 + WAVES;
+    const bool has1 = u1 < nu;
+    const int ph0 = s_phys[u0], ph1 = has1 ? s_phys[u1] : -1;
+    KRegs K0, K1;
+    VRegs V0, V1;
+    load_k(kslab(ph0), lane, K0);
+    load_v(vslab(ph0), lane, V0);
+    load_k(kslab(ph1), lane, K1);  // page 0 stands in when there is no second block
+    auto load_v1 = [&]() { load_v(vslab(ph1), lane, V1); };
+    if (ph0 >= 0) {
+      int lim[QT];
+      const bool part = block_lim(s_union[u0], lim);
+      attend_block<QT>(K0, V0, Q, lim, part, first, qk2, lane, &s_slot[wave], st, load_v1);
+      first = false;
+    } else {
+      load_v1();
+    }
+    if (ph1 >= 0) {
+      int lim[QT];
+      const bool part = block_lim(s_union[u1], lim);
+      attend_block<QT>(K1, V1, Q, lim, part, first, qk2, lane, &s_slot[wave], st, [] {});
+      first = false;
     }
   }
 
-  // ---- merge the waves through LDS, one wave after the other (fixed order:
-  // bitwise reproducible), then normalise and store
+  // ---- merge the waves: each wave stores its rows scaled to the common max,
+  // then every thread sums its outputs over the waves in a fixed order
+  // (bitwise reproducible)
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-    if (a == 0) {
-      s_m[wave][qt * 16 + n] = st.m[qt];
-      s_l[wave][qt * 16 + n] = st.l[qt];
-    }
+  for (int qt = 0; qt < QT; ++qt) {
+    if (a == 0) s_m[wave][qt * 16 + n] = st.m[qt];
+    if (n == 0)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) s_l[wave][qt * 16 + 4 * a + qq] = st.L[qt][qq];
+  }
   __syncthreads();
+  const int nq = nr * kHpg;
+  // denominators, common maxima and this wave's factors, per O row the lane holds
   float fac[QT][4];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      const int qi = qt * 16 + 4 * a + qq;  // O row held by this lane
+      const int qi = qt * 16 + 4 * a + qq;
       float M = -__builtin_inff();
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][qi]);
       const float mine = s_m[wave][qi];
-      fac[qt][qq] = mine == -__builtin_inff() ? 0.f : __expf(mine - M);
+      fac[qt][qq] = mine == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mine - M);
     }
-  for (int w = 0; w < WAVES; ++w) {
-    if (wave == w) {
+  // the output rows go through LDS in two halves of NQ/2 rows (LDS budget)
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+  for (int half = 0; half < 2; ++half) {
+    const int q_lo = half * (NQ / 2);
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            float* dst = &s_o[qt * 16 + 4 * a + qq][16 * nt + n];
-            const float val = st.O[qt][nt][qq] * fac[qt][qq];
-            *dst = (w == 0) ? val : *dst + val;
-          }
-    }
+      for (int qq = 0; qq < 4; ++qq) {
+        const int qi = qt * 16 + 4 * a + qq;
+        if (qi >= q_lo && qi < q_lo + NQ / 2 && qi < nq)
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) s_o[wave][qi - q_lo][16 * nt + n] = st.O[qt][nt][qq] * fac[qt][qq];
+      }
     __syncthreads();
-  }
-  const int nq = nr * kHpg;
-  for (int i = tid; i < nq * (kDim / 4); i += WAVES * 64) {
-    const int qi = i / (kDim / 4), d4 = i % (kDim / 4);
-    float M = -__builtin_inff();
+    const int rows = min(NQ / 2, nq - q_lo);
+    for (int i = tid; i < rows * (kDim / 4); i += NT) {
+      const int ql = i / (kDim / 4), d4 = i % (kDim / 4);
+      const int qi = q_lo + ql;
+      float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][qi]);
-    float den = 0.f;
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][qi]);
+      float den = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-      if (s_m[w][qi] != -__builtin_inff()) den += s_l[w][qi] * __expf(s_m[w][qi] - M);
-    const float inv = den > 0.f ? v_scale / den : 0.f;
-    const float4 o4 = *reinterpret_cast<const float4*>(&s_o[qi][4 * d4]);
-    const int r = r0 + qi / kHpg, hh = qi % kHpg;
-    *reinterpret_cast<float4*>(&out[((((int64_t)b * R + r) * kGroups + g) * kHpg + hh) * kDim + 4 * d4]) =
-        make_float4(o4.x * inv, o4.y * inv, o4.z * inv, o4.w * inv);
+      for (int w = 0; w < WAVES; ++w) {
+        if (s_m[w][qi] != -__builtin_inff()) den += s_l[w][qi] * __builtin_amdgcn_exp2f(s_m[w][qi] - M);
+        const float4 o4 = *reinterpret_cast<const float4*>(&s_o[w][ql][4 * d4]);
+        acc.x += o4.x, acc.y += o4.y, acc.z += o4.z, acc.w += o4.w;
+      }
+      const float inv = den > 0.f ? v_scale / den : 0.f;
+      const int r = r0 + qi / kHpg, hh = qi % kHpg;
+      *reinterpret_cast<float4*>(&out[((((int64_t)b * R + r) * kGroups + g) * kHpg + hh) * kDim + 4 * d4]) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (half == 0 && nq > NQ / 2) __syncthreads();  // s_o is rewritten for the second half
   }
 }
 
@@ -501,11 +615,12 @@ static int launch_attend_nvfp4(const msa_batch* bt, const uint8_t* q, float q_sc
                                int32_t* cnt, int32_t topk, float* out, hipStream_t s) {
   const int R = bt->rows_per_req, P = bt->max_pages_per_req;
   const int RG = (R + 3) / 4;
-  const float qk_scale = sm_scale * kc->tensor_scale * q_scale;
+  // scores enter the kernel's softmax in base 2
+  const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   const dim3 grid(kGroups * RG, bt->num_reqs);
 #define MSA_ATTEND(QT, K)                                                                                      \
   hipLaunchKernelGGL((attend_nvfp4_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4)>), grid, dim3((QT == 1 ? 8 : 4) * 64), \
-                     0, s, bt->block_table, bt->ctx_lens, R, P, q, qk_scale, vc->tensor_scale,                   \
+                     0, s, bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale,                   \
                      (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt,  \
                      topk, out)
   const int km = SELECT ? select_kmax(P) : 8;

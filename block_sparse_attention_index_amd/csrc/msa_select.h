@@ -47,30 +47,37 @@ __device__ __forceinline__ void top3_insert(uint64_t k, uint64_t& t0, uint64_t& 
   t0 = g0 ? k : t0;
 }
 
-// Selection of one (request, row, group) by one whole wave.  `row` holds the
-// block scores (or token scores when kTok) of the row; p is the row's
-// position; n = number of blocks it sees.  Calls emit(rank, id) once for each
-// selected block (rank = position in ascending order) from the lane that
+// Scores of candidate blocks j = lane + 64 i (i < KMAX) of a block-score row
+// with `cap` entries, loaded before the row length is known: the index is
+// clamped into the row and candidates past the latest block are masked by the
+// selection.  Every load is unconditional, so they issue back to back.
+template <int KMAX>
+__device__ __forceinline__ void load_row_scores(const float* __restrict__ row, int cap, int lane,
+                                                float (&sc)[KMAX > 0 ? KMAX : 1]) {
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) sc[i] = row[min(lane + 64 * i, cap - 1)];
+}
+
+// Selection of one (request, row, group) by one whole wave, n = number of
+// blocks the row sees.  With KMAX > 0, sc holds the scores of this lane's
+// candidates (blocks lane + 64 i; entries for j >= n - 1 are ignored); with
+// KMAX == 0, score_of(j) reads them on demand.  Calls emit(rank, id) once for
+// each selected block (rank = position in ascending order) from the lane that
 // holds it, and returns the count.
-template <bool kTok, int KMAX, typename Emit>
-__device__ __forceinline__ int select_row(const float* __restrict__ row, int n, int p, int topk, int lane,
-                                          Emit emit) {
+template <int KMAX, typename ScoreOf, typename Emit>
+__device__ __forceinline__ int select_core(const float (&sc)[KMAX > 0 ? KMAX : 1], ScoreOf score_of, int n,
+                                           int topk, int lane, Emit emit) {
   if (n <= topk) {
     if (lane < n) emit(lane, lane);
     return n;
   }
   const int latest = n - 1;
-  auto key_of = [&](int j, float sc) {
-    return ((uint64_t)order_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+  auto key_of = [&](int j, float s) {
+    return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
   };
   uint64_t keys[KMAX > 0 ? KMAX : 1];
   uint64_t t0 = 0, t1 = 0, t2 = 0;
   if (KMAX > 0) {
-    // all loads unconditional (index clamped into the row) so they issue back to back;
-    // candidates past the latest block are masked to key 0 afterwards
-    float sc[KMAX > 0 ? KMAX : 1];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) sc[i] = block_score<kTok>(row, min(lane + 64 * i, latest - 1), p);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       const int j = lane + 64 * i;
@@ -78,7 +85,7 @@ __device__ __forceinline__ int select_row(const float* __restrict__ row, int n, 
       top3_insert(keys[i], t0, t1, t2);
     }
   } else {
-    for (int j = lane; j < latest; j += 64) top3_insert(key_of(j, block_score<kTok>(row, j, p)), t0, t1, t2);
+    for (int j = lane; j < latest; j += 64) top3_insert(key_of(j, score_of(j)), t0, t1, t2);
   }
   int mine = -1;  // the block this lane ends up holding in the output set
   for (int k = 0; k < topk - 1; ++k) {
@@ -106,7 +113,7 @@ __device__ __forceinline__ int select_row(const float* __restrict__ row, int n, 
             if (keys[i] < W) top3_insert(keys[i], t0, t1, t2);
         } else {
           for (int j = lane; j < latest; j += 64) {
-            const uint64_t kk = key_of(j, block_score<kTok>(row, j, p));
+            const uint64_t kk = key_of(j, score_of(j));
             if (kk < W) top3_insert(kk, t0, t1, t2);
           }
         }
@@ -122,6 +129,19 @@ __device__ __forceinline__ int select_row(const float* __restrict__ row, int n, 
   }
   if (lane < topk) emit(rank, mine);
   return topk;
+}
+
+// Selection from a score row in memory (block scores, or token scores when
+// kTok: a block then scores the max of its visible tokens); p is the row's
+// position.
+template <bool kTok, int KMAX, typename Emit>
+__device__ __forceinline__ int select_row(const float* __restrict__ row, int n, int p, int topk, int lane,
+                                          Emit emit) {
+  float sc[KMAX > 0 ? KMAX : 1];
+  const int last = max(n - 2, 0);  // highest candidate (the latest block is kept apart)
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) sc[i] = block_score<kTok>(row, min(lane + 64 * i, last), p);
+  return select_core<KMAX>(sc, [&](int j) { return block_score<kTok>(row, j, p); }, n, topk, lane, emit);
 }
 
 // Register capacity (candidates per lane) for a block-table width.

@@ -18,13 +18,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const int32_t* __restrict__ l
   if (row_id >= B * R * kGroups) return;
   const int b = row_id / (R * kGroups);
   const int r = (row_id / kGroups) % R;
+  const int64_t stride = kTok ? (int64_t)max_pages * kPage : max_pages;
+  const float* row = scores + (int64_t)row_id * stride;
+  // block scores are loaded before the row length arrives (masked by the selection)
+  float sc[KMAX > 0 ? KMAX : 1];
+  if (!kTok) load_row_scores<KMAX>(row, max_pages, lane, sc);
   const int L = clamp_len(lens[b], max_pages);
   const int p = L - R + r;
   const int n = p < 0 ? 0 : p / kPage + 1;
   int32_t* out = sel + (int64_t)row_id * topk;
-  const int64_t stride = kTok ? (int64_t)max_pages * kPage : max_pages;
-  const float* row = scores + (int64_t)row_id * stride;
-  const int c = select_row<kTok, KMAX>(row, n, p, topk, lane, [&](int rank, int id) { out[rank] = id; });
+  auto emit = [&](int rank, int id) { out[rank] = id; };
+  const int c = kTok ? select_row<true, KMAX>(row, n, p, topk, lane, emit)
+                     : select_core<KMAX>(sc, [&](int j) { return row[j]; }, n, topk, lane, emit);
   if (lane >= c && lane < topk) out[lane] = -1;
   if (lane == 0) cnt[row_id] = c;
 }
