@@ -18,6 +18,7 @@ Prints one JSON line (rank 0, one GPU).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 from types import SimpleNamespace
 import os
@@ -103,6 +104,30 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
             "sample": f"{len(rows)} of {wl.B} requests ({int(wl.lengths[rows].sum())} of "
                       f"{int(wl.lengths.sum())} context tokens), full step x{reps} in {el:.1f} s, "
                       f"scaled by context tokens"}
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_nvfp4_long_ctx_b32_64k_192k_hbm_traffic.md")
+INDEX_KERNEL_SOURCES = ["include/msa.h", "block_sparse_attention_index_amd/csrc/msa_device.h",
+                        "block_sparse_attention_index_amd/csrc/msa_index.hip"]
+
+
+def recorded_traffic():
+    """HBM bytes per index-kernel launch as the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary records them (copy-kernel calibrated), or None when the
+    summary is absent or the kernel's sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(line.strip().split(": ", 1) for line in text.splitlines()
+                  if line.strip().startswith("index-kernel-") and ": " in line)
+    h = hashlib.sha256()
+    for f in INDEX_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("index-kernel-source-sha256") != h.hexdigest():
+        return None
+    return int(fields["index-kernel-traffic-bytes-per-launch"])
 
 
 def setup(seed=0, n_replicas=2):
@@ -276,7 +301,8 @@ def main():
                    "topk_blocks": wl.topk, "block_tokens": 128, "parallelism": "single-gpu",
                    "cache_replicas": len(decs), "hip_graph": use_graph},
         "roofline": {"bound": "hbm", "kernel": "index_nvfp4_kernel (steps 1+2)", "achieved": idx_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE x 1, copy-calibrated)",
                      "bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"]},
         "step_hbm": {"algorithmic_bytes": nbytes["total"], "achieved_GBps": step_gbps,
                      "frac_of_peak": step_gbps / PEAK_HBM_GBPS, "kv_tokens_read": nbytes["kv_tokens"]},
