@@ -1,45 +1,24 @@
 // msa_insert.hip -- step 0 (cache insert with NVFP4 quantisation), the FP8
 // query quantiser and the dequantisation test aid.
 //
-// Insert: one thread per (token, cache head, 16-dim group).  Each thread
-// reads its 16 FP32 values (four 16-byte loads), derives the E4M3 group
-// scale and the sixteen E2M1 codes with the amax recipe below (every step an
-// FP32 operation with round-to-nearest-even, no contraction), and writes
-// them into the page slab of the token's slot.  Token-major slabs take the 8
-// code bytes as one 64-bit store; dim-major (value) slabs hold the codes of 8
-// consecutive tokens of one dim in a dword, so each nibble is replaced with
-// an atomic AND then OR (vector memory atomics, no read round trip) --
-// tokens inserted together may share that dword.
+// Insert: one 16-lane row (a DPP row) per (token, cache head, 16-dim
+// group), one element per lane.  The row reduces the group's amax with DPP,
+// every lane derives the E4M3 group scale and its own E2M1 code with the amax
+// recipe below (every step an FP32 operation with round-to-nearest-even, no
+// contraction), and the codes go into the page slab of the token's slot.
+// Token-major slabs: adjacent lanes pair their nibbles into a byte (one DPP
+// swap) and the even lanes store the bytes.  Dim-major (value) slabs hold the
+// codes of 8 consecutive tokens of one dim in a dword, so each lane replaces
+// its nibble with an atomic AND then OR (vector memory atomics, no read round
+// trip) -- tokens inserted together may share that dword.  One element per
+// lane keeps each lane's dependency chain to one quantisation (a single
+// IEEE division instead of sixteen in a row).
 #pragma clang fp contract(off)
 
 #include "msa_device.h"
 #include "msa_kernels.h"
 
 namespace msa {
-
-// Quantise 16 FP32 values: returns the E4M3 scale code, codes packed 2 per
-// byte (element 2i in the low nibble of byte i) in the 64-bit word.
-__device__ __forceinline__ uint32_t nvfp4_group(const float* x, float ts, uint64_t* packed) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  float t1 = amax / 6.0f;
-  float s32 = t1 / ts;
-  uint32_t sc = e4m3_encode(s32);
-  float sv = e4m3_to_f32(sc);
-  uint64_t out = 0;
-  if (sv != 0.0f) {
-    float denom = sv * ts;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float y = x[i] / denom;
-      uint32_t c = e2m1_mag(fabsf(y)) | ((__float_as_uint(x[i]) >> 28) & 0x8u);
-      out |= (uint64_t)c << (4 * i);
-    }
-  }
-  *packed = out;
-  return sc;
-}
 
 // Up to three target caches (keys, values, index keys), passed as scalars so
 // that choosing one per thread is a register select, not a memory load.
@@ -61,9 +40,11 @@ struct InsertArgs {
 __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int64_t* __restrict__ slots, int32_t n) {
   const int32_t units = A.u0 + A.u1 + A.u2;  // 16-dim groups per token over all caches
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)n * units) return;
-  const int32_t tok = (int32_t)(gid / units);
-  int32_t u = (int32_t)(gid - (int64_t)tok * units);
+  const int64_t gunit = gid >> 4;  // (token, group) of this 16-lane row
+  const int i = (int)(gid & 15);   // element within the group
+  if (gunit >= (int64_t)n * units) return;  // whole rows leave together (blockDim is a multiple of 16)
+  const int32_t tok = (int32_t)(gunit / units);
+  int32_t u = (int32_t)(gunit - (int64_t)tok * units);
   const int c = u < A.u0 ? 0 : (u < A.u0 + A.u1 ? 1 : 2);
   u -= c == 0 ? 0 : (c == 1 ? A.u0 : A.u0 + A.u1);
   uint8_t* pages = c == 0 ? A.pages0 : (c == 1 ? A.pages1 : A.pages2);
@@ -77,52 +58,46 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
 
   // Both loads go out before anything waits on them: an invalid slot only
   // predicates the stores (an early return would let the compiler sink the
-  // row loads behind the slot load).
+  // row load behind the slot load).
   const int64_t slot = slots[tok];
-  const float4* src4 = reinterpret_cast<const float4*>(src + ((int64_t)tok * heads + head) * kDim + grp * 16);
-  float4 f[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = src4[i];
+  const float x = src[((int64_t)tok * heads + head) * kDim + grp * 16 + i];
   const bool valid = slot >= 0 && slot < (int64_t)num_pages * kPage;
   const int64_t page = valid ? slot >> 7 : 0;
   const int off = (int)(slot & 127);
   if (!nvfp4) {
-    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(pages + (page * heads + head) * (int64_t)kF32Slab) +
-                                            off * kDim + grp * 16);
-    if (valid)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = f[i];
+    float* dst = reinterpret_cast<float*>(pages + (page * heads + head) * (int64_t)kF32Slab);
+    if (valid) dst[off * kDim + grp * 16 + i] = x;
     return;
   }
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[4 * i] = f[i].x;
-    x[4 * i + 1] = f[i].y;
-    x[4 * i + 2] = f[i].z;
-    x[4 * i + 3] = f[i].w;
+  // group amax over the row; NaN elements count as 0 (max(|x|, 0) drops them)
+  const float amax = wave_max16(fmaxf(fabsf(x), 0.0f));
+  const float t1 = amax / 6.0f;
+  const float s32 = t1 / ts;
+  const uint32_t sc = e4m3_encode(s32);
+  const float sv = e4m3_to_f32(sc);
+  uint32_t code = 0;
+  if (sv != 0.0f) {
+    const float denom = sv * ts;
+    const float y = x / denom;
+    code = e2m1_mag(fabsf(y)) | ((__float_as_uint(x) >> 28) & 0x8u);
   }
-  uint64_t packed;
-  const uint32_t sc = nvfp4_group(x, ts, &packed);
   uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
-  if (!valid) return;
   if (!dim_major) {
-    *reinterpret_cast<uint64_t*>(slab + off * 64 + grp * 8) = packed;
-    slab[kScaleOff + off * 8 + grp] = (uint8_t)sc;
-  } else {
-    // Clear this token's nibble, then set it: atomic AND / OR on the dword
-    // (fire-and-forget); the other 7 tokens of the dword may be written by
-    // other threads at the same time.
-    const unsigned int sh = 4u * (unsigned)(off & 7);
-    const unsigned int keep = ~(0xFu << sh);
-    unsigned int* words = reinterpret_cast<unsigned int*>(slab + grp * 16 * 64 + (off >> 3) * 4);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const unsigned int cd = (unsigned int)(packed >> (4 * i)) & 0xFu;
-      atomicAnd(words + i * 16, keep);
-      atomicOr(words + i * 16, cd << sh);
+    // element 2j in the low nibble of byte j: lane 2j takes lane 2j+1's code
+    const uint32_t hi = dpp_mov<0xB1, 0xf>(code);  // quad_perm [1,0,3,2]
+    if (valid) {
+      if ((i & 1) == 0) slab[off * 64 + grp * 8 + (i >> 1)] = (uint8_t)(code | (hi << 4));
+      if (i == 0) slab[kScaleOff + off * 8 + grp] = (uint8_t)sc;
     }
-    slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
+  } else if (valid) {
+    // dim d = 16 grp + i, token off: nibble (off & 7) of dword off/8 of the dim's 64-byte row.
+    // Clear this token's nibble, then set it (fire-and-forget atomics); the other
+    // 7 tokens of the dword may be written by other rows at the same time.
+    const unsigned int sh = 4u * (unsigned)(off & 7);
+    unsigned int* word = reinterpret_cast<unsigned int*>(slab + (grp * 16 + i) * 64 + (off >> 3) * 4);
+    atomicAnd(word, ~(0xFu << sh));
+    atomicOr(word, code << sh);
+    if (i == 0) slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
   }
 }
 
@@ -205,7 +180,7 @@ extern "C" int msa_launch_kv_insert(const float* k, const float* v, const float*
   fill(kc, k, A.pages0, A.src0, A.np0, A.h0, A.nv0, A.dm0, A.ts0, A.u0);
   fill(vc, v, A.pages1, A.src1, A.np1, A.h1, A.nv1, A.dm1, A.ts1, A.u1);
   fill(ic, idx_k, A.pages2, A.src2, A.np2, A.h2, A.nv2, A.dm2, A.ts2, A.u2);
-  const int64_t total = (int64_t)n * (A.u0 + A.u1 + A.u2);
+  const int64_t total = (int64_t)n * (A.u0 + A.u1 + A.u2) * 16;  // one 16-lane row per (token, group)
   if (total == 0) return 0;
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(kv_insert_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A, slots, n);
