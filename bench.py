@@ -246,6 +246,7 @@ def main():
     calls = {
         "insert": lambda d: d.insert(*new, stream=stream),
         "index": lambda d: d.index(q_idx, wl.q_scale, None, stream),
+        "insert_index": lambda d: d.insert_index(new[0], new[1], new[2], q_idx, wl.q_scale, None, stream),
         "topk": lambda d: d.select(stream),
         "decode": lambda d: d.attend(q, wl.q_scale, wl.sm_scale, stream),
         "select_decode": lambda d: d.select_attend(q, wl.q_scale, wl.sm_scale, stream),

@@ -58,6 +58,8 @@ def _load() -> C.CDLL:
                                         vp, vp, sz, vp]),
         "msa_select_decode": (C.c_int, [P(msa_batch), vp, i32, vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp,
                                         vp, vp, vp]),
+        "msa_insert_index_score": (C.c_int, [P(msa_batch), vp, vp, vp, vp, i32, f32, P(msa_cache), P(msa_cache),
+                                             P(msa_cache), vp, vp, vp]),
         "msa_status_str": (C.c_char_p, [C.c_int]),
         "msa_debug_dequant": (C.c_int, [P(msa_cache), vp, i32, i32, vp, vp]),
     }
@@ -174,6 +176,15 @@ def msa_index_score(batch: Batch, q_idx, q_dtype: int, q_scale: float, idx_cache
                     token_scores=None, stream=None) -> None:
     _check(lib.msa_index_score(batch.ref(), _ptr(q_idx), q_dtype, float(q_scale), idx_cache.ref(),
                                _ptr(block_scores), _ptr(token_scores), _stream(stream)), "msa_index_score")
+
+
+def msa_insert_index_score(batch: Batch, k_new, v_new, idx_new, q_idx, q_dtype: int, q_scale: float,
+                           k_cache: Cache, v_cache: Cache, idx_cache: Cache, block_scores, token_scores=None,
+                           stream=None) -> None:
+    _check(lib.msa_insert_index_score(batch.ref(), _ptr(k_new), _ptr(v_new), _ptr(idx_new), _ptr(q_idx), q_dtype,
+                                      float(q_scale), k_cache.ref(), v_cache.ref(), idx_cache.ref(),
+                                      _ptr(block_scores), _ptr(token_scores), _stream(stream)),
+           "msa_insert_index_score")
 
 
 def msa_block_maxpool_topk(batch: Batch, scores, scores_are_token_level: int, topk: int, sel_blocks, sel_count,

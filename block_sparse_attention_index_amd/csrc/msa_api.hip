@@ -147,6 +147,27 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
              : MSA_ERR_HIP;
 }
 
+int msa_insert_index_score(const msa_batch* batch, const float* k_new, const float* v_new, const float* idx_new,
+                           const void* q_idx, int32_t q_dtype, float q_scale, const msa_cache* k_cache,
+                           const msa_cache* v_cache, const msa_cache* idx_cache, float* block_scores,
+                           float* token_scores, hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if ((st = check_cache(idx_cache, 1, false, false)) != MSA_OK) return st;
+  for (const msa_cache* c : {k_cache, v_cache, idx_cache})
+    if (c->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !idx_new || !q_idx || !block_scores) return MSA_ERR_INVALID_ARG;
+  if (q_dtype != MSA_FP8_E4M3) return MSA_ERR_UNSUPPORTED;
+  if (!finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
+  return msa_launch_insert_index_score(batch, k_new, v_new, idx_new, q_idx, q_scale, k_cache, v_cache, idx_cache,
+                                       block_scores, token_scores, stream) == 0
+             ? MSA_OK
+             : MSA_ERR_HIP;
+}
+
 const char* msa_status_str(int status) {
   switch (status) {
     case MSA_OK: return "ok";

@@ -323,6 +323,8 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
   __shared__ int s_nu;
   __shared__ float s_m[WAVES][NQ];
   __shared__ float s_l[WAVES][NQ];
+  __shared__ float s_fac[WAVES][NQ];  // each wave's factor exp2(m_w - M) per query row
+  __shared__ float s_inv[NQ];         // v_scale / denominator per query row
   __shared__ ScaleSlot s_slot[WAVES];         // scales of each wave's current block
   __shared__ float s_o[WAVES][NQ / 2][kDim];  // each wave's rescaled output rows (half the columns at a time)
 
@@ -441,9 +443,10 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
     }
   }
 
-  // ---- merge the waves: each wave stores its rows scaled to the common max,
-  // then every thread sums its outputs over the waves in a fixed order
-  // (bitwise reproducible)
+  // ---- merge the waves: per query row, the common max, each wave's factor
+  // and the reciprocal denominator once; then each wave stores its rows
+  // scaled by its factor and every thread sums its outputs over the waves in a
+  // fixed order (bitwise reproducible)
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     if (a == 0) s_m[wave][qt * 16 + n] = st.m[qt];
@@ -453,19 +456,21 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
   }
   __syncthreads();
   const int nq = nr * kHpg;
-  // denominators, common maxima and this wave's factors, per O row the lane holds
-  float fac[QT][4];
+  if (tid < nq) {
+    float M = -__builtin_inff();
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][tid]);
+    float den = 0.f;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int qi = qt * 16 + 4 * a + qq;
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][qi]);
-      const float mine = s_m[wave][qi];
-      fac[qt][qq] = mine == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mine - M);
+    for (int w = 0; w < WAVES; ++w) {
+      const float mw = s_m[w][tid];
+      const float f = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      s_fac[w][tid] = f;
+      den += s_l[w][tid] * f;
     }
+    s_inv[tid] = den > 0.f ? v_scale / den : 0.f;
+  }
+  __syncthreads();
   // the output rows go through LDS in two halves of NQ/2 rows (LDS budget)
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -475,27 +480,24 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int qi = qt * 16 + 4 * a + qq;
-        if (qi >= q_lo && qi < q_lo + NQ / 2 && qi < nq)
+        if (qi >= q_lo && qi < q_lo + NQ / 2 && qi < nq) {
+          const float f = s_fac[wave][qi];
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) s_o[wave][qi - q_lo][16 * nt + n] = st.O[qt][nt][qq] * fac[qt][qq];
+          for (int nt = 0; nt < 8; ++nt) s_o[wave][qi - q_lo][16 * nt + n] = st.O[qt][nt][qq] * f;
+        }
       }
     __syncthreads();
     const int rows = min(NQ / 2, nq - q_lo);
     for (int i = tid; i < rows * (kDim / 4); i += NT) {
       const int ql = i / (kDim / 4), d4 = i % (kDim / 4);
       const int qi = q_lo + ql;
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][qi]);
-      float den = 0.f;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        if (s_m[w][qi] != -__builtin_inff()) den += s_l[w][qi] * __builtin_amdgcn_exp2f(s_m[w][qi] - M);
         const float4 o4 = *reinterpret_cast<const float4*>(&s_o[w][ql][4 * d4]);
         acc.x += o4.x, acc.y += o4.y, acc.z += o4.z, acc.w += o4.w;
       }
-      const float inv = den > 0.f ? v_scale / den : 0.f;
+      const float inv = s_inv[qi];
       const int r = r0 + qi / kHpg, hh = qi % kHpg;
       *reinterpret_cast<float4*>(&out[((((int64_t)b * R + r) * kGroups + g) * kHpg + hh) * kDim + 4 * d4]) =
           make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);

@@ -123,6 +123,53 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// ---------------------------------------------------------------- NVFP4 quantiser
+// One 16-element group on one 16-lane DPP row, element i in lane i of the
+// row: returns the E4M3 group scale and sets this lane's E2M1 code (sign in
+// bit 3), by the amax recipe -- every step one FP32 operation with
+// round-to-nearest-even:
+//   s = E4M3_sat((amax / 6) / ts);  s == 0 -> code +0;
+//   else code = sign(x) | E2M1_sat(|x / (s * ts)|).
+// NaN elements count as 0 in the amax (max(|x|, 0) drops them).
+__device__ __forceinline__ uint32_t nvfp4_row_quantize(float x, float ts, uint32_t& code) {
+  const float amax = wave_max16(fmaxf(fabsf(x), 0.0f));
+  const float t1 = amax / 6.0f;
+  const float s32 = t1 / ts;
+  const uint32_t sc = e4m3_encode(s32);
+  const float sv = e4m3_to_f32(sc);
+  code = 0;
+  if (sv != 0.0f) {
+    const float denom = sv * ts;
+    const float y = x / denom;
+    code = e2m1_mag(fabsf(y)) | ((__float_as_uint(x) >> 28) & 0x8u);
+  }
+  return sc;
+}
+
+// Store a row's group (token `off` of the slab, 16-dim group `grp`, this
+// lane's element i).  Token-major: adjacent lanes pair their nibbles into a
+// byte (element 2j in the low nibble of byte j) and the even lanes store it.
+// Dim-major: dim 16 grp + i holds the token's nibble (off & 7) in dword
+// off/8 of its 64-byte row; the nibble is cleared then set with atomic AND /
+// OR (other tokens of the dword may be written at the same time).  Lane 0
+// stores the scale.  `valid` (uniform over the row) suppresses every store.
+__device__ __forceinline__ void nvfp4_row_store(uint8_t* slab, int off, int grp, int i, uint32_t code, uint32_t sc,
+                                                bool dim_major, bool valid) {
+  if (!dim_major) {
+    const uint32_t hi = dpp_mov<0xB1, 0xf>(code);  // quad_perm [1,0,3,2]: lane 2j gets lane 2j+1's code
+    if (valid) {
+      if ((i & 1) == 0) slab[off * 64 + grp * 8 + (i >> 1)] = (uint8_t)(code | (hi << 4));
+      if (i == 0) slab[kScaleOff + off * 8 + grp] = (uint8_t)sc;
+    }
+  } else if (valid) {
+    const unsigned int sh = 4u * (unsigned)(off & 7);
+    unsigned int* word = reinterpret_cast<unsigned int*>(slab + (grp * 16 + i) * 64 + (off >> 3) * 4);
+    atomicAnd(word, ~(0xFu << sh));
+    atomicOr(word, code << sh);
+    if (i == 0) slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
+  }
+}
+
 // Context length clamped to the block-table capacity; negative read as 0.
 __device__ __forceinline__ int clamp_len(int L, int max_pages) {
   int cap = max_pages * kPage;

@@ -92,22 +92,79 @@ __device__ __forceinline__ void score_page(const PageRegs& pr, const v8i (&A)[R]
   }
 }
 
+// The step's new tokens, for the insert fused into the index launch: rows of
+// positions L_b - R .. L_b - 1 of every request ([B][R][4][128] keys and
+// values, [B][R][128] index keys, FP32), written into the NVFP4 caches (keys
+// and index keys token-major, values dim-major) at the slots the block table
+// gives them.
+struct NewRows {
+  const float* k;
+  const float* v;
+  const float* idx;
+  uint8_t* kpages;
+  uint8_t* vpages;
+  uint8_t* ipages;
+  int32_t kv_num_pages;
+  float ts_k, ts_v, ts_i;
+};
+
 // Pages [j0, j0 + PPW) of request b per wave; with PREFETCH the next page's
 // loads are issued before the current page is scored (register double buffer).
-template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1>
+// Workgroup x of request b takes page chunk (latest - x) mod gridDim.x, so the
+// chunk holding the newest tokens is dispatched first and the chunks past the
+// context (nothing to score) last; every XCD (workgroup x -> XCD x mod 8) still
+// gets an even share of each request.  With INSERT the workgroup first writes
+// the new tokens that fall in its chunk into the caches (one 16-lane row per
+// 16-element group, as the insert kernel does) and makes them visible to its
+// own waves before any page is read.
+template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1, bool INSERT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_nvfp4_kernel(const int32_t* __restrict__ table,
                                                           const int32_t* __restrict__ lens, int32_t max_pages,
                                                           const uint8_t* __restrict__ q_idx, float out_scale,
                                                           const uint8_t* __restrict__ pages, int32_t num_pages,
                                                           float* __restrict__ block_scores,
-                                                          float* __restrict__ token_scores) {
+                                                          float* __restrict__ token_scores, NewRows NR) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
-  const int j0 = (blockIdx.x * 4 + wave) * PPW;
-  if (j0 >= max_pages) return;
   const int L = clamp_len(lens[b], max_pages);
   const int npb = (L + kPage - 1) / kPage;
+  const int C = (int)gridDim.x;
+  const int latest = npb > 0 ? (npb - 1) / (4 * PPW) : 0;
+  const int chunk = (latest - (int)blockIdx.x + C) % C;
+  if (INSERT) {
+    // new tokens [max(L - R, 0), L) that lie in this chunk's token range
+    const int lo = chunk * 4 * PPW * kPage;
+    const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * PPW * kPage);
+    if (t0 < t1) {
+      const int i = threadIdx.x & 15;
+      const int nrow = (t1 - t0) * 72;  // 16-dim groups: 32 keys, 32 values, 8 index keys per token
+      for (int rr = threadIdx.x >> 4; rr < nrow; rr += 16) {
+        const int tok = t0 + rr / 72;
+        int u = rr % 72;
+        const int c = u < 32 ? 0 : (u < 64 ? 1 : 2);
+        u -= 32 * c;
+        const int heads = c == 2 ? 1 : kGroups;
+        const int head = u >> 3, grp = u & 7;
+        const int r = tok - (L - R);
+        const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
+        const float x = src[(((int64_t)b * R + r) * heads + head) * kDim + grp * 16 + i];
+        const int ph = table[(int64_t)b * max_pages + tok / kPage];
+        const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
+        uint8_t* base = c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages);
+        uint32_t code;
+        const uint32_t sc = nvfp4_row_quantize(x, c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i), code);
+        nvfp4_row_store(base + ((int64_t)(valid ? ph : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i,
+                        code, sc, c == 1, valid);
+      }
+      // the index keys just written are read back by this workgroup's waves
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
+  const int j0 = (chunk * 4 + wave) * PPW;
+  if (j0 >= max_pages) return;
   const int j1 = min(j0 + PPW, max_pages);
   const int grp = lane >> 4;  // this lane's query group (output) and fp4 lane group
   const int col = lane & 15;  // token within a 16-token chunk
@@ -219,28 +276,45 @@ __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restric
     block_scores[((int64_t)b * R * kGroups + rg) * max_pages + j] = fmaxf(red[0][rg], red[1][rg]);
 }
 
-template <int R, int PPW, bool PREFETCH, bool NT, int WPE>
+template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT>
 static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
-                             float* ts, hipStream_t s) {
+                             float* ts, const NewRows& nr, hipStream_t s) {
   dim3 grid((bt->max_pages_per_req + 4 * PPW - 1) / (4 * PPW), bt->num_reqs);
   if (ts)
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE>), grid, dim3(256), 0, s, bt->block_table,
-                       bt->ctx_lens, bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages,
-                       bs, ts);
-  else
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts);
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, nr);
+  else
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT>), grid, dim3(256), 0, s,
+                       bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, nr);
 }
 
 // One page per wave, non-temporal (streaming) loads, and an occupancy target
 // of WPE waves per SIMD: measured best on the 128K-context shapes (the
 // streaming hint alone is worth ~12%; many short waves balance the ragged
 // contexts better than a deeper per-wave pipeline).
-template <int R>
+template <int R, bool INSERT>
 static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
-                         float* ts, hipStream_t s) {
-  launch_nvfp4_cfg<R, 1, false, true, (R <= 2 ? 4 : (R <= 4 ? 3 : 2))>(bt, q, out_scale, ic, bs, ts, s);
+                         float* ts, const NewRows& nr, hipStream_t s) {
+  launch_nvfp4_cfg<R, 1, false, true, (R <= 2 ? 4 : (R <= 4 ? 3 : 2)), INSERT>(bt, q, out_scale, ic, bs, ts, nr, s);
+}
+
+template <bool INSERT>
+static int launch_nvfp4_rows(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                             float* ts, const NewRows& nr, hipStream_t s) {
+  switch (bt->rows_per_req) {
+    case 1: launch_nvfp4<1, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 2: launch_nvfp4<2, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 3: launch_nvfp4<3, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 4: launch_nvfp4<4, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 5: launch_nvfp4<5, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 6: launch_nvfp4<6, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 7: launch_nvfp4<7, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 8: launch_nvfp4<8, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace msa
@@ -263,17 +337,15 @@ extern "C" int msa_launch_index_score(const msa_batch* bt, const void* q_idx, in
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const float out_scale = ic->tensor_scale * q_scale;
-  const uint8_t* q = (const uint8_t*)q_idx;
-  switch (bt->rows_per_req) {
-    case 1: launch_nvfp4<1>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 2: launch_nvfp4<2>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 3: launch_nvfp4<3>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 4: launch_nvfp4<4>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 5: launch_nvfp4<5>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 6: launch_nvfp4<6>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 7: launch_nvfp4<7>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    case 8: launch_nvfp4<8>(bt, q, out_scale, ic, block_scores, token_scores, s); break;
-    default: return -1;
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return launch_nvfp4_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, NewRows{}, s);
+}
+
+extern "C" int msa_launch_insert_index_score(const msa_batch* bt, const float* k_new, const float* v_new,
+                                             const float* idx_new, const void* q_idx, float q_scale,
+                                             const msa_cache* kc, const msa_cache* vc, const msa_cache* ic,
+                                             float* block_scores, float* token_scores, hipStream_t s) {
+  NewRows nr{k_new, v_new, idx_new, (uint8_t*)kc->pages, (uint8_t*)vc->pages, (uint8_t*)ic->pages,
+             kc->num_pages, kc->tensor_scale, vc->tensor_scale, ic->tensor_scale};
+  const float out_scale = ic->tensor_scale * q_scale;
+  return launch_nvfp4_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, nr, s);
 }

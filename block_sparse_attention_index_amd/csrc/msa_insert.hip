@@ -69,36 +69,9 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
     if (valid) dst[off * kDim + grp * 16 + i] = x;
     return;
   }
-  // group amax over the row; NaN elements count as 0 (max(|x|, 0) drops them)
-  const float amax = wave_max16(fmaxf(fabsf(x), 0.0f));
-  const float t1 = amax / 6.0f;
-  const float s32 = t1 / ts;
-  const uint32_t sc = e4m3_encode(s32);
-  const float sv = e4m3_to_f32(sc);
-  uint32_t code = 0;
-  if (sv != 0.0f) {
-    const float denom = sv * ts;
-    const float y = x / denom;
-    code = e2m1_mag(fabsf(y)) | ((__float_as_uint(x) >> 28) & 0x8u);
-  }
-  uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
-  if (!dim_major) {
-    // element 2j in the low nibble of byte j: lane 2j takes lane 2j+1's code
-    const uint32_t hi = dpp_mov<0xB1, 0xf>(code);  // quad_perm [1,0,3,2]
-    if (valid) {
-      if ((i & 1) == 0) slab[off * 64 + grp * 8 + (i >> 1)] = (uint8_t)(code | (hi << 4));
-      if (i == 0) slab[kScaleOff + off * 8 + grp] = (uint8_t)sc;
-    }
-  } else if (valid) {
-    // dim d = 16 grp + i, token off: nibble (off & 7) of dword off/8 of the dim's 64-byte row.
-    // Clear this token's nibble, then set it (fire-and-forget atomics); the other
-    // 7 tokens of the dword may be written by other rows at the same time.
-    const unsigned int sh = 4u * (unsigned)(off & 7);
-    unsigned int* word = reinterpret_cast<unsigned int*>(slab + (grp * 16 + i) * 64 + (off >> 3) * 4);
-    atomicAnd(word, ~(0xFu << sh));
-    atomicOr(word, code << sh);
-    if (i == 0) slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
-  }
+  uint32_t code;
+  const uint32_t sc = nvfp4_row_quantize(x, ts, code);
+  nvfp4_row_store(pages + (page * heads + head) * (int64_t)kNvSlab, off, grp, i, code, sc, dim_major != 0, valid);
 }
 
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* __restrict__ x, int64_t n, float scale,

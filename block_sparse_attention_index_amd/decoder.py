@@ -2,7 +2,8 @@
 
 Plumbing only: it owns the torch tensors the C ABI writes into and issues the
 calls in order -- insert (optional), index score + max-pool, selection,
-sparse attention -- on one stream, with no host synchronisation, so the step
+sparse attention, or for NVFP4 caches the two fused launches (insert + index,
+selection + attention) -- on one stream, with no host synchronisation, so the step
 can be captured into a HIP graph.
 """
 from __future__ import annotations
@@ -10,8 +11,8 @@ from __future__ import annotations
 import torch
 
 from . import (MSA_DIM_MAJOR, MSA_F32, MSA_FP8_E4M3, MSA_NVFP4, MSA_TOKEN_MAJOR, Batch, Cache,
-               msa_block_maxpool_topk, msa_decode_workspace_bytes, msa_index_score, msa_kv_insert,
-               msa_select_decode, msa_sparse_decode)
+               msa_block_maxpool_topk, msa_decode_workspace_bytes, msa_index_score, msa_insert_index_score,
+               msa_kv_insert, msa_select_decode, msa_sparse_decode)
 
 GROUPS = 4
 HEADS = 32
@@ -45,6 +46,12 @@ class MsaDecoder:
     def index(self, q_idx, q_scale=1.0, token_scores=None, stream=None):
         msa_index_score(self.batch, q_idx, self.q_dtype, q_scale, self.idx, self.block_scores, token_scores, stream)
 
+    def insert_index(self, k, v, idx_k, q_idx, q_scale=1.0, token_scores=None, stream=None):
+        """Steps 0+1+2 in one launch (NVFP4 caches): k, v [B*R][4][128] and idx_k [B*R][128] are the rows of
+        positions L_b - R .. L_b - 1, request-major."""
+        msa_insert_index_score(self.batch, k, v, idx_k, q_idx, self.q_dtype, q_scale, self.k, self.v, self.idx,
+                               self.block_scores, token_scores, stream)
+
     def select(self, stream=None):
         msa_block_maxpool_topk(self.batch, self.block_scores, 0, self.topk, self.sel, self.cnt, stream)
 
@@ -59,12 +66,19 @@ class MsaDecoder:
 
     def step(self, q_idx, q, q_scale, sm_scale, new_tokens=None, stream=None, fused=True):
         """new_tokens: optional (k [n][4][128], v [n][4][128], idx [n][128], slots [n]) FP32 rows to insert first.
-        fused: steps 3+4 in one launch when the caches are NVFP4."""
-        if new_tokens is not None:
-            k, v, i, s = new_tokens
-            self.insert(k, v, i, s, stream)
-        self.index(q_idx, q_scale, None, stream)
-        if fused and self.k.dtype == MSA_NVFP4:
+        fused (NVFP4 caches): insert + index in one launch and selection + attention in another; the new rows
+        must then be those of positions L_b - R .. L_b - 1, request-major (their slots follow from the block
+        table and are not read)."""
+        nvfp4 = self.k.dtype == MSA_NVFP4
+        if fused and nvfp4 and new_tokens is not None:
+            k, v, i, _ = new_tokens
+            self.insert_index(k, v, i, q_idx, q_scale, None, stream)
+        else:
+            if new_tokens is not None:
+                k, v, i, s = new_tokens
+                self.insert(k, v, i, s, stream)
+            self.index(q_idx, q_scale, None, stream)
+        if fused and nvfp4:
             self.select_attend(q, q_scale, sm_scale, stream)
         else:
             self.select(stream)

@@ -145,6 +145,26 @@ int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, 
                     const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream);
 
 /*
+ * Steps 0+1+2 in one launch (NVFP4 caches, FP8 index queries): the step's
+ * new tokens are written into the caches, then the index scores are computed
+ * with them included.  The new tokens of request b are its last R positions,
+ * L_b - R .. L_b - 1 (positions below 0 are skipped), at the slots its
+ * block-table row gives them: k_new, v_new [B][R][4][128] FP32, idx_new
+ * [B][R][128] FP32, row r of request b at position L_b - R + r.  They are
+ * quantised and stored exactly as msa_kv_insert_nvfp4 stores them (keys and
+ * index keys token-major, values dim-major), a token whose page id is outside
+ * the pool is not written, and block_scores / token_scores come out as
+ * msa_index_score computes them after that insert.  The pages holding new
+ * tokens must not be shared between requests.  The pages fuse the insert
+ * into the QKV GEMM epilogue (vLLM post, "QKV GEMM + norm + RoPE + KV 插入融合");
+ * here the workgroup that scores a new token's page writes the token first.
+ */
+int msa_insert_index_score(const msa_batch* batch, const float* k_new, const float* v_new, const float* idx_new,
+                           const void* q_idx, int32_t q_dtype, float q_scale, const msa_cache* k_cache,
+                           const msa_cache* v_cache, const msa_cache* idx_cache, float* block_scores,
+                           float* token_scores, hipStream_t stream);
+
+/*
  * Step 3: block selection (vLLM post, "how MSA works").  For each (b, r, g)
  * with n visible blocks: all blocks if n <= topk; otherwise the latest block
  * n-1 plus the topk-1 best of the others by score, ties to the lower block

@@ -96,6 +96,19 @@ def test_host_validation_without_gpu(lib):
                                  C.byref(v), fake, fake, fake, None) == -1
     assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k),
                                  C.byref(v), fake, fake, None, None) == -1
+    # fused insert + index: NVFP4 caches, FP8 queries, every row pointer present, value cache dim-major
+    f32i = Cache(0, 0, 1, 16, 1.0, fake)
+    ins = lib.msa_insert_index_score
+    assert ins(C.byref(good), fake, fake, fake, fake, 1, C.c_float(1.0), C.byref(f32k), C.byref(v), C.byref(f32i),
+               fake, None, None) == -2
+    assert ins(C.byref(good), None, fake, fake, fake, 1, C.c_float(1.0), C.byref(k), C.byref(v), C.byref(idx), fake,
+               None, None) == -1
+    assert ins(C.byref(good), fake, fake, fake, fake, 0, C.c_float(1.0), C.byref(k), C.byref(v), C.byref(idx), fake,
+               None, None) == -2
+    assert ins(C.byref(good), fake, fake, fake, fake, 1, C.c_float(1.0), C.byref(k), C.byref(k), C.byref(idx), fake,
+               None, None) == -2
+    assert ins(C.byref(good), fake, fake, fake, fake, 1, C.c_float(0.0), C.byref(k), C.byref(v), C.byref(idx), fake,
+               None, None) == -1
 
 
 def test_workspace_size_formula(lib):

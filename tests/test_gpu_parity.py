@@ -42,12 +42,21 @@ def _dev(x, dt=None):
     return t if dt is None else t.to(dt)
 
 
-def gpu_setup(M, wl):
+def gpu_setup(M, wl, hold_new=False):
+    """Device caches holding the workload's rows.  hold_new: leave out each request's
+    last R positions (the step's new tokens) and return their rows, request-major
+    [B*R], as a fourth value (k, v, idx, slots); rows of positions below 0 are zero
+    with slot -1 (no token)."""
     from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
 
     k, v, idx = make_caches(wl.cache == "nvfp4", wl.num_pages, wl.tensor_scale)
     batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R)
     dec = MsaDecoder(batch, k, v, idx, wl.topk)
+    n_new = wl.B * wl.R
+    nk = np.zeros((n_new, 4, 128), np.float32)
+    nv = np.zeros((n_new, 4, 128), np.float32)
+    ni = np.zeros((n_new, 128), np.float32)
+    nslots = np.full(n_new, -1, np.int64)
     # one request at a time, so that full-size caches never sit in host memory at once
     if wl.prefix_tokens:
         pos = np.arange(wl.prefix_tokens, dtype=np.int64)
@@ -57,7 +66,16 @@ def gpu_setup(M, wl):
         pos = wl.own_positions(b)
         if pos.shape[0]:
             xi, xk, xv = W.request_rows(wl, b)
-            dec.insert(_dev(xk), _dev(xv), _dev(xi), _dev(wl.slots(b, pos)))
+            keep = pos < int(wl.lengths[b]) - wl.R if hold_new else np.ones(pos.shape[0], bool)
+            if keep.any():
+                dec.insert(_dev(xk[keep]), _dev(xv[keep]), _dev(xi[keep]), _dev(wl.slots(b, pos[keep])))
+            if hold_new:
+                for r in range(wl.R):
+                    p_ = int(wl.lengths[b]) - wl.R + r
+                    if p_ >= wl.prefix_tokens:
+                        j = p_ - wl.prefix_tokens
+                        nk[b * wl.R + r], nv[b * wl.R + r], ni[b * wl.R + r] = xk[j], xv[j], xi[j]
+                        nslots[b * wl.R + r] = wl.slots(b, np.array([p_]))[0]
         if wl.num_pages > 4096 and b % 8 == 7:
             print(f"  inserted requests 0..{b}", flush=True)
     qi32, q32 = W.queries(wl)
@@ -67,6 +85,8 @@ def gpu_setup(M, wl):
     else:
         q_idx, q = _dev(qi32), _dev(q32)
     torch.cuda.synchronize()
+    if hold_new:
+        return dec, q_idx, q, (_dev(nk), _dev(nv), _dev(ni), _dev(nslots))
     return dec, q_idx, q
 
 
@@ -270,9 +290,13 @@ def test_sparse_decode_on_oracle_selection(M, oracle, case):
 
 
 # ---------------------------------------------------------------- whole step
-def _check_full_step(M, oracle, wl, sample=None, fused=True):
-    dec, q_idx, q = gpu_setup(M, wl)
-    dec.step(q_idx, q, wl.q_scale, wl.sm_scale, fused=fused)
+def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False):
+    if new_rows:  # the step itself inserts each request's last R rows
+        dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True)
+        dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new, fused=fused)
+    else:
+        dec, q_idx, q = gpu_setup(M, wl)
+        dec.step(q_idx, q, wl.q_scale, wl.sm_scale, fused=fused)
     torch.cuda.synchronize()
     g_sel, g_cnt = dec.sel.cpu().numpy(), dec.cnt.cpu().numpy()
     g_out = dec.out.cpu().numpy().astype(np.float64)
@@ -344,6 +368,36 @@ def test_full_step(M, oracle, case, fused):
     _check_full_step(M, oracle, wl, fused=fused)
 
 
+@pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r8"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_full_step_with_new_rows(M, oracle, case, fused):
+    """The step inserts each request's R new rows itself (fused: insert + index in one
+    launch), then indexes, selects and attends; checked against the oracle on all rows."""
+    wl = CASES[case]()
+    _print_case(f"{case} new rows fused={fused}", wl)
+    _check_full_step(M, oracle, wl, fused=fused, new_rows=True)
+
+
+@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8"])
+def test_insert_index_equals_separate_calls(M, oracle, case):
+    """msa_insert_index_score: the caches bitwise as msa_kv_insert_nvfp4 writes them (and as
+    the oracle writes them), and bitwise the block scores of msa_index_score after that insert."""
+    wl = CASES[case]()
+    _print_case(case, wl)
+    dec_a, q_idx, _, (nk, nv, ni, ns) = gpu_setup(M, wl, hold_new=True)
+    dec_b, _, _, _ = gpu_setup(M, wl, hold_new=True)
+    dec_a.insert(nk, nv, ni, ns)
+    dec_a.index(q_idx, wl.q_scale)
+    dec_b.block_scores.fill_(3.0)
+    dec_b.insert_index(nk, nv, ni, q_idx, wl.q_scale)
+    torch.cuda.synchronize()
+    ci, ck, cv = oracle_caches(oracle, wl)
+    for ca, cb, co in ((dec_a.idx, dec_b.idx, ci), (dec_a.k, dec_b.k, ck), (dec_a.v, dec_b.v, cv)):
+        assert torch.equal(ca.pages, cb.pages)
+        assert np.array_equal(cb.pages.cpu().numpy(), co.bytes)
+    assert torch.equal(dec_a.block_scores.view(torch.int32), dec_b.block_scores.view(torch.int32))
+
+
 @pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8"])
 def test_select_decode_equals_separate_calls(M, oracle, case):
     """msa_select_decode: same selection as msa_block_maxpool_topk and bitwise the same
@@ -373,21 +427,27 @@ def test_full_step_deterministic(M, oracle):
     assert torch.equal(a[2].view(torch.int32), dec.out.view(torch.int32))
 
 
-def test_graph_replay_matches_eager(M, oracle):
-    """The step has no memset nodes and no host sync: capture it and replay it several times."""
+@pytest.mark.parametrize("new_rows", [False, True])
+def test_graph_replay_matches_eager(M, oracle, new_rows):
+    """The step has no memset nodes and no host sync: capture it and replay it several
+    times (with new rows, every replay inserts the same rows again, which is idempotent)."""
     wl = CASES["cfg3_small"]()
-    _print_case("graph replay", wl)
-    dec, q_idx, q = gpu_setup(M, wl)
-    dec.step(q_idx, q, wl.q_scale, wl.sm_scale)
+    _print_case(f"graph replay new_rows={new_rows}", wl)
+    if new_rows:
+        dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True)
+    else:
+        (dec, q_idx, q), new = gpu_setup(M, wl), None
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new)
     torch.cuda.synchronize()
     eager = dec.out.clone()
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        dec.step(q_idx, q, wl.q_scale, wl.sm_scale)
+        dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new)
     for _ in range(3):
         dec.out.zero_()
         dec.sel.fill_(-7)
+        dec.block_scores.fill_(1.0)
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(dec.out.view(torch.int32), eager.view(torch.int32))
