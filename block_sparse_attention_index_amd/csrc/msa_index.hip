@@ -110,10 +110,13 @@ struct NewRows {
 
 // Pages [j0, j0 + PPW) of request b per wave; with PREFETCH the next page's
 // loads are issued before the current page is scored (register double buffer).
-// Workgroup x of request b takes page chunk (latest - x) mod gridDim.x, so the
-// chunk holding the newest tokens is dispatched first and the chunks past the
-// context (nothing to score) last; every XCD (workgroup x -> XCD x mod 8) still
-// gets an even share of each request.  With INSERT the workgroup first writes
+// One-dimensional grid of B x C workgroups (C = page chunks per request row of
+// the table).  Workgroups 0..B-1 take the chunk holding each request's newest
+// tokens, so the chunks that insert the step's tokens start first; workgroup
+// B + b*(C-1) + i then takes chunk i of request b, skipping the newest one
+// (i >= latest_b -> chunk i + 1).  Each request's remaining chunks are
+// consecutive workgroups, which the dispatcher deals round-robin to the 8
+// XCDs, and the chunks past a context (nothing to score) close its run.  With INSERT the workgroup first writes
 // the new tokens that fall in its chunk into the caches (one 16-lane row per
 // 16-element group, as the insert kernel does) and makes them visible to its
 // own waves before any page is read.
@@ -123,15 +126,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                                           const uint8_t* __restrict__ q_idx, float out_scale,
                                                           const uint8_t* __restrict__ pages, int32_t num_pages,
                                                           float* __restrict__ block_scores,
-                                                          float* __restrict__ token_scores, NewRows NR) {
+                                                          float* __restrict__ token_scores, int32_t B,
+                                                          NewRows NR) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int b = blockIdx.y;
+  const int C = (max_pages + 4 * PPW - 1) / (4 * PPW);
+  const int id = (int)blockIdx.x;
+  const int b = id < B ? id : (id - B) / max(C - 1, 1);
+  const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
   const int L = clamp_len(lens[b], max_pages);
   const int npb = (L + kPage - 1) / kPage;
-  const int C = (int)gridDim.x;
   const int latest = npb > 0 ? (npb - 1) / (4 * PPW) : 0;
-  const int chunk = (latest - (int)blockIdx.x + C) % C;
+  const int chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
   if (INSERT) {
     // new tokens [max(L - R, 0), L) that lie in this chunk's token range
     const int lo = chunk * 4 * PPW * kPage;
@@ -279,15 +285,15 @@ __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restric
 template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT>
 static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                              float* ts, const NewRows& nr, hipStream_t s) {
-  dim3 grid((bt->max_pages_per_req + 4 * PPW - 1) / (4 * PPW), bt->num_reqs);
+  const dim3 grid((unsigned)(((bt->max_pages_per_req + 4 * PPW - 1) / (4 * PPW)) * bt->num_reqs));
   if (ts)
     hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, nr);
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, nr);
   else
     hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, nr);
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, nr);
 }
 
 // One page per wave, non-temporal (streaming) loads, and an occupancy target
