@@ -191,6 +191,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--layers-per-graph", type=int, default=10,
+                    help="layer-steps captured in one HIP graph, as one forward pass over that many sparse layers "
+                         "captures them (replicas alternate as the layers' own caches); the largest divisor of "
+                         "--steps not above this value is used")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the oracle's timed sample")
     args = ap.parse_args()
@@ -209,16 +213,23 @@ def main():
     def run_step(i, s):
         decs[i % len(decs)].step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new, stream=s)
 
-    graphs = []
+    # layer-steps per graph: the largest divisor of K not above the request, a multiple of the
+    # replica count (so the replicas keep alternating across replays) unless it is 1
+    per_graph = 1
+    for d_ in range(min(args.layers_per_graph, args.steps), 0, -1):
+        if args.steps % d_ == 0 and (d_ % len(decs) == 0 or d_ == 1):
+            per_graph = d_
+            break
+    graph = None
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             run_step(i, stream)
         if use_graph:
-            for r in range(len(decs)):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    run_step(r, stream)
-                graphs.append(g)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(per_graph):
+                    run_step(i, stream)
+            graph.replay()  # untimed
     torch.cuda.synchronize()
 
     # ---- timed region: K whole steps
@@ -228,17 +239,19 @@ def main():
     wall0 = time.perf_counter()
     with torch.cuda.stream(stream):
         t_start.record(stream)
-        for i in range(args.steps):
-            if use_graph:
-                graphs[i % len(graphs)].replay()
-            else:
+        if use_graph:
+            for _ in range(args.steps // per_graph):
+                graph.replay()
+        else:
+            for i in range(args.steps):
                 run_step(i, stream)
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (events), wall {wall / args.steps * 1e6:.1f} us/step")
+    log(f"timed {args.steps} steps ({per_graph} per graph): {ms_step * 1e3:.1f} us/step (events), "
+        f"wall {wall / args.steps * 1e6:.1f} us/step")
 
     # ---- per-kernel durations: for each kernel, a HIP graph of `reps` back-to-back
     # launches (alternating cache replicas) replayed between two HIP events on
@@ -301,7 +314,8 @@ def main():
                    "ctx_tokens_mean": float(wl.lengths.mean()), "ctx_tokens_min": int(wl.lengths.min()),
                    "ctx_tokens_max": int(wl.lengths.max()), "kv_cache": "nvfp4", "index_cache": "nvfp4",
                    "topk_blocks": wl.topk, "block_tokens": 128, "parallelism": "single-gpu",
-                   "cache_replicas": len(decs), "hip_graph": use_graph},
+                   "cache_replicas": len(decs), "hip_graph": use_graph,
+                   "layer_steps_per_graph": per_graph if use_graph else None},
         "roofline": {"bound": "hbm", "kernel": "index_nvfp4_kernel with the insert fused in (steps 0-2)",
                      "achieved": idx_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic(),

@@ -326,6 +326,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
   __shared__ float s_fac[WAVES][NQ];  // each wave's factor exp2(m_w - M) per query row
   __shared__ float s_inv[NQ];         // v_scale / denominator per query row
   __shared__ ScaleSlot s_slot[WAVES];         // scales of each wave's current block
+  __shared__ SelectScratch s_sel[SELECT ? 4 : 1];  // selection scratch of waves 0..nr-1
   __shared__ float s_o[WAVES][NQ / 2][kDim];  // each wave's rescaled output rows (half the columns at a time)
 
   const int RG = (R + 3) / 4;
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
       const float* srow_scores = block_scores + row_id * max_pages;
       int32_t* o = sel + row_id * topk;
       int* srow = s_rowsel + wave * topk;
-      const int c = select_core<KMAX>(sc, [&](int j) { return srow_scores[j]; }, nb, topk, lane,
+      const int c = select_fast<KMAX>(sc, [&](int j) { return srow_scores[j]; }, nb, topk, lane, &s_sel[SELECT ? wave : 0],
                                       [&](int rank, int id) {
                                         srow[rank] = id;
                                         o[rank] = id;

@@ -131,6 +131,120 @@ __device__ __forceinline__ int select_core(const float (&sc)[KMAX > 0 ? KMAX : 1
   return topk;
 }
 
+// Per-wave LDS scratch of select_fast.
+constexpr int kSelCand = 512;  // candidate capacity (beyond it: the round-based selection)
+struct SelectScratch {
+  uint64_t heads[64];
+  uint64_t cand[kSelCand];
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t lanes_below_mask(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// The same selection as select_core with no serial rounds.  With need =
+// topk - 1 blocks to pick besides the latest:
+//  1. each lane takes the max of its candidate keys (its "head");
+//  2. T0 = the need-th largest head, found by ranking the 64 heads against
+//     each other (keys are distinct; lanes with no candidate hold 0, below
+//     every key, and at least need lanes hold one);
+//  3. every key among the need largest is >= T0 (the need heads >= T0 already
+//     outrank anything below it), and only the need lanes with heads >= T0
+//     can hold such keys, so the keys >= T0 -- compacted by ballot into LDS in
+//     ascending block order -- are at most need * KMAX candidates;
+//  4. a candidate's rank among the candidates is its rank among all keys: the
+//     need best are picked, and a ballot prefix count gives each its place in
+//     ascending block order.
+// Beyond kSelCand candidates (adversarial scores with KMAX = 0) it runs
+// select_core instead.  S: this wave's scratch.
+template <int KMAX, typename ScoreOf, typename Emit>
+__device__ __forceinline__ int select_fast(const float (&sc)[KMAX > 0 ? KMAX : 1], ScoreOf score_of, int n, int topk,
+                                           int lane, SelectScratch* S, Emit emit) {
+  if (n <= topk) {
+    if (lane < n) emit(lane, lane);
+    return n;
+  }
+  const int latest = n - 1;
+  const int need = topk - 1;
+  if (need == 0) {
+    if (lane == 0) emit(0, latest);
+    return 1;
+  }
+  auto key_of = [&](int j, float s) {
+    return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+  };
+  auto kmax = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  uint64_t keys[KMAX > 0 ? KMAX : 1];
+  uint64_t head = 0;
+  if (KMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      const int j = lane + 64 * i;
+      keys[i] = j < latest ? key_of(j, sc[i]) : 0ull;
+    }
+    // pairwise tree: independent compares issue back to back
+    uint64_t t[KMAX > 0 ? KMAX : 1];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) t[i] = keys[i];
+#pragma unroll
+    for (int w = 1; w < KMAX; w *= 2)
+#pragma unroll
+      for (int i = 0; i + w < KMAX; i += 2 * w) t[i] = kmax(t[i], t[i + w]);
+    head = t[0];
+  } else {
+    for (int j = lane; j < latest; j += 64) head = kmax(head, key_of(j, score_of(j)));
+  }
+  S->heads[lane] = head;
+  wave_lds_sync();
+  int rk = 0;
+#pragma unroll 16
+  for (int i = 0; i < 64; ++i) rk += S->heads[i] > head ? 1 : 0;
+  const uint64_t at = __ballot(rk == need - 1);
+  const int src = __ffsll((unsigned long long)at) - 1;
+  const uint64_t T0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(head >> 32), src) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)head, src);
+  // candidates >= T0 in ascending block order (block j = lane + 64 i: i-major, then lane)
+  const uint64_t below = lanes_below_mask(lane);
+  int C = 0;
+  auto add = [&](uint64_t k) {
+    const bool c = k >= T0;
+    const uint64_t bal = __ballot(c);
+    const int off = C + __popcll(bal & below);
+    if (c && off < kSelCand) S->cand[off] = k;
+    C += __popcll(bal);
+  };
+  if (KMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) add(keys[i]);
+  } else {
+    for (int base = 0; base < latest; base += 64) {
+      const int j = base + lane;
+      add(j < latest ? key_of(j, score_of(min(j, latest - 1))) : 0ull);
+    }
+  }
+  if (C > kSelCand) return select_core<KMAX>(sc, score_of, n, topk, lane, emit);
+  wave_lds_sync();
+  int placed = 0;
+  for (int base = 0; base < C; base += 64) {
+    const int c = base + lane;
+    const uint64_t mine = c < C ? S->cand[c] : ~0ull;
+    int r = 0;
+    for (int m = 0; m < C; ++m) r += S->cand[m] > mine ? 1 : 0;
+    const bool pick = c < C && r < need;
+    const uint64_t bal = __ballot(pick);
+    if (pick) emit(placed + __popcll(bal & below), (int)(0xFFFFFFFFu - (uint32_t)mine));
+    placed += __popcll(bal);
+  }
+  if (lane == 0) emit(need, latest);
+  return topk;
+}
+
 // Selection from a score row in memory (block scores, or token scores when
 // kTok: a block then scores the max of its visible tokens); p is the row's
 // position.

@@ -1,8 +1,8 @@
 // msa_topk.hip -- step 3 as a kernel of its own: top-k block selection with
 // the latest block kept (vLLM M3.1 post, "MiniMax 稀疏注意力的工作原理";
 // "MiniMax goes sparse", section 1 Step 1).  One wave per (request, row,
-// group) runs select_row (msa_select.h); the ids are stored ascending, -1
-// padded, with their count.
+// group) runs select_fast (block scores) or select_row (token scores)
+// (msa_select.h); the ids are stored ascending, -1 padded, with their count.
 #include "msa_kernels.h"
 #include "msa_select.h"
 
@@ -13,6 +13,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const int32_t* __restrict__ l
                                                    int32_t max_pages, const float* __restrict__ scores,
                                                    int32_t topk, int32_t* __restrict__ sel,
                                                    int32_t* __restrict__ cnt) {
+  __shared__ SelectScratch scratch[4];
   const int lane = threadIdx.x & 63;
   const int row_id = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row_id >= B * R * kGroups) return;
@@ -29,7 +30,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const int32_t* __restrict__ l
   int32_t* out = sel + (int64_t)row_id * topk;
   auto emit = [&](int rank, int id) { out[rank] = id; };
   const int c = kTok ? select_row<true, KMAX>(row, n, p, topk, lane, emit)
-                     : select_core<KMAX>(sc, [&](int j) { return row[j]; }, n, topk, lane, emit);
+                     : select_fast<KMAX>(sc, [&](int j) { return row[j]; }, n, topk, lane, &scratch[threadIdx.x >> 6],
+                                         emit);
   if (lane >= c && lane < topk) out[lane] = -1;
   if (lane == 0) cnt[row_id] = c;
 }

@@ -262,6 +262,30 @@ def test_topk_exact_on_shared_scores(M, oracle, topk, P):
     assert np.array_equal(sel.cpu().numpy(), rs2)
 
 
+@pytest.mark.parametrize("topk,P", [(16, 300), (16, 1400), (16, 2500), (16, 4000), (64, 300), (64, 1400)])
+def test_topk_lane_periodic_scores(M, oracle, topk, P):
+    """Scores that depend only on the block index modulo 64 (one register lane of the
+    selection), so whole lanes tie: every key of the best lanes is a candidate, which
+    fills the candidate buffer and, past its capacity, takes the round-based path."""
+    print(f"[case] lane-periodic topk={topk} P={P}", flush=True)
+    B, R = 3, 1
+    lens = np.array([P * 128, P * 128 - 77, 64 * 128 * 3 + 5], np.int32)
+    table = np.zeros((B, P), np.int32)
+    j = np.arange(P)
+    base = (100.0 - (j % 64)).astype(np.float32)
+    scores = np.broadcast_to(base, (B, R, 4, P)).copy()
+    scores[1] = np.broadcast_to((j % 64).astype(np.float32), (R, 4, P))  # increasing with the lane
+    scores[2, 0, 1] = np.float32(1.0)  # all equal: the lowest block indices win
+    batch = M.Batch(_dev(table), _dev(lens), R)
+    sel = torch.empty((B, R, 4, topk), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, R, 4), dtype=torch.int32, device="cuda")
+    M.msa_block_maxpool_topk(batch, _dev(scores), 0, topk, sel, cnt)
+    bt = oracle.OracleBatch(table, lens, R)
+    rs, rc = oracle.select(bt, scores.astype(np.float64), topk)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(sel.cpu().numpy(), rs)
+
+
 # ---------------------------------------------------------------- step 4
 def _out_err(got, ref):
     return np.abs(got - ref).max(-1) / np.maximum(np.abs(ref).max(-1), 1e-30)
