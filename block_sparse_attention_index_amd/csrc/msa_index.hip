@@ -30,25 +30,50 @@ namespace msa {
 // One page of the index cache as one wave holds it: lane l keeps, for each
 // 16-token chunk c, the 16 code bytes of token 16c + l%16, dims
 // 32*(l/16)..+31 (the fp4 operand), and the 8 scale bytes of that token.
+// With WIDE scale loads the 1 KB of scales arrives as one 16-byte load per
+// lane (tokens 2l, 2l+1) and is redistributed through a 1 KB LDS slot of the
+// wave (stage_scales), instead of eight 8-byte loads per lane.
 struct PageRegs {
   uint4 cw[8];
   uint2 sw[8];
+  uint4 sraw;
 };
 
 // NT: non-temporal loads (the index is read once per step; streaming hint).
-template <bool NT>
-__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ slab, int col, int grp) {
+template <bool NT, bool WIDE = false>
+__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ slab, int col, int grp,
+                                          int lane = 0) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
     const u4* cp = reinterpret_cast<const u4*>(slab + (16 * c + col) * 64 + 16 * grp);
-    const u2* sp = reinterpret_cast<const u2*>(slab + kScaleOff + (16 * c + col) * 8);
     const u4 cv = NT ? __builtin_nontemporal_load(cp) : *cp;
-    const u2 sv = NT ? __builtin_nontemporal_load(sp) : *sp;
     pr.cw[c] = make_uint4(cv.x, cv.y, cv.z, cv.w);
-    pr.sw[c] = make_uint2(sv.x, sv.y);
+    if (!WIDE) {
+      const u2* sp = reinterpret_cast<const u2*>(slab + kScaleOff + (16 * c + col) * 8);
+      const u2 sv = NT ? __builtin_nontemporal_load(sp) : *sp;
+      pr.sw[c] = make_uint2(sv.x, sv.y);
+    }
   }
+  if (WIDE) {
+    const u4* sp = reinterpret_cast<const u4*>(slab + kScaleOff + 16 * lane);
+    const u4 sv = NT ? __builtin_nontemporal_load(sp) : *sp;
+    pr.sraw = make_uint4(sv.x, sv.y, sv.z, sv.w);
+  }
+}
+
+// WIDE: every lane's 8 scale bytes per chunk from the wave's LDS slot.
+__device__ __forceinline__ void stage_scales(PageRegs& pr, uint4* slot, int lane, int col) {
+  slot[lane] = pr.sraw;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint2* s2 = reinterpret_cast<const uint2*>(slot);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) pr.sw[c] = s2[16 * c + col];
+  // the slot is rewritten by this wave's next page: keep those stores behind these reads
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Scores of one resident page for all R rows; returns per-row maxima (unscaled).
@@ -120,7 +145,8 @@ struct NewRows {
 // the new tokens that fall in its chunk into the caches (one 16-lane row per
 // 16-element group, as the insert kernel does) and makes them visible to its
 // own waves before any page is read.
-template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1, bool INSERT = false>
+template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1, bool INSERT = false,
+          bool WIDE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_nvfp4_kernel(const int32_t* __restrict__ table,
                                                           const int32_t* __restrict__ lens, int32_t max_pages,
                                                           const uint8_t* __restrict__ q_idx, float out_scale,
@@ -221,6 +247,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     finish(j, m);
   };
 
+  static_assert(!(WIDE && PREFETCH), "wide scale loads are staged per page: no prefetch");
+  __shared__ uint4 s_scales[WIDE ? 4 : 1][64];
   PageRegs buf[PREFETCH ? 2 : 1];
   int phys_cur = __shfl(my_phys, 0);
   if (PREFETCH && phys_cur >= 0) load_page<NT>(buf[0], pages + (int64_t)phys_cur * kNvSlab, col, grp);
@@ -230,7 +258,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (j >= j1) break;
     PageRegs& cur = buf[PREFETCH ? (k & 1) : 0];
     const int phys_next = (k + 1 < PPW) ? __shfl(my_phys, k + 1) : -1;
-    if (!PREFETCH && phys_cur >= 0) load_page<NT>(cur, pages + (int64_t)phys_cur * kNvSlab, col, grp);
+    if (!PREFETCH && phys_cur >= 0) {
+      load_page<NT, WIDE>(cur, pages + (int64_t)phys_cur * kNvSlab, col, grp, lane);
+      if (WIDE) stage_scales(cur, &s_scales[WIDE ? wave : 0][0], lane, col);
+    }
     if (PREFETCH && phys_next >= 0 && j + 1 < j1)
       load_page<NT>(buf[(k + 1) & 1], pages + (int64_t)phys_next * kNvSlab, col, grp);
     if (phys_cur >= 0) {
@@ -282,28 +313,31 @@ __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restric
     block_scores[((int64_t)b * R * kGroups + rg) * max_pages + j] = fmaxf(red[0][rg], red[1][rg]);
 }
 
-template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT>
+template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT, bool WIDE>
 static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                              float* ts, const NewRows& nr, hipStream_t s) {
   const dim3 grid((unsigned)(((bt->max_pages_per_req + 4 * PPW - 1) / (4 * PPW)) * bt->num_reqs));
   if (ts)
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT, WIDE>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
                        (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, nr);
   else
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
                        (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, nr);
 }
 
-// One page per wave, non-temporal (streaming) loads, and an occupancy target
-// of WPE waves per SIMD: measured best on the 128K-context shapes (the
-// streaming hint alone is worth ~12%; many short waves balance the ragged
-// contexts better than a deeper per-wave pipeline).
+// One page per wave, non-temporal (streaming) loads, wide scale loads, and an
+// occupancy target of WPE waves per SIMD: measured best on the 128K-context
+// shapes (the streaming hint alone is worth ~12%, one 16-byte scale load per
+// lane instead of eight 8-byte ones ~4.5%; many short waves balance the
+// ragged contexts better than a deeper per-wave pipeline, and 4-6 waves per
+// SIMD are equal while 8 thrash).
 template <int R, bool INSERT>
 static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                          float* ts, const NewRows& nr, hipStream_t s) {
-  launch_nvfp4_cfg<R, 1, false, true, (R <= 2 ? 4 : (R <= 4 ? 3 : 2)), INSERT>(bt, q, out_scale, ic, bs, ts, nr, s);
+  launch_nvfp4_cfg<R, 1, false, true, (R <= 2 ? 4 : (R <= 4 ? 3 : 2)), INSERT, true>(bt, q, out_scale, ic, bs, ts, nr,
+                                                                                    s);
 }
 
 template <bool INSERT>
