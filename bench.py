@@ -31,8 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense FP16 matrix peak
 METRIC = "MSA decode layer-steps/s + achieved HBM GB/s (% of peak), 128K ctx NVFP4 KV"
-CONFIG_ID = 3
+CONFIG_ID = 3  # the 128K-context batch the metric is quoted on
 
 
 def log(msg):
@@ -40,28 +41,35 @@ def log(msg):
 
 
 def algorithmic_bytes(wl, sel, cnt):
-    """Minimum bytes one step moves (per the method): the whole index of every
+    """Minimum bytes one step moves (per the method): the index of every
     context (72 B/token), K+V of the selected tokens of each (request, group)
     (144 B/token: 64+8 B of K, 64+8 B of V), queries, outputs, block table,
-    and the insert of the new rows (FP32 in, NVFP4 out)."""
+    and the insert of the new rows (FP32 in, NVFP4 out).  A physical page is
+    counted once however many requests (a shared prefix) or rows select it."""
     B, R = wl.B, wl.R
-    idx = int(wl.lengths.astype(np.int64).sum()) * 72
-    kv_tokens = 0
-    p = wl.lengths.astype(np.int64)[:, None] - R + np.arange(R)[None, :]
+    L = wl.lengths.astype(np.int64)
+    idx_tok = {}  # physical page -> tokens of it some request's context covers
+    for b in range(B):
+        npb = -(-int(L[b]) // 128)
+        for j in range(npb):
+            ph = int(wl.block_table[b, j])
+            idx_tok[ph] = max(idx_tok.get(ph, 0), min(128, int(L[b]) - 128 * j))
+    idx = sum(idx_tok.values()) * 72
+    kv_lim = {}  # (group, physical page) -> last token any selecting row sees
+    p = L[:, None] - R + np.arange(R)[None, :]
     for b in range(B):
         for g in range(4):
-            blocks = set()
-            lim = {}
             for r in range(R):
                 for j in sel[b, r, g, : cnt[b, r, g]]:
                     j = int(j)
-                    blocks.add(j)
-                    lim[j] = max(lim.get(j, -1), min(127, int(p[b, r]) - 128 * j))
-            kv_tokens += sum(lim[j] + 1 for j in blocks)
+                    key = (g, int(wl.block_table[b, j]))
+                    kv_lim[key] = max(kv_lim.get(key, -1), min(127, int(p[b, r]) - 128 * j))
+    kv_tokens = sum(v + 1 for v in kv_lim.values())
     kv = kv_tokens * 144
     q_bytes = B * R * 4 * 128 + B * R * 32 * 128  # FP8 index queries + queries
     out_bytes = B * R * 32 * 128 * 4
-    table = B * wl.max_pages * 4 + B * 4
+    P = wl.prefix_pages
+    table = (P + B * (wl.max_pages - P)) * 4 + B * 4
     insert = B * R * (9 * 128 * 4 + 9 * 72)  # FP32 rows in, NVFP4 bytes out
     return {"index": idx + B * R * 4 * 128 + table, "insert_index": idx + B * R * 4 * 128 + table + insert, "kv": kv,
             "total": idx + kv + q_bytes + out_bytes + table + insert, "kv_tokens": kv_tokens}
@@ -80,6 +88,11 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
     ci = O.OracleCache(dt, O.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
     ck = O.OracleCache(dt, O.TOKEN_MAJOR, 4, wl.num_pages, wl.tensor_scale)
     cv = O.OracleCache(dt, O.DIM_MAJOR, 4, wl.num_pages, wl.tensor_scale)
+    if wl.prefix_tokens:
+        xi, xk, xv = W.prefix_rows(wl)
+        s = wl.slots(0, np.arange(wl.prefix_tokens, dtype=np.int64))
+        ci.write(s, xi), ck.write(s, xk), cv.write(s, xv)
+        del xi, xk, xv
     for b in rows:
         pos = wl.own_positions(int(b))
         xi, xk, xv = W.request_rows(wl, int(b))
@@ -131,7 +144,7 @@ def recorded_traffic(key="insert-index-kernel-traffic-bytes-per-launch"):
     return int(fields[key]) if key in fields else None
 
 
-def setup(seed=0, n_replicas=2):
+def setup(seed=0, n_replicas=2, config=CONFIG_ID):
     """Device state of the benchmark workload: filled caches (``n_replicas`` copies),
     decoders, the step's new rows and quantised queries."""
     import torch
@@ -141,14 +154,19 @@ def setup(seed=0, n_replicas=2):
     from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
 
     dev = torch.device("cuda:0")
-    wl = W.make_workload(CONFIG_ID, seed=seed)
+    wl = W.make_workload(config, seed=seed)
     log(f"workload {wl.name}: B={wl.B} R={wl.R} tokens={int(wl.lengths.sum())} pages={wl.num_pages}")
 
     # ---- caches (replica 0 filled by the insert kernel from device-drawn rows)
     k0, v0, i0 = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
     table = torch.from_numpy(wl.block_table).to(dev)
     lens = torch.from_numpy(wl.lengths).to(dev)
-    batch = M.Batch(table, lens, wl.R)
+    batch = M.Batch(table, lens, wl.R, wl.prefix_pages)
+    if wl.prefix_tokens:  # the shared prefix is written once, into the pages every request's table names
+        xi, xk, xv = W.torch_rows(wl, 0, dev, prefix=True)
+        slots = torch.from_numpy(wl.slots(0, np.arange(wl.prefix_tokens, dtype=np.int64))).to(dev)
+        M.msa_kv_insert(xk, xv, xi, slots, k0, v0, i0)
+        del xi, xk, xv
     for b in range(wl.B):
         pos = wl.own_positions(b)
         xi, xk, xv = W.torch_rows(wl, b, dev)
@@ -189,6 +207,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--config", type=int, default=CONFIG_ID, choices=[2, 3, 4, 5],
+                    help="workload: 3 = 32 requests at 64K-192K tokens (the default, the metric's own); "
+                         "2 = 8 x 32K; 4 = 16 requests x 4 speculative rows; 5 = 64 requests sharing a "
+                         "256K-token prefix")
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--layers-per-graph", type=int, default=10,
@@ -204,7 +226,7 @@ def main():
               "(the context-parallel indexer design is documented, not built).", file=sys.stderr)
         sys.exit(2)
 
-    st = setup(args.seed, args.replicas)
+    st = setup(args.seed, args.replicas, args.config)
     torch, M, W, wl, decs, q_idx, q, new = st.torch, st.M, st.W, st.wl, st.decs, st.q_idx, st.q, st.new
 
     stream = torch.cuda.Stream()
@@ -265,6 +287,15 @@ def main():
         "decode": lambda d: d.attend(q, wl.q_scale, wl.sm_scale, stream),
         "select_decode": lambda d: d.select_attend(q, wl.q_scale, wl.sm_scale, stream),
     }
+    P = wl.prefix_pages
+    if P:
+        # the prefix kernel alone: a batch whose table ends with the shared pages leaves the
+        # per-request scan nothing to do
+        from block_sparse_attention_index_amd.decoder import MsaDecoder
+
+        pbatch = M.Batch(st.batch.block_table[:, :P].contiguous(), st.batch.ctx_lens, wl.R, P)
+        pdec = {id(d): MsaDecoder(pbatch, d.k, d.v, d.idx, wl.topk) for d in decs}
+        calls["prefix"] = lambda d: pdec[id(d)].index(q_idx, wl.q_scale, None, stream)
     us = {}
     for name, call in calls.items():
         g = torch.cuda.CUDAGraph()
@@ -287,6 +318,7 @@ def main():
     nbytes = algorithmic_bytes(wl, sel, cnt)
     steps_per_s = 1e3 / ms_step
     idx_gbps = nbytes["insert_index"] / (us["insert_index"] * 1e-6) / 1e9
+    prefix_flops = 2 * 128 * 128 * P * wl.B * wl.R * 4  # dims x tokens x index queries
     step_gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
 
     cpu = None
@@ -318,12 +350,18 @@ def main():
                    "layer_steps_per_graph": per_graph if use_graph else None},
         "roofline": {"bound": "hbm", "kernel": "index_nvfp4_kernel with the insert fused in (steps 0-2)",
                      "achieved": idx_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic(),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic() if args.config == CONFIG_ID else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE x 1, copy-calibrated)",
                      "bytes_per_launch": nbytes["insert_index"], "avg_launch_us": us["insert_index"],
                      "plain_scan": {"bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"],
                                     "achieved": nbytes["index"] / (us["index"] * 1e-6) / 1e9,
-                                    "traffic": recorded_traffic("index-kernel-traffic-bytes-per-launch")}},
+                                    "traffic": recorded_traffic("index-kernel-traffic-bytes-per-launch")
+                                    if args.config == CONFIG_ID else None}},
+        "prefix_mfma": None if not P else {
+            "kernel": "prefix_index_kernel (shared-prefix scores on v_mfma_f32_16x16x32_f16)",
+            "bound": "mfma", "flops_per_launch": prefix_flops, "avg_launch_us": us["prefix"],
+            "achieved": prefix_flops / (us["prefix"] * 1e-6) / 1e12, "peak": PEAK_F16_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": prefix_flops / (us["prefix"] * 1e-6) / 1e12 / PEAK_F16_MFMA_TFLOPS},
         "step_hbm": {"algorithmic_bytes": nbytes["total"], "achieved_GBps": step_gbps,
                      "frac_of_peak": step_gbps / PEAK_HBM_GBPS, "kv_tokens_read": nbytes["kv_tokens"]},
         "kernel_us": us,

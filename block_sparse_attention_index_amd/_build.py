@@ -15,7 +15,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["msa_api.hip", "msa_insert.hip", "msa_index.hip", "msa_topk.hip", "msa_attn.hip"]
+SOURCES = ["msa_api.hip", "msa_insert.hip", "msa_index.hip", "msa_prefix.hip", "msa_topk.hip", "msa_attn.hip"]
+# Per-file flags.  msa_prefix.hip: max-pooling of matrix-core results is
+# compiled without NaN canonicalisation (every fmaxf there would otherwise
+# first quieten its operand with an extra v_max x, x); the hardware maximum
+# still returns the non-NaN operand, which is what fmaxf returns.
+EXTRA_FLAGS = {"msa_prefix.hip": ["-fno-honor-nans"]}
 
 
 def build(verbose: bool = False, jobs: int = 5) -> str:
@@ -31,7 +36,7 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = common + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = common + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -114,13 +114,6 @@ struct AttnState {
   v4f O[QT][8];  // unnormalised output: rows 4*(lane/16)+q (queries), dims 16*nt + lane%16
 };
 
-typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 nt_load4(const uint8_t* p) {
-  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // Query operands: column n of tile qt = query qi = 16qt + n -> (row qi/8, head qi%8 of group g),
 // dims 32a + 8ks + 0..7 for k-step ks (the K operand uses the same dim order).
 template <int QT>

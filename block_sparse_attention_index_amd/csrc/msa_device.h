@@ -87,6 +87,13 @@ __device__ __forceinline__ h8 e2m1x8_to_h8(uint32_t w) {
 }
 
 // ---------------------------------------------------------------- slabs
+// 16-byte load with the streaming (non-temporal) hint: data read once per step.
+__device__ __forceinline__ uint4 nt_load4(const uint8_t* p) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ const uint8_t* slab_ptr(const uint8_t* pages, int64_t page, int heads, int head,
                                                    int slab_bytes) {
   return pages + (page * heads + head) * (int64_t)slab_bytes;

@@ -135,8 +135,11 @@ struct NewRows {
 
 // Pages [j0, j0 + PPW) of request b per wave; with PREFETCH the next page's
 // loads are issued before the current page is scored (register double buffer).
+// The scan covers pages p0 .. max_pages-1 of every request (p0 > 0: the
+// leading pages are shared by all requests and scored once, by
+// prefix_index_kernel); chunk i is pages p0 + 4*PPW*i ...
 // One-dimensional grid of B x C workgroups (C = page chunks per request row of
-// the table).  Workgroups 0..B-1 take the chunk holding each request's newest
+// the table past p0).  Workgroups 0..B-1 take the chunk holding each request's newest
 // tokens, so the chunks that insert the step's tokens start first; workgroup
 // B + b*(C-1) + i then takes chunk i of request b, skipping the newest one
 // (i >= latest_b -> chunk i + 1).  Each request's remaining chunks are
@@ -153,20 +156,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                                           const uint8_t* __restrict__ pages, int32_t num_pages,
                                                           float* __restrict__ block_scores,
                                                           float* __restrict__ token_scores, int32_t B,
-                                                          NewRows NR) {
+                                                          int32_t p0, NewRows NR) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int C = (max_pages + 4 * PPW - 1) / (4 * PPW);
+  const int C = (max_pages - p0 + 4 * PPW - 1) / (4 * PPW);
   const int id = (int)blockIdx.x;
   const int b = id < B ? id : (id - B) / max(C - 1, 1);
   const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
   const int L = clamp_len(lens[b], max_pages);
   const int npb = (L + kPage - 1) / kPage;
-  const int latest = npb > 0 ? (npb - 1) / (4 * PPW) : 0;
+  const int latest = npb > p0 ? (npb - 1 - p0) / (4 * PPW) : 0;
   const int chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
   if (INSERT) {
     // new tokens [max(L - R, 0), L) that lie in this chunk's token range
-    const int lo = chunk * 4 * PPW * kPage;
+    const int lo = (p0 + chunk * 4 * PPW) * kPage;
     const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * PPW * kPage);
     if (t0 < t1) {
       const int i = threadIdx.x & 15;
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   }
-  const int j0 = (chunk * 4 + wave) * PPW;
+  const int j0 = p0 + (chunk * 4 + wave) * PPW;
   if (j0 >= max_pages) return;
   const int j1 = min(j0 + PPW, max_pages);
   const int grp = lane >> 4;  // this lane's query group (output) and fp4 lane group
@@ -316,15 +319,18 @@ __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restric
 template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT, bool WIDE>
 static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                              float* ts, const NewRows& nr, hipStream_t s) {
-  const dim3 grid((unsigned)(((bt->max_pages_per_req + 4 * PPW - 1) / (4 * PPW)) * bt->num_reqs));
+  const int p0 = ic->dtype == MSA_NVFP4 ? bt->shared_prefix_pages : 0;
+  const int chunks = (bt->max_pages_per_req - p0 + 4 * PPW - 1) / (4 * PPW);
+  if (chunks <= 0) return;  // every page is shared: the prefix kernel scored them all
+  const dim3 grid((unsigned)(chunks * bt->num_reqs));
   if (ts)
     hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT, WIDE>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, nr);
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
   else
     hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, nr);
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
 }
 
 // One page per wave, non-temporal (streaming) loads, wide scale loads, and an
@@ -376,6 +382,7 @@ extern "C" int msa_launch_index_score(const msa_batch* bt, const void* q_idx, in
                          ic->num_pages, block_scores, token_scores);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   const float out_scale = ic->tensor_scale * q_scale;
   return launch_nvfp4_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, NewRows{}, s);
 }
@@ -386,6 +393,7 @@ extern "C" int msa_launch_insert_index_score(const msa_batch* bt, const float* k
                                              float* block_scores, float* token_scores, hipStream_t s) {
   NewRows nr{k_new, v_new, idx_new, (uint8_t*)kc->pages, (uint8_t*)vc->pages, (uint8_t*)ic->pages,
              kc->num_pages, kc->tensor_scale, vc->tensor_scale, ic->tensor_scale};
+  if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   const float out_scale = ic->tensor_scale * q_scale;
   return launch_nvfp4_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, nr, s);
 }

@@ -96,12 +96,23 @@ typedef struct {
   void* pages;        /* device, num_pages * num_heads * slab bytes        */
 } msa_cache;
 
-/* One decode step's batch (the struct itself is host memory). */
+/*
+ * One decode step's batch (the struct itself is host memory).
+ * shared_prefix_pages = P > 0 declares that entries 0..P-1 of every
+ * block-table row name the same physical pages (a prefix every request
+ * shares).  With an NVFP4 index cache the indexer then reads each of those
+ * pages once and scores it for all B*R*4 index queries together, on the
+ * matrix cores, and scans only pages P.. per request; the pages are taken
+ * from row 0 of the table, and rows whose other entries differ get row 0's
+ * scores (undefined results, not checked on the device).  Contexts shorter
+ * than the prefix are fine (invisible tokens are masked as usual).  With an
+ * F32 index cache P is not used.  0 <= P <= max_pages_per_req.
+ */
 typedef struct {
   int32_t num_reqs;            /* B >= 1                                        */
   int32_t rows_per_req;        /* R in 1..MSA_MAX_ROWS (speculative rows)       */
   int32_t max_pages_per_req;   /* row stride of block_table (>= 1)              */
-  int32_t shared_prefix_pages; /* leading pages identical in every row (hint), 0 if none */
+  int32_t shared_prefix_pages; /* P: leading table entries shared by every row, 0 if none */
   const int32_t* block_table;  /* device [B][max_pages_per_req] physical page ids */
   const int32_t* ctx_lens;     /* device [B] L_b, new rows included              */
 } msa_batch;
@@ -155,7 +166,9 @@ int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, 
  * index keys token-major, values dim-major), a token whose page id is outside
  * the pool is not written, and block_scores / token_scores come out as
  * msa_index_score computes them after that insert.  The pages holding new
- * tokens must not be shared between requests.  The pages fuse the insert
+ * tokens must not be shared between requests: in particular every new row
+ * lies past the shared prefix, L_b - R >= 128 * shared_prefix_pages
+ * (otherwise the result is undefined).  The pages fuse the insert
  * into the QKV GEMM epilogue (vLLM post, "QKV GEMM + norm + RoPE + KV 插入融合");
  * here the workgroup that scores a new token's page writes the token first.
  */

@@ -42,15 +42,16 @@ def _dev(x, dt=None):
     return t if dt is None else t.to(dt)
 
 
-def gpu_setup(M, wl, hold_new=False):
+def gpu_setup(M, wl, hold_new=False, shared=True):
     """Device caches holding the workload's rows.  hold_new: leave out each request's
     last R positions (the step's new tokens) and return their rows, request-major
     [B*R], as a fourth value (k, v, idx, slots); rows of positions below 0 are zero
-    with slot -1 (no token)."""
+    with slot -1 (no token).  shared: declare the workload's shared prefix pages in
+    the batch (the indexer then scores them once for all requests)."""
     from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
 
     k, v, idx = make_caches(wl.cache == "nvfp4", wl.num_pages, wl.tensor_scale)
-    batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R)
+    batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R, wl.prefix_pages if shared else 0)
     dec = MsaDecoder(batch, k, v, idx, wl.topk)
     n_new = wl.B * wl.R
     nk = np.zeros((n_new, 4, 128), np.float32)
@@ -104,6 +105,12 @@ CASES = {
     "ragged": lambda: W.make_workload(3, seed=5, lengths=[1, 127, 128, 129, 2047, 2048, 2049, 5000], R=1),
     "ragged_r4": lambda: W.make_workload(4, seed=6, lengths=[0, 2, 3, 4, 131, 2051, 2052, 7000], R=4),
     "r3": lambda: W.make_workload(4, seed=7, B=2, len_div=64, R=3),
+    # shared prefix of 32 pages (4,096 tokens); 70 requests x 4 groups = 280 index queries span
+    # several query tiles of the prefix kernel, the last one partial
+    "prefix_wide": lambda: W.make_workload(5, seed=9, B=70, len_div=64),
+    # contexts shorter than, equal to and just past the shared prefix, two rows each
+    "prefix_short": lambda: W.make_workload(5, seed=10, len_div=64, R=2,
+                                            lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 9000)]),
     "r8": lambda: W.make_workload(4, seed=8, B=2, len_div=64, R=8),
 }
 
@@ -199,7 +206,7 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 
 # ---------------------------------------------------------------- steps 1+2
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
-                                  "ragged_r4", "r3", "r8"])
+                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -383,7 +390,7 @@ def _sampled_caches(oracle, wl, rows):
 
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
-                                  "ragged_r4", "r3", "r8"])
+                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
@@ -392,7 +399,8 @@ def test_full_step(M, oracle, case, fused):
     _check_full_step(M, oracle, wl, fused=fused)
 
 
-@pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r8"])
+@pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged", "ragged_r4", "r8",
+                                  "prefix_wide"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step_with_new_rows(M, oracle, case, fused):
     """The step inserts each request's R new rows itself (fused: insert + index in one
@@ -493,6 +501,17 @@ def test_full_size_config4_sampled(M, oracle):
     wl = W.make_workload(4, seed=0)
     _print_case("config 4 full size", wl)
     _check_full_step(M, oracle, wl, sample=[0, 5])
+
+
+def test_full_size_config5_sampled(M, oracle):
+    """The shared-prefix workload at full size (64 requests on one 262,144-token
+    prefix + 1K-8K private tokens each), with the step inserting its new rows, in
+    the bench's launch configuration; the oracle checks two sampled requests."""
+    wl = W.make_workload(5, seed=0)
+    _print_case("config 5 full size", wl)
+    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths))]
+    _check_full_step(M, oracle, wl, sample=rows, new_rows=True)
+
 
 
 def test_abi_errors_on_device(M):
