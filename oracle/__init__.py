@@ -26,6 +26,7 @@ PAGE = 128
 DIM = 128
 NVFP4_SLAB = 9216
 F32_SLAB = PAGE * DIM * 4
+FP8_SLAB = PAGE * DIM
 
 _lib = None
 
@@ -45,6 +46,8 @@ def lib() -> C.CDLL:
         L.ref_nvfp4_quantize_group.restype = None
         L.ref_nvfp4_quantize_group.argtypes = [vp, f32, vp, vp]
         L.ref_nvfp4_value.restype, L.ref_nvfp4_value.argtypes = f64, [u8, u8, f32]
+        L.ref_fp8_quantize.restype, L.ref_fp8_quantize.argtypes = u8, [f32, f32]
+        L.ref_fp8_value.restype, L.ref_fp8_value.argtypes = f64, [u8, f32]
         L.ref_cache_write.restype, L.ref_cache_write.argtypes = C.c_int, [vp, i64, C.c_int, vp]
         L.ref_cache_write_many.restype, L.ref_cache_write_many.argtypes = i64, [vp, vp, i64, vp]
         L.ref_cache_value.restype, L.ref_cache_value.argtypes = f64, [vp, i64, C.c_int, C.c_int, C.c_int]
@@ -114,6 +117,18 @@ def nvfp4_value(code: int, scale: int, tensor_scale: float) -> float:
     return lib().ref_nvfp4_value(code, scale, C.c_float(tensor_scale))
 
 
+def fp8_quantize(x, tensor_scale: float) -> np.ndarray:
+    """FP8 cache codes of FP32 values: E4M3(x / tensor_scale)."""
+    x = np.asarray(x, dtype=np.float32)
+    L = lib()
+    ts = C.c_float(tensor_scale)
+    return np.array([L.ref_fp8_quantize(float(v), ts) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def fp8_value(code: int, tensor_scale: float) -> float:
+    return lib().ref_fp8_value(code, C.c_float(tensor_scale))
+
+
 def quantize_queries(x, q_scale: float = 1.0) -> np.ndarray:
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     out = np.zeros(x.shape, dtype=np.uint8)
@@ -146,7 +161,7 @@ class OracleCache:
     def __init__(self, dtype: int, layout: int, num_heads: int, num_pages: int, tensor_scale: float = 1.0):
         self.dtype, self.layout, self.num_heads, self.num_pages = dtype, layout, num_heads, num_pages
         self.tensor_scale = float(np.float32(tensor_scale))
-        self.slab = F32_SLAB if dtype == F32 else NVFP4_SLAB
+        self.slab = {F32: F32_SLAB, FP8_E4M3: FP8_SLAB, NVFP4: NVFP4_SLAB}[dtype]
         self.bytes = np.zeros(num_pages * num_heads * self.slab, dtype=np.uint8)
         self._s = _RefCache(dtype, layout, num_heads, num_pages, self.tensor_scale, self.bytes.ctypes.data)
 

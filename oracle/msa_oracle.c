@@ -34,6 +34,8 @@
 #define REF_NVFP4_GROUP 16  /* elements per E4M3 scale (from 34,560/61,440 B, [P2 M3.1 changes]) */
 #define REF_NVFP4_SLAB 9216 /* 128 tokens x (64 B codes + 8 B scales) */
 #define REF_F32_SLAB (REF_PAGE * REF_DIM * 4)
+#define REF_FP8_SLAB (REF_PAGE * REF_DIM) /* one byte per element: 128 B per token per head, the pages'
+                                            FP8 index-key cost [P2 how MSA works] */
 
 enum { REF_F32 = 0, REF_FP8_E4M3 = 1, REF_NVFP4 = 2 };
 enum { REF_TOKEN_MAJOR = 0, REF_DIM_MAJOR = 1 };
@@ -149,6 +151,22 @@ double ref_nvfp4_value(uint8_t code, uint8_t scale, float tensor_scale) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* FP8 cache element.  The pages name an FP8 cache beside NVFP4 and give its
+ * cost -- 128 B of index keys and 1,024 B of K/V (4 heads x 128 dims) per
+ * token and layer [P2 how MSA works], 61,440 B per token over the model
+ * [P2 M3.1 changes] -- i.e. one byte per element; they give no scale
+ * granularity.  Reading taken: E4M3 elements with one FP32 scale per cache
+ * tensor, as for the NVFP4 tensor scale:
+ *   code  = E4M3(x / tensor_scale)   FP32 division, RNE, saturating (NaN -> 0x7F)
+ *   value = e4m3 * tensor_scale      exact in double                         */
+uint8_t ref_fp8_quantize(float x, float tensor_scale) {
+  volatile float y = x / tensor_scale;
+  return ref_e4m3_encode(y);
+}
+
+double ref_fp8_value(uint8_t code, float tensor_scale) { return ref_e4m3_value(code) * (double)tensor_scale; }
+
+/* ------------------------------------------------------------------------- */
 /* Paged cache.  One slab per (page, head); page p, head h starts at byte
  * (p * num_heads + h) * slab_bytes.  Slab layouts:
  *   F32 token-major : float [128 tokens][128 dims]
@@ -158,8 +176,10 @@ double ref_nvfp4_value(uint8_t code, uint8_t scale, float tensor_scale) {
  *   NVFP4 dim-major (V):
  *       codes  [128 dims][64 B]    (byte i of dim d: tokens 2i lo nibble, 2i+1 hi)
  *       scales [8 groups][128 tokens] (byte (j, t): scale of token t, dims 16j..)
- * The quantisation group is always 16 consecutive dims of one token; only the
- * placement of the bytes differs between the two NVFP4 layouts.            */
+ *   FP8 token-major (K and index keys): [128 tokens][128 dims], one E4M3 byte each
+ *   FP8 dim-major (V): [128 dims][128 tokens]
+ * The NVFP4 quantisation group is always 16 consecutive dims of one token;
+ * only the placement of the bytes differs between the two layouts.          */
 typedef struct {
   int32_t dtype;
   int32_t layout;
@@ -169,7 +189,9 @@ typedef struct {
   uint8_t* pages;
 } ref_cache;
 
-static int64_t slab_bytes(const ref_cache* c) { return c->dtype == REF_F32 ? REF_F32_SLAB : REF_NVFP4_SLAB; }
+static int64_t slab_bytes(const ref_cache* c) {
+  return c->dtype == REF_F32 ? REF_F32_SLAB : (c->dtype == REF_FP8_E4M3 ? REF_FP8_SLAB : REF_NVFP4_SLAB);
+}
 
 static uint8_t* slab(const ref_cache* c, int64_t page, int head) {
   return c->pages + (page * c->num_heads + head) * slab_bytes(c);
@@ -184,6 +206,16 @@ int ref_cache_write(const ref_cache* c, int64_t slot, int head, const float* x) 
   uint8_t* s = slab(c, page, head);
   if (c->dtype == REF_F32) {
     memcpy(s + (int64_t)t * REF_DIM * 4, x, REF_DIM * 4);
+    return 0;
+  }
+  if (c->dtype == REF_FP8_E4M3) {
+    for (int d = 0; d < REF_DIM; ++d) {
+      uint8_t code = ref_fp8_quantize(x[d], c->tensor_scale);
+      if (c->layout == REF_TOKEN_MAJOR)
+        s[t * REF_DIM + d] = code;
+      else
+        s[d * REF_PAGE + t] = code;
+    }
     return 0;
   }
   for (int j = 0; j < REF_DIM / REF_NVFP4_GROUP; ++j) {
@@ -236,6 +268,8 @@ double ref_cache_value(const ref_cache* c, int64_t page, int head, int t, int d)
     memcpy(&v, s + ((int64_t)t * REF_DIM + d) * 4, 4);
     return (double)v;
   }
+  if (c->dtype == REF_FP8_E4M3)
+    return ref_fp8_value(c->layout == REF_TOKEN_MAJOR ? s[t * REF_DIM + d] : s[d * REF_PAGE + t], c->tensor_scale);
   uint8_t code, sc;
   if (c->layout == REF_TOKEN_MAJOR) {
     uint8_t b = s[t * 64 + d / 2];

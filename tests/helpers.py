@@ -10,8 +10,8 @@ import workload as W
 
 def oracle_caches(o, wl):
     """Fill the oracle's own caches from the seeded FP32 rows (oracle quantiser)."""
-    dt = o.F32 if wl.cache == "f32" else o.NVFP4
-    vlayout = o.DIM_MAJOR if dt == o.NVFP4 else o.TOKEN_MAJOR
+    dt = {"f32": o.F32, "nvfp4": o.NVFP4, "fp8": o.FP8_E4M3}[wl.cache]
+    vlayout = o.TOKEN_MAJOR if dt == o.F32 else o.DIM_MAJOR
     idx = o.OracleCache(dt, o.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
     k = o.OracleCache(dt, o.TOKEN_MAJOR, wl.G, wl.num_pages, wl.tensor_scale)
     v = o.OracleCache(dt, vlayout, wl.G, wl.num_pages, wl.tensor_scale)
@@ -95,10 +95,16 @@ def _e4m3_table():
     return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
 
 
-def decode_pages_f64(raw, nvfp4: bool, dim_major: bool, heads: int, num_pages: int, tensor_scale: float):
+def decode_pages_f64(raw, nvfp4: bool, dim_major: bool, heads: int, num_pages: int, tensor_scale: float,
+                     fp8: bool = False):
     """Exact float64 values [pages][heads][128 tok][128 dim] of a page pool, decoded from
-    its bytes by the documented slab layout (test-side, independent of the oracle)."""
+    its bytes by the documented slab layout (test-side, independent of the oracle).
+    fp8: one E4M3 byte per element, [tok][dim] (token-major) or [dim][tok], times the
+    tensor scale."""
     raw = np.asarray(raw, dtype=np.uint8)
+    if fp8:
+        v = _e4m3_table()[raw.reshape(num_pages, heads, 128, 128)] * tensor_scale
+        return np.swapaxes(v, -1, -2) if dim_major else v
     if not nvfp4:
         return raw.view(np.float32).reshape(num_pages, heads, 128, 128).astype(np.float64)
     slabs = raw.reshape(num_pages, heads, 9216)

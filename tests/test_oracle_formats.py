@@ -218,3 +218,73 @@ def test_queries_e4m3(oracle):
     assert np.array_equal(got, want)
     dec = oracle.decode_queries(got, oracle.FP8_E4M3, 0.5)
     assert np.array_equal(dec, torch.from_numpy(want).view(torch.float8_e4m3fn).double().numpy() * 0.5)
+
+
+# ---------------------------------------------------------------- FP8 cache elements
+def test_fp8_byte_cost_matches_pages(oracle):
+    """One byte per element: 128 B of index keys and 1,024 B of K+V (4 heads x 128 dims) per
+    token and layer, the pages' FP8 figures; 61,440 B per token is 60 such layers, the same
+    layer count as NVFP4's 34,560 B at 576 B per layer."""
+    facts = {r[0]: int(r[1]) for r in read_golden("page_facts.txt")}
+    idx = oracle.OracleCache(oracle.FP8_E4M3, oracle.TOKEN_MAJOR, 1, 1, 1.0)
+    assert idx.bytes.size // 128 == facts["index_bytes_per_token_fp8"]
+    kv = oracle.OracleCache(oracle.FP8_E4M3, oracle.TOKEN_MAJOR, facts["kv_heads"], 1, 1.0)
+    assert 2 * kv.bytes.size // 128 == facts["dense_kv_bytes_per_token_fp8"]
+    layers = facts["fp8_kv_bytes_per_token"] // facts["dense_kv_bytes_per_token_fp8"]
+    assert layers * facts["dense_kv_bytes_per_token_fp8"] == facts["fp8_kv_bytes_per_token"]
+    assert layers * 576 == facts["nvfp4_kv_bytes_per_token"]
+
+
+def test_fp8_quantize_matches_torch(oracle):
+    """In range, an FP8 cache code is PyTorch's float8_e4m3fn rounding of the FP32 quotient x / ts."""
+    rng = np.random.default_rng(21)
+    ts = float(np.float32(8 / 448))
+    x = np.clip(rng.standard_normal(20000).astype(np.float32) * 2, -7.9, 7.9).astype(np.float32)
+    x[:50] = 0.0
+    x[50:100] = rng.standard_normal(50).astype(np.float32) * 1e-4  # E4M3 subnormals
+    got = oracle.fp8_quantize(x, ts)
+    y = torch.from_numpy(x) / torch.tensor(ts, dtype=torch.float32)
+    want = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    vals = _torch_e4m3_values()
+    assert np.array_equal(np.array([oracle.fp8_value(int(c), ts) for c in got[:200]]), vals[got[:200]] * ts)
+
+
+def test_fp8_quantize_rounds_even_saturates_and_keeps_nan(oracle):
+    ts = 0.25  # a power of two: x / ts is exact, so the rounding seen is the E4M3 one
+    vals = _torch_e4m3_values()
+    for c in range(0, 0x7E):  # consecutive finite non-negative codes c, c + 1
+        mid = (vals[c] + vals[c + 1]) / 2
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.fp8_quantize(np.float32(mid * ts), ts) == want
+        assert oracle.fp8_quantize(np.float32(-mid * ts), ts) == (want | 0x80)
+    for big in (449.0 * ts, 1e6, 3e38):
+        assert oracle.fp8_quantize(np.float32(big), ts) == 0x7E
+        assert oracle.fp8_quantize(np.float32(-big), ts) == 0xFE
+    assert oracle.fp8_quantize(np.float32(np.nan), ts) & 0x7F == 0x7F
+    assert oracle.fp8_quantize(np.float32(-0.0), ts) == 0x80
+
+
+def test_fp8_layouts_hold_the_same_values(oracle):
+    """Token-major [tok][dim] and dim-major [dim][tok] slabs: the same bytes at transposed
+    offsets, and each value is E4M3(x / ts) * ts."""
+    rng = np.random.default_rng(22)
+    ts = float(np.float32(8 / 448))
+    x = rng.standard_normal((40, 4, 128)).astype(np.float32)
+    slots = rng.choice(3 * 128, size=40, replace=False)
+    tm = oracle.OracleCache(oracle.FP8_E4M3, oracle.TOKEN_MAJOR, 4, 3, ts)
+    dm = oracle.OracleCache(oracle.FP8_E4M3, oracle.DIM_MAJOR, 4, 3, ts)
+    tm.write(slots, x)
+    dm.write(slots, x)
+    a = tm.bytes.reshape(3, 4, 128, 128)
+    b = dm.bytes.reshape(3, 4, 128, 128)
+    assert np.array_equal(a, np.swapaxes(b, -1, -2))
+    codes = oracle.fp8_quantize(x, ts)
+    for i, s in enumerate(slots):
+        assert np.array_equal(a[s // 128, :, s % 128, :], codes[i])
+    vals = _torch_e4m3_values()
+    for i, s in enumerate(slots[:5]):
+        for h in range(4):
+            for d in (0, 17, 127):
+                assert tm.value(int(s // 128), h, int(s % 128), d) == vals[codes[i, h, d]] * ts
+                assert dm.value(int(s // 128), h, int(s % 128), d) == vals[codes[i, h, d]] * ts

@@ -72,6 +72,25 @@ def test_indexer_nvfp4_matches_numpy_over_dequantised_pages(oracle):
                 np.testing.assert_allclose(ts[b, r, g], w, rtol=1e-12, atol=1e-9)
 
 
+def test_indexer_fp8_matches_numpy_over_dequantised_pages(oracle):
+    wl = W.make_workload(3, seed=1, B=3, len_div=64, R=2, cache="fp8")
+    ci, ck, cv = oracle_caches(oracle, wl)
+    _, _, qi, _ = oracle_queries(oracle, wl)
+    bt = oracle_batch(oracle, wl)
+    ts = oracle.index_scores(bt, qi, ci)
+    deq = decode_pages_f64(ci.bytes, False, False, 1, wl.num_pages, wl.tensor_scale, fp8=True)
+    assert np.array_equal(ci.dequant_pages(np.arange(wl.num_pages)), deq.astype(np.float32))
+    p = row_positions(wl)
+    for b in range(wl.B):
+        rows = _gather_tokens(wl, deq, 0, b, int(wl.lengths[b]))
+        for r in range(wl.R):
+            n = p[b, r] + 1
+            for g in range(wl.G):
+                w = np.full(wl.max_pages * 128, -np.inf)
+                w[:n] = rows[:n] @ qi[b, r, g]
+                np.testing.assert_allclose(ts[b, r, g], w, rtol=1e-12, atol=1e-9)
+
+
 def test_maxpool_matches_numpy(oracle):
     wl = W.make_workload(3, seed=2, B=2, len_div=64, R=3)
     ci, _, _ = oracle_caches(oracle, wl)
@@ -166,18 +185,20 @@ def _sdpa_reference(q, k, v, mask, scale):
     return out[0, :, 0, :].numpy()
 
 
-@pytest.mark.parametrize("cfg,R,lens", [(1, 1, [2048]), (1, 4, [1999, 5]), (3, 1, [1500, 2048])])
-def test_attention_dense_case_equals_sdpa(oracle, cfg, R, lens):
+@pytest.mark.parametrize("cfg,R,lens,cache", [(1, 1, [2048], None), (1, 4, [1999, 5], None),
+                                              (3, 1, [1500, 2048], None), (3, 2, [1500, 2048, 3], "fp8")])
+def test_attention_dense_case_equals_sdpa(oracle, cfg, R, lens, cache):
     """With <= 16 blocks every block is selected: MSA is dense causal GQA attention."""
-    wl = W.make_workload(cfg, seed=5, lengths=lens, R=R)
+    wl = W.make_workload(cfg, seed=5, lengths=lens, R=R, cache=cache)
     ci, ck, cv = oracle_caches(oracle, wl)
     _, _, qi, q = oracle_queries(oracle, wl)
     bt = oracle_batch(oracle, wl)
     res = oracle.decode_step(bt, qi, q, wl.sm_scale, ci, ck, cv, wl.topk)
     p = row_positions(wl)
-    if wl.cache == "nvfp4":
-        dk = decode_pages_f64(ck.bytes, True, False, wl.G, wl.num_pages, wl.tensor_scale)
-        dv = decode_pages_f64(cv.bytes, True, True, wl.G, wl.num_pages, wl.tensor_scale)
+    if wl.cache != "f32":
+        fp8 = wl.cache == "fp8"
+        dk = decode_pages_f64(ck.bytes, not fp8, False, wl.G, wl.num_pages, wl.tensor_scale, fp8=fp8)
+        dv = decode_pages_f64(cv.bytes, not fp8, True, wl.G, wl.num_pages, wl.tensor_scale, fp8=fp8)
         assert np.array_equal(cv.dequant_pages(np.arange(wl.num_pages)), dv.astype(np.float32))
     for b in range(wl.B):
         if wl.cache == "f32":

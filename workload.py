@@ -31,6 +31,8 @@ H = G * HPG
 TOPK = 16
 # NVFP4 per-tensor FP32 scale for N(0,1) rows: amax bound 8 over (E2M1 max 6 x E4M3 max 448).
 NVFP4_TENSOR_SCALE = float(np.float32(8.0 / (6.0 * 448.0)))
+# FP8 (E4M3 per element) per-tensor FP32 scale for N(0,1) rows: amax bound 8 over E4M3 max 448.
+FP8_TENSOR_SCALE = float(np.float32(8.0 / 448.0))
 SM_SCALE = float(np.float32(1.0 / np.sqrt(DIM)))
 
 CONFIGS = {
@@ -51,7 +53,7 @@ class Workload:
     seed: int
     B: int
     R: int
-    cache: str  # "f32" | "nvfp4"
+    cache: str  # "f32" | "nvfp4" | "fp8"
     lengths: np.ndarray  # [B] int32, tokens in cache incl. the R new rows
     block_table: np.ndarray  # [B][max_pages] int32 physical page ids (unused tail = 0)
     num_pages: int
@@ -88,9 +90,10 @@ class Workload:
 
 
 def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int = 1,
-                  lengths: list[int] | None = None, R: int | None = None) -> Workload:
+                  lengths: list[int] | None = None, R: int | None = None, cache: str | None = None) -> Workload:
     """Build the shapes of a configuration.  ``B``/``len_div`` shrink it for
-    parity tests; ``lengths`` overrides the drawn lengths (edge cases)."""
+    parity tests; ``lengths`` overrides the drawn lengths (edge cases);
+    ``cache`` = "fp8" stores the same shapes in FP8 caches instead of NVFP4."""
     cfg = CONFIGS[config]
     rng = np.random.default_rng([seed, 0])
     B = cfg["B"] if B is None else B
@@ -125,8 +128,11 @@ def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int
         n = own_pages[b]
         table[b, prefix_pages:prefix_pages + n] = perm[nxt:nxt + n]
         nxt += n
-    ts = NVFP4_TENSOR_SCALE if cfg["cache"] == "nvfp4" else 1.0
-    return Workload(name=cfg["name"], seed=seed, B=B, R=R, cache=cfg["cache"], lengths=lens.astype(np.int32),
+    kind = cfg["cache"] if cache is None else cache
+    assert kind in ("f32", "nvfp4", "fp8")
+    ts = {"nvfp4": NVFP4_TENSOR_SCALE, "fp8": FP8_TENSOR_SCALE, "f32": 1.0}[kind]
+    name = cfg["name"] if kind == cfg["cache"] else f'{cfg["name"]}_{kind}'
+    return Workload(name=name, seed=seed, B=B, R=R, cache=kind, lengths=lens.astype(np.int32),
                     block_table=table, num_pages=int(num_pages), prefix_tokens=int(prefix), tensor_scale=ts)
 
 
