@@ -42,11 +42,13 @@ def log(msg):
 
 def algorithmic_bytes(wl, sel, cnt):
     """Minimum bytes one step moves (per the method): the index of every
-    context (72 B/token), K+V of the selected tokens of each (request, group)
-    (144 B/token: 64+8 B of K, 64+8 B of V), queries, outputs, block table,
-    and the insert of the new rows (FP32 in, NVFP4 out).  A physical page is
-    counted once however many requests (a shared prefix) or rows select it."""
+    context (72 B/token in NVFP4, 128 B in FP8), K+V of the selected tokens of
+    each (request, group) (NVFP4 144 B/token: 64+8 B of K, 64+8 B of V; FP8
+    256 B), queries, outputs, block table, and the insert of the new rows
+    (FP32 in, quantised out).  A physical page is counted once however many
+    requests (a shared prefix) or rows select it."""
     B, R = wl.B, wl.R
+    row_b = 128 if wl.cache == "fp8" else 72  # one 128-dim row of one head
     L = wl.lengths.astype(np.int64)
     idx_tok = {}  # physical page -> tokens of it some request's context covers
     for b in range(B):
@@ -54,7 +56,7 @@ def algorithmic_bytes(wl, sel, cnt):
         for j in range(npb):
             ph = int(wl.block_table[b, j])
             idx_tok[ph] = max(idx_tok.get(ph, 0), min(128, int(L[b]) - 128 * j))
-    idx = sum(idx_tok.values()) * 72
+    idx = sum(idx_tok.values()) * row_b
     kv_lim = {}  # (group, physical page) -> last token any selecting row sees
     p = L[:, None] - R + np.arange(R)[None, :]
     for b in range(B):
@@ -65,12 +67,12 @@ def algorithmic_bytes(wl, sel, cnt):
                     key = (g, int(wl.block_table[b, j]))
                     kv_lim[key] = max(kv_lim.get(key, -1), min(127, int(p[b, r]) - 128 * j))
     kv_tokens = sum(v + 1 for v in kv_lim.values())
-    kv = kv_tokens * 144
+    kv = kv_tokens * 2 * row_b
     q_bytes = B * R * 4 * 128 + B * R * 32 * 128  # FP8 index queries + queries
     out_bytes = B * R * 32 * 128 * 4
     P = wl.prefix_pages
     table = (P + B * (wl.max_pages - P)) * 4 + B * 4
-    insert = B * R * (9 * 128 * 4 + 9 * 72)  # FP32 rows in, NVFP4 bytes out
+    insert = B * R * (9 * 128 * 4 + 9 * row_b)  # FP32 rows in, quantised rows out
     return {"index": idx + B * R * 4 * 128 + table, "insert_index": idx + B * R * 4 * 128 + table + insert, "kv": kv,
             "total": idx + kv + q_bytes + out_bytes + table + insert, "kv_tokens": kv_tokens}
 
@@ -84,7 +86,7 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
     import workload as W
 
     rows = np.asarray(sample_reqs)
-    dt = O.NVFP4
+    dt = O.FP8_E4M3 if wl.cache == "fp8" else O.NVFP4
     ci = O.OracleCache(dt, O.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
     ck = O.OracleCache(dt, O.TOKEN_MAJOR, 4, wl.num_pages, wl.tensor_scale)
     cv = O.OracleCache(dt, O.DIM_MAJOR, 4, wl.num_pages, wl.tensor_scale)
@@ -144,7 +146,7 @@ def recorded_traffic(key="insert-index-kernel-traffic-bytes-per-launch"):
     return int(fields[key]) if key in fields else None
 
 
-def setup(seed=0, n_replicas=2, config=CONFIG_ID):
+def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4"):
     """Device state of the benchmark workload: filled caches (``n_replicas`` copies),
     decoders, the step's new rows and quantised queries."""
     import torch
@@ -154,11 +156,12 @@ def setup(seed=0, n_replicas=2, config=CONFIG_ID):
     from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
 
     dev = torch.device("cuda:0")
-    wl = W.make_workload(config, seed=seed)
+    wl = W.make_workload(config, seed=seed, cache=kv)
+    kv_dtype = M.MSA_FP8_E4M3 if kv == "fp8" else M.MSA_NVFP4
     log(f"workload {wl.name}: B={wl.B} R={wl.R} tokens={int(wl.lengths.sum())} pages={wl.num_pages}")
 
     # ---- caches (replica 0 filled by the insert kernel from device-drawn rows)
-    k0, v0, i0 = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
+    k0, v0, i0 = make_caches(kv_dtype, wl.num_pages, wl.tensor_scale, dev)
     table = torch.from_numpy(wl.block_table).to(dev)
     lens = torch.from_numpy(wl.lengths).to(dev)
     batch = M.Batch(table, lens, wl.R, wl.prefix_pages)
@@ -176,7 +179,7 @@ def setup(seed=0, n_replicas=2, config=CONFIG_ID):
     torch.cuda.synchronize()
     replicas = [(k0, v0, i0)]
     for _ in range(n_replicas - 1):
-        k, v, i = make_caches(True, wl.num_pages, wl.tensor_scale, dev)
+        k, v, i = make_caches(kv_dtype, wl.num_pages, wl.tensor_scale, dev)
         k.pages.copy_(k0.pages), v.pages.copy_(v0.pages), i.pages.copy_(i0.pages)
         replicas.append((k, v, i))
     decs = [MsaDecoder(batch, k, v, i, wl.topk, dev) for (k, v, i) in replicas]
@@ -211,6 +214,8 @@ def main():
                     help="workload: 3 = 32 requests at 64K-192K tokens (the default, the metric's own); "
                          "2 = 8 x 32K; 4 = 16 requests x 4 speculative rows; 5 = 64 requests sharing a "
                          "256K-token prefix")
+    ap.add_argument("--kv", choices=["nvfp4", "fp8"], default="nvfp4",
+                    help="cache format of keys, values and index keys (default NVFP4, the metric's own)")
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--layers-per-graph", type=int, default=10,
@@ -226,7 +231,8 @@ def main():
               "(the context-parallel indexer design is documented, not built).", file=sys.stderr)
         sys.exit(2)
 
-    st = setup(args.seed, args.replicas, args.config)
+    st = setup(args.seed, args.replicas, args.config, args.kv)
+    headline = args.config == CONFIG_ID and args.kv == "nvfp4"
     torch, M, W, wl, decs, q_idx, q, new = st.torch, st.M, st.W, st.wl, st.decs, st.q_idx, st.q, st.new
 
     stream = torch.cuda.Stream()
@@ -340,23 +346,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 kv x fp8 q (fp8xfp4 + f16 mfma, f32 accumulate)",
+        "dtype": ("fp8 kv x fp8 q (fp8xfp8 + f16 mfma, f32 accumulate)" if wl.cache == "fp8"
+                  else "nvfp4 kv x fp8 q (fp8xfp4 + f16 mfma, f32 accumulate)"),
         "data": "synthetic N(0,1) rows, seeded, device-generated",
         "config": {"workload": wl.name, "global_batch": wl.B, "rows_per_req": wl.R,
                    "ctx_tokens_mean": float(wl.lengths.mean()), "ctx_tokens_min": int(wl.lengths.min()),
-                   "ctx_tokens_max": int(wl.lengths.max()), "kv_cache": "nvfp4", "index_cache": "nvfp4",
+                   "ctx_tokens_max": int(wl.lengths.max()), "kv_cache": wl.cache, "index_cache": wl.cache,
                    "topk_blocks": wl.topk, "block_tokens": 128, "parallelism": "single-gpu",
                    "cache_replicas": len(decs), "hip_graph": use_graph,
                    "layer_steps_per_graph": per_graph if use_graph else None},
-        "roofline": {"bound": "hbm", "kernel": "index_nvfp4_kernel with the insert fused in (steps 0-2)",
+        "roofline": {"bound": "hbm", "kernel": f"index_{wl.cache}_kernel with the insert fused in (steps 0-2)",
                      "achieved": idx_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic() if args.config == CONFIG_ID else None,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic() if headline else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE x 1, copy-calibrated)",
                      "bytes_per_launch": nbytes["insert_index"], "avg_launch_us": us["insert_index"],
                      "plain_scan": {"bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"],
                                     "achieved": nbytes["index"] / (us["index"] * 1e-6) / 1e9,
                                     "traffic": recorded_traffic("index-kernel-traffic-bytes-per-launch")
-                                    if args.config == CONFIG_ID else None}},
+                                    if headline else None}},
         "prefix_mfma": None if not P else {
             "kernel": "prefix_index_kernel (shared-prefix scores on v_mfma_f32_16x16x32_f16)",
             "bound": "mfma", "flops_per_launch": prefix_flops, "avg_launch_us": us["prefix"],

@@ -23,6 +23,7 @@ HEAD_DIM = 128
 HEADS_PER_GROUP = 8
 NVFP4_SLAB_BYTES = 9216
 F32_SLAB_BYTES = 65536
+FP8_SLAB_BYTES = 16384
 
 
 class MsaError(RuntimeError):
@@ -110,7 +111,7 @@ class Cache:
 
     @staticmethod
     def slab_bytes(dtype: int) -> int:
-        return F32_SLAB_BYTES if dtype == MSA_F32 else NVFP4_SLAB_BYTES
+        return {MSA_F32: F32_SLAB_BYTES, MSA_FP8_E4M3: FP8_SLAB_BYTES, MSA_NVFP4: NVFP4_SLAB_BYTES}[dtype]
 
     @classmethod
     def empty(cls, dtype: int, layout: int, num_heads: int, num_pages: int, tensor_scale: float = 1.0,

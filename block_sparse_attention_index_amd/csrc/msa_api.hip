@@ -12,10 +12,10 @@ bool finite_pos(float x) { return isfinite(x) && x > 0.0f; }
 
 int check_cache(const msa_cache* c, int want_heads, bool allow_dim_major, bool require_dim_major) {
   if (!c || !c->pages || c->num_pages < 1 || c->num_heads != want_heads) return MSA_ERR_INVALID_ARG;
-  if (c->dtype != MSA_NVFP4 && c->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
+  if (c->dtype != MSA_NVFP4 && c->dtype != MSA_FP8_E4M3 && c->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
   if (c->layout != MSA_TOKEN_MAJOR && c->layout != MSA_DIM_MAJOR) return MSA_ERR_INVALID_ARG;
   if (c->dtype == MSA_F32 && c->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
-  if (c->dtype == MSA_NVFP4) {
+  if (c->dtype != MSA_F32) {  // quantised caches: values dim-major, keys and index keys token-major
     if (require_dim_major && c->layout != MSA_DIM_MAJOR) return MSA_ERR_UNSUPPORTED;
     if (!allow_dim_major && c->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
   }
@@ -34,7 +34,7 @@ int check_batch(const msa_batch* b) {
 }
 
 int query_dtype_ok(int32_t q_dtype, const msa_cache* c) {
-  if (c->dtype == MSA_NVFP4) return q_dtype == MSA_FP8_E4M3 ? MSA_OK : MSA_ERR_UNSUPPORTED;
+  if (c->dtype != MSA_F32) return q_dtype == MSA_FP8_E4M3 ? MSA_OK : MSA_ERR_UNSUPPORTED;
   return q_dtype == MSA_F32 ? MSA_OK : MSA_ERR_UNSUPPORTED;
 }
 
@@ -46,7 +46,7 @@ int insert_impl(const float* k, const float* v, const float* idx_k, const int64_
     return MSA_ERR_INVALID_ARG;
   int st;
   if (kc && (st = check_cache(kc, 4, false, false)) != MSA_OK) return st;
-  if (vc && (st = check_cache(vc, 4, true, vc->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if (vc && (st = check_cache(vc, 4, true, vc->dtype != MSA_F32)) != MSA_OK) return st;
   if (ic && (st = check_cache(ic, 1, false, false)) != MSA_OK) return st;
   if (nvfp4_only)
     for (const msa_cache* c : {kc, vc, ic})
@@ -114,7 +114,7 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
   if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype != MSA_F32)) != MSA_OK) return st;
   if (k_cache->dtype != v_cache->dtype || k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
   if (!q || !sel_blocks || !sel_count || !out || !workspace) return MSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
@@ -134,8 +134,8 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
   if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype == MSA_NVFP4)) != MSA_OK) return st;
-  if (k_cache->dtype != MSA_NVFP4 || v_cache->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype != MSA_F32)) != MSA_OK) return st;
+  if (k_cache->dtype == MSA_F32 || v_cache->dtype != k_cache->dtype) return MSA_ERR_UNSUPPORTED;
   if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
   if (!block_scores || !q || !sel_blocks || !sel_count || !out) return MSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
@@ -154,10 +154,10 @@ int msa_insert_index_score(const msa_batch* batch, const float* k_new, const flo
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
   if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype == MSA_NVFP4)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype != MSA_F32)) != MSA_OK) return st;
   if ((st = check_cache(idx_cache, 1, false, false)) != MSA_OK) return st;
   for (const msa_cache* c : {k_cache, v_cache, idx_cache})
-    if (c->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+    if (c->dtype == MSA_F32 || c->dtype != k_cache->dtype) return MSA_ERR_UNSUPPORTED;
   if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
   if (!k_new || !v_new || !idx_new || !q_idx || !block_scores) return MSA_ERR_INVALID_ARG;
   if (q_dtype != MSA_FP8_E4M3) return MSA_ERR_UNSUPPORTED;
@@ -182,7 +182,7 @@ const char* msa_status_str(int status) {
 int msa_debug_dequant(const msa_cache* cache, const int32_t* pages, int32_t n_pages, int32_t mode, float* out,
                       hipStream_t stream) {
   if (!cache || !cache->pages || cache->num_heads < 1 || cache->num_pages < 1) return MSA_ERR_INVALID_ARG;
-  if (cache->dtype != MSA_NVFP4 && cache->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
+  if (cache->dtype != MSA_NVFP4 && cache->dtype != MSA_FP8_E4M3 && cache->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
   if (cache->dtype == MSA_F32 && cache->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
   if (n_pages < 0 || (n_pages > 0 && (!pages || !out)) || (mode != 0 && mode != 1)) return MSA_ERR_INVALID_ARG;
   if (n_pages == 0) return MSA_OK;

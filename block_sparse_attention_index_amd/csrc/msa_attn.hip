@@ -167,6 +167,43 @@ __device__ __forceinline__ void load_v(const uint8_t* __restrict__ vs_, int lane
   r.vsc = nt_load4(vs_ + kScaleOff + 16 * lane);
 }
 
+// FP8 caches: a lane's 32 bytes per M-tile (keys) or per 16-dim tile
+// (values), one E4M3 byte per element, no per-element scales (the tensor
+// scales are folded into the softmax and output scales).
+struct KRegs8 {
+  uint4 kc[8][2];  // K bytes of token tok(m): dims 32a .. 32a+15, 32a+16 .. 32a+31
+};
+struct VRegs8 {
+  uint4 vw[8][2];  // V bytes of dim 16nt + n: tokens 32a .. 32a+15, 32a+16 .. 32a+31
+};
+
+__device__ __forceinline__ void load_k(const uint8_t* __restrict__ ks_, int lane, KRegs8& r) {
+  const int n = lane & 15, a = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    r.kc[m][0] = nt_load4(ks_ + tile_token(m, n) * kDim + 32 * a);
+    r.kc[m][1] = nt_load4(ks_ + tile_token(m, n) * kDim + 32 * a + 16);
+  }
+}
+
+__device__ __forceinline__ void load_v(const uint8_t* __restrict__ vs_, int lane, VRegs8& r) {
+  const int n = lane & 15, a = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    r.vw[nt][0] = nt_load4(vs_ + (16 * nt + n) * kPage + 32 * a);
+    r.vw[nt][1] = nt_load4(vs_ + (16 * nt + n) * kPage + 32 * a + 16);
+  }
+}
+
+// 8 E4M3 bytes (step s of a 32-byte lane tile: bytes 8s .. 8s+7) -> exact FP16.
+__device__ __forceinline__ h8 e4m3x8_step(const uint4 (&w)[2], int s) {
+  const uint4& q = w[s >> 1];
+  const uint32_t lo = (s & 1) ? q.z : q.x, hi = (s & 1) ? q.w : q.y;
+  const h2 x0 = e4m3x2_to_h2<false>(lo), x1 = e4m3x2_to_h2<true>(lo);
+  const h2 x2 = e4m3x2_to_h2<false>(hi), x3 = e4m3x2_to_h2<true>(hi);
+  return h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
 // Per-wave LDS slots of one block's scales.
 struct ScaleSlot {
   uint4 k[64];  // raw K scale bytes, [token][group]
@@ -179,12 +216,14 @@ struct ScaleSlot {
 // (wave-uniform) says the state is still empty, so nothing needs rescaling.
 // after_qk() runs once the key registers are consumed (the caller issues the
 // next block's loads there).
-template <int QT, typename AfterQK>
-__device__ __forceinline__ void attend_block(const KRegs& kr, const VRegs& vr, const h8 (&Q)[QT][4],
+template <int QT, typename KR, typename VR, typename AfterQK>
+__device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h8 (&Q)[QT][4],
                                              const int (&lim)[QT], bool partial, bool first, float qk2, int lane,
                                              ScaleSlot* slot, AttnState<QT>& st, AfterQK after_qk) {
+  constexpr bool FP8 = __is_same(KR, KRegs8);
   const int n = lane & 15, a = lane >> 4;
-  // ---- scales through LDS: each lane needs scales that other lanes of this wave loaded
+  // ---- NVFP4 scales through LDS: each lane needs scales that other lanes of this wave loaded
+  if constexpr (!FP8) {
   slot->k[lane] = kr.ksc;
   {
     const uint32_t w[4] = {vr.vsc.x, vr.vsc.y, vr.vsc.z, vr.vsc.w};
@@ -198,13 +237,15 @@ __device__ __forceinline__ void attend_block(const KRegs& kr, const VRegs& vr, c
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   const uint8_t* kraw = reinterpret_cast<const uint8_t*>(slot->k);
 
   // ---- S^T = K Q^T (k-steps outermost: the 8 accumulators are independent)
   h2 ksc[8];
+  if constexpr (!FP8)
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-    ksc[m] = e4m3x2_to_h2<false>(*reinterpret_cast<const uint16_t*>(kraw + tile_token(m, n) * 8 + 2 * a));
+    for (int m = 0; m < 8; ++m)
+      ksc[m] = e4m3x2_to_h2<false>(*reinterpret_cast<const uint16_t*>(kraw + tile_token(m, n) * 8 + 2 * a));
   v4f Sacc[QT][8];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
@@ -214,10 +255,14 @@ __device__ __forceinline__ void attend_block(const KRegs& kr, const VRegs& vr, c
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const uint32_t word = ks == 0 ? kr.kc[m].x : ks == 1 ? kr.kc[m].y : ks == 2 ? kr.kc[m].z : kr.kc[m].w;
-      const _Float16 s = ks < 2 ? ksc[m][0] : ksc[m][1];
-      h8 kv = e2m1x8_to_h8(word);
-      kv = kv * h8{s, s, s, s, s, s, s, s};
+      h8 kv;
+      if constexpr (FP8) {
+        kv = e4m3x8_step(kr.kc[m], ks);
+      } else {
+        const uint32_t word = ks == 0 ? kr.kc[m].x : ks == 1 ? kr.kc[m].y : ks == 2 ? kr.kc[m].z : kr.kc[m].w;
+        const _Float16 s = ks < 2 ? ksc[m][0] : ksc[m][1];
+        kv = e2m1x8_to_h8(word) * h8{s, s, s, s, s, s, s, s};
+      }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
         Sacc[qt][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, Q[qt][ks], Sacc[qt][m], 0, 0, 0);
@@ -283,9 +328,13 @@ __device__ __forceinline__ void attend_block(const KRegs& kr, const VRegs& vr, c
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const uint32_t word = kk == 0 ? vr.vw[nt].x : kk == 1 ? vr.vw[nt].y : kk == 2 ? vr.vw[nt].z : vr.vw[nt].w;
-      h8 vv = e2m1x8_to_h8(word);
-      vv = vv * slot->v[nt * 16 + 4 * a + kk];
+      h8 vv;
+      if constexpr (FP8) {
+        vv = e4m3x8_step(vr.vw[nt], kk);
+      } else {
+        const uint32_t word = kk == 0 ? vr.vw[nt].x : kk == 1 ? vr.vw[nt].y : kk == 2 ? vr.vw[nt].z : vr.vw[nt].w;
+        vv = e2m1x8_to_h8(word) * slot->v[nt * 16 + 4 * a + kk];
+      }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
         st.O[qt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[qt][kk], vv, st.O[qt][nt], 0, 0, 0);
@@ -300,8 +349,9 @@ constexpr int kTabLds = 2048;  // block-table rows up to this width are staged i
 // Steps 3 (when SELECT) and 4 for one (request, group, row group); grid (groups x row groups, requests).
 // WAVES per workgroup: 8 with one query tile; 4 with two, so that each wave can
 // hold the doubled accumulators in registers (one wave per SIMD).
-template <int QT, bool SELECT, int KMAX, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
+// FP8: FP8 caches (one E4M3 byte per element), else NVFP4.
+template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8>
+__global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t R, int32_t max_pages,
     const uint8_t* __restrict__ q, float qk2, float v_scale, const uint8_t* __restrict__ kpages,
     const uint8_t* __restrict__ vpages, int32_t num_pages, const float* __restrict__ block_scores,
@@ -318,7 +368,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
   __shared__ float s_l[WAVES][NQ];
   __shared__ float s_fac[WAVES][NQ];  // each wave's factor exp2(m_w - M) per query row
   __shared__ float s_inv[NQ];         // v_scale / denominator per query row
-  __shared__ ScaleSlot s_slot[WAVES];         // scales of each wave's current block
+  __shared__ ScaleSlot s_slot[FP8 ? 1 : WAVES];  // NVFP4: scales of each wave's current block
   __shared__ SelectScratch s_sel[SELECT ? 4 : 1];  // selection scratch of waves 0..nr-1
   __shared__ float s_o[WAVES][NQ / 2][kDim];  // each wave's rescaled output rows (half the columns at a time)
 
@@ -405,9 +455,26 @@ __global__ __launch_bounds__(WAVES * 64) void attend_nvfp4_kernel(
     }
     return __any(part) != 0;
   };
-  auto kslab = [&](int ph) { return kpages + ((int64_t)max(ph, 0) * kGroups + g) * kNvSlab; };
-  auto vslab = [&](int ph) { return vpages + ((int64_t)max(ph, 0) * kGroups + g) * kNvSlab; };
+  constexpr int kSlab = FP8 ? kFp8Slab : kNvSlab;
+  auto kslab = [&](int ph) { return kpages + ((int64_t)max(ph, 0) * kGroups + g) * kSlab; };
+  auto vslab = [&](int ph) { return vpages + ((int64_t)max(ph, 0) * kGroups + g) * kSlab; };
   bool first = true;
+  if constexpr (FP8) {
+    // FP8 blocks are twice the register bytes of NVFP4 ones: one block at a time
+    for (int u = wave; u < nu; u += WAVES) {
+      const int ph = s_phys[u];
+      KRegs8 K;
+      VRegs8 V;
+      load_k(kslab(ph), lane, K);
+      load_v(vslab(ph), lane, V);
+      if (ph >= 0) {
+        int lim[QT];
+        const bool part = block_lim(s_union[u], lim);
+        attend_block<QT>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, [] {});
+        first = false;
+      }
+    }
+  } else
   // blocks wave, wave + WAVES, ... of the union, two at a time: the second
   // block's keys load with the first block's, its values once the first
   // block's keys are consumed (register budget of two waves per SIMD)
@@ -604,9 +671,9 @@ extern "C" size_t msa_decode_partials_bytes(const msa_batch* bt, int32_t topk) {
   return q * (kDim + 2) * sizeof(float);
 }
 
-// NVFP4 route: one launch, selection fused in when block_scores != NULL.
-template <bool SELECT>
-static int launch_attend_nvfp4(const msa_batch* bt, const uint8_t* q, float q_scale, float sm_scale,
+// NVFP4 and FP8 route: one launch, selection fused in when block_scores != NULL.
+template <bool SELECT, bool FP8>
+static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, float sm_scale,
                                const msa_cache* kc, const msa_cache* vc, const float* block_scores, int32_t* sel,
                                int32_t* cnt, int32_t topk, float* out, hipStream_t s) {
   const int R = bt->rows_per_req, P = bt->max_pages_per_req;
@@ -615,7 +682,7 @@ static int launch_attend_nvfp4(const msa_batch* bt, const uint8_t* q, float q_sc
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   const dim3 grid(kGroups * RG, bt->num_reqs);
 #define MSA_ATTEND(QT, K)                                                                                      \
-  hipLaunchKernelGGL((attend_nvfp4_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4)>), grid, dim3((QT == 1 ? 8 : 4) * 64), \
+  hipLaunchKernelGGL((attend_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4), FP8>), grid, dim3((QT == 1 ? 8 : 4) * 64),   \
                      0, s, bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale,                   \
                      (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt,  \
                      topk, out)
@@ -645,7 +712,10 @@ extern "C" int msa_launch_sparse_decode(const msa_batch* bt, const void* q, int3
                                         void* workspace, hipStream_t s) {
   const int B = bt->num_reqs, R = bt->rows_per_req, P = bt->max_pages_per_req;
   if (kc->dtype == MSA_NVFP4)
-    return launch_attend_nvfp4<false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
+    return launch_attend<false, false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
+                                       (int32_t*)cnt, topk, out, s);
+  if (kc->dtype == MSA_FP8_E4M3)
+    return launch_attend<false, true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
                                       (int32_t*)cnt, topk, out, s);
   const int S = (int)f32_splits(bt, topk);
   float* part_o = (float*)workspace;
@@ -664,6 +734,9 @@ extern "C" int msa_launch_select_decode(const msa_batch* bt, const float* block_
                                         const void* q, float q_scale, float sm_scale, const msa_cache* kc,
                                         const msa_cache* vc, int32_t* sel, int32_t* cnt, float* out,
                                         hipStream_t s) {
-  return launch_attend_nvfp4<true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
-                                   out, s);
+  if (kc->dtype == MSA_FP8_E4M3)
+    return launch_attend<true, true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
+                                     out, s);
+  return launch_attend<true, false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
+                                    out, s);
 }

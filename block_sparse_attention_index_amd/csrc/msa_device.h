@@ -16,6 +16,7 @@ constexpr int kGroups = 4;  // KV heads = GQA groups
 constexpr int kNvSlab = MSA_NVFP4_SLAB_BYTES;
 constexpr int kScaleOff = 8192;  // scales follow the 128 x 64 B of codes
 constexpr int kF32Slab = MSA_F32_SLAB_BYTES;
+constexpr int kFp8Slab = MSA_FP8_SLAB_BYTES;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));

@@ -278,6 +278,160 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   }
 }
 
+// FP8 caches (one E4M3 byte per element, FP32 tensor scale): the same scan
+// over 128 B per token.  Keys and index queries are both FP8, so one
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) multiplies 16 tokens'
+// full 128-dim rows against 16 query rows with exact products: A row 4g + i
+// holds index query (group g, row 4*rp + i), B column n token n of a 16-token
+// chunk.  Lane group c of either operand carries bytes 16c..16c+15 and
+// 64+16c..64+16c+15 of its 128-byte row (the instruction's FP8 operand
+// layout, the same for A and B, so every product pairs equal dims).  Output
+// lane (n, c) holds the scores of group c, rows 4*rp .. 4*rp+3, token n; the
+// block max is a 16-lane row reduction.  Grid, chunk order and the fused
+// insert follow index_nvfp4_kernel (one page per wave, 4 per workgroup).
+template <int R, bool kTok, bool INSERT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_fp8_kernel(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages,
+    const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
+    float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t B, NewRows NR) {
+  constexpr int RP = (R + 3) / 4;  // MFMAs per 16-token chunk (4 rows each)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int C = (max_pages + 3) / 4;
+  const int id = (int)blockIdx.x;
+  const int b = id < B ? id : (id - B) / max(C - 1, 1);
+  const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
+  const int L = clamp_len(lens[b], max_pages);
+  const int npb = (L + kPage - 1) / kPage;
+  const int latest = npb > 0 ? (npb - 1) / 4 : 0;
+  const int chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
+  if (INSERT) {
+    // new tokens [max(L - R, 0), L) in this chunk: one thread per element
+    // (4 x 128 keys, 4 x 128 values, 128 index keys per token)
+    const int lo = chunk * 4 * kPage;
+    const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * kPage);
+    constexpr int kPerTok = 9 * kDim;
+    for (int e = threadIdx.x; e < (t1 - t0) * kPerTok; e += 256) {
+      const int tok = t0 + e / kPerTok;
+      int u = e % kPerTok;
+      const int c = u < 4 * kDim ? 0 : (u < 8 * kDim ? 1 : 2);
+      u -= c * 4 * kDim;
+      const int heads = c == 2 ? 1 : kGroups;
+      const int head = u / kDim, d = u % kDim;
+      const int r = tok - (L - R);
+      const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
+      const float x = src[(((int64_t)b * R + r) * heads + head) * kDim + d];
+      const int ph = table[(int64_t)b * max_pages + tok / kPage];
+      const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
+      uint8_t* slab = (c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages)) +
+                      ((int64_t)(valid ? ph : 0) * heads + head) * kFp8Slab;
+      const int off = tok & (kPage - 1);
+      const float ts = c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i);
+      if (valid) slab[c == 1 ? d * kPage + off : off * kDim + d] = (uint8_t)e4m3_encode(x / ts);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  const int j = chunk * 4 + wave;
+  if (j >= max_pages) return;
+  const int n = lane & 15, c = lane >> 4;
+  const int64_t T = (int64_t)max_pages * kPage;
+
+  // A operands: row m = lane % 16 -> (group m / 4, row 4 rp + m % 4)
+  v8i A[RP];
+#pragma unroll
+  for (int rp = 0; rp < RP; ++rp) {
+    const int r = 4 * rp + (n & 3), g = n >> 2;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (r < R) {
+      const uint8_t* q = q_idx + (((int64_t)b * R + r) * kGroups + g) * kDim;
+      lo = *reinterpret_cast<const uint4*>(q + 16 * c);
+      hi = *reinterpret_cast<const uint4*>(q + 64 + 16 * c);
+    }
+    A[rp] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  int pos_lim[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) pos_lim[r] = L - R + r;
+
+  int phys = j < npb ? table[(int64_t)b * max_pages + j] : -1;
+  if (phys >= num_pages) phys = -1;
+  float m[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) m[r] = -__builtin_inff();
+  if (phys >= 0) {
+    const uint8_t* slab = pages + (int64_t)phys * kFp8Slab;
+    uint4 kw[8][2];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      kw[ch][0] = nt_load4(slab + (16 * ch + n) * kDim + 16 * c);
+      kw[ch][1] = nt_load4(slab + (16 * ch + n) * kDim + 64 + 16 * c);
+    }
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      const v8i Bop = v8i{(int)kw[ch][0].x, (int)kw[ch][0].y, (int)kw[ch][0].z, (int)kw[ch][0].w,
+                          (int)kw[ch][1].x, (int)kw[ch][1].y, (int)kw[ch][1].z, (int)kw[ch][1].w};
+      const int t = j * kPage + 16 * ch + n;
+#pragma unroll
+      for (int rp = 0; rp < RP; ++rp) {
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rp], Bop, z, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * rp + i;
+          if (r >= R) break;
+          const bool vis = t <= pos_lim[r];
+          if (kTok)
+            token_scores[(((int64_t)b * R + r) * kGroups + c) * T + t] = vis ? d[i] * out_scale : -__builtin_inff();
+          if (vis) m[r] = fmaxf(m[r], d[i]);
+        }
+      }
+    }
+  } else if (kTok) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      for (int ch = 0; ch < 8; ++ch)
+        token_scores[(((int64_t)b * R + r) * kGroups + c) * T + j * kPage + 16 * ch + n] = -__builtin_inff();
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float mm = wave_max16(m[r]);
+    if (n == 0) block_scores[(((int64_t)b * R + r) * kGroups + c) * max_pages + j] = mm * out_scale;
+  }
+}
+
+template <int R, bool INSERT>
+static void launch_fp8(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                       float* ts, const NewRows& nr, hipStream_t s) {
+  const dim3 grid((unsigned)(((bt->max_pages_per_req + 3) / 4) * bt->num_reqs));
+  if (ts)
+    hipLaunchKernelGGL((index_fp8_kernel<R, true, INSERT>), grid, dim3(256), 0, s, bt->block_table, bt->ctx_lens,
+                       bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs, ts,
+                       bt->num_reqs, nr);
+  else
+    hipLaunchKernelGGL((index_fp8_kernel<R, false, INSERT>), grid, dim3(256), 0, s, bt->block_table, bt->ctx_lens,
+                       bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs, ts,
+                       bt->num_reqs, nr);
+}
+
+template <bool INSERT>
+static int launch_fp8_rows(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                           float* ts, const NewRows& nr, hipStream_t s) {
+  switch (bt->rows_per_req) {
+    case 1: launch_fp8<1, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 2: launch_fp8<2, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 3: launch_fp8<3, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 4: launch_fp8<4, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 5: launch_fp8<5, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 6: launch_fp8<6, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 7: launch_fp8<7, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    case 8: launch_fp8<8, INSERT>(bt, q, out_scale, ic, bs, ts, nr, s); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // F32 cache, F32 queries: one workgroup per (page, request), one thread per token.
 template <bool kTok>
 __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restrict__ table,
@@ -382,8 +536,10 @@ extern "C" int msa_launch_index_score(const msa_batch* bt, const void* q_idx, in
                          ic->num_pages, block_scores, token_scores);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   const float out_scale = ic->tensor_scale * q_scale;
+  if (ic->dtype == MSA_FP8_E4M3)  // the shared-prefix declaration is not used with FP8 caches
+    return launch_fp8_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, NewRows{}, s);
+  if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   return launch_nvfp4_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, NewRows{}, s);
 }
 
@@ -393,7 +549,9 @@ extern "C" int msa_launch_insert_index_score(const msa_batch* bt, const float* k
                                              float* block_scores, float* token_scores, hipStream_t s) {
   NewRows nr{k_new, v_new, idx_new, (uint8_t*)kc->pages, (uint8_t*)vc->pages, (uint8_t*)ic->pages,
              kc->num_pages, kc->tensor_scale, vc->tensor_scale, ic->tensor_scale};
-  if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   const float out_scale = ic->tensor_scale * q_scale;
+  if (ic->dtype == MSA_FP8_E4M3)
+    return launch_fp8_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, nr, s);
+  if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   return launch_nvfp4_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, nr, s);
 }

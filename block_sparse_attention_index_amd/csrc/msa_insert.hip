@@ -1,5 +1,5 @@
-// msa_insert.hip -- step 0 (cache insert with NVFP4 quantisation), the FP8
-// query quantiser and the dequantisation test aid.
+// msa_insert.hip -- step 0 (cache insert with NVFP4 or FP8 quantisation),
+// the FP8 query quantiser and the dequantisation test aid.
 //
 // Insert: one 16-lane row (a DPP row) per (token, cache head, 16-dim
 // group), one element per lane.  The row reduces the group's amax with DPP,
@@ -12,7 +12,9 @@
 // its nibble with an atomic AND then OR (vector memory atomics, no read round
 // trip) -- tokens inserted together may share that dword.  One element per
 // lane keeps each lane's dependency chain to one quantisation (a single
-// IEEE division instead of sixteen in a row).
+// IEEE division instead of sixteen in a row).  FP8 caches: each lane stores
+// its own element, E4M3(x / tensor_scale), one byte, at [token][dim] or
+// [dim][token].
 #pragma clang fp contract(off)
 
 #include "msa_device.h"
@@ -31,7 +33,7 @@ struct InsertArgs {
   const float* src2;
   int32_t np0, np1, np2;     // page-pool sizes
   int32_t h0, h1, h2;        // heads
-  int32_t nv0, nv1, nv2;     // 1 = NVFP4, 0 = F32
+  int32_t nv0, nv1, nv2;     // msa_dtype: MSA_NVFP4, MSA_FP8_E4M3 or MSA_F32
   int32_t dm0, dm1, dm2;     // 1 = dim-major slab
   float ts0, ts1, ts2;       // tensor scales
   int32_t u0, u1, u2;        // 16-dim groups per token (heads * 8), 0 if absent
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
   const float* src = c == 0 ? A.src0 : (c == 1 ? A.src1 : A.src2);
   const int32_t num_pages = c == 0 ? A.np0 : (c == 1 ? A.np1 : A.np2);
   const int32_t heads = c == 0 ? A.h0 : (c == 1 ? A.h1 : A.h2);
-  const int32_t nvfp4 = c == 0 ? A.nv0 : (c == 1 ? A.nv1 : A.nv2);
+  const int32_t fmt = c == 0 ? A.nv0 : (c == 1 ? A.nv1 : A.nv2);
   const int32_t dim_major = c == 0 ? A.dm0 : (c == 1 ? A.dm1 : A.dm2);
   const float ts = c == 0 ? A.ts0 : (c == 1 ? A.ts1 : A.ts2);
   const int head = u >> 3, grp = u & 7;
@@ -64,9 +66,15 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
   const bool valid = slot >= 0 && slot < (int64_t)num_pages * kPage;
   const int64_t page = valid ? slot >> 7 : 0;
   const int off = (int)(slot & 127);
-  if (!nvfp4) {
+  if (fmt == MSA_F32) {
     float* dst = reinterpret_cast<float*>(pages + (page * heads + head) * (int64_t)kF32Slab);
     if (valid) dst[off * kDim + grp * 16 + i] = x;
+    return;
+  }
+  if (fmt == MSA_FP8_E4M3) {
+    uint8_t* slab = pages + (page * heads + head) * (int64_t)kFp8Slab;
+    const int d = grp * 16 + i;
+    if (valid) slab[dim_major ? d * kPage + off : off * kDim + d] = (uint8_t)e4m3_encode(x / ts);
     return;
   }
   uint32_t code;
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* __restr
 
 // One thread per (page, head, token, 8-dim chunk): decodes 8 elements.
 __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __restrict__ pages, int32_t num_pages,
-                                                            int32_t heads, int32_t nvfp4, int32_t dim_major,
+                                                            int32_t heads, int32_t fmt, int32_t dim_major,
                                                             float ts, const int32_t* __restrict__ page_ids,
                                                             int32_t n_pages, int32_t mode, float* __restrict__ out) {
   int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -98,9 +106,18 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
     for (int e = 0; e < 8; ++e) o[e] = __builtin_nanf("");
     return;
   }
-  if (!nvfp4) {
+  if (fmt == MSA_F32) {
     const float* s = reinterpret_cast<const float*>(pages + (page * heads + head) * (int64_t)kF32Slab) + t * kDim;
     for (int e = 0; e < 8; ++e) o[e] = s[chunk * 8 + e];
+    return;
+  }
+  if (fmt == MSA_FP8_E4M3) {
+    // both modes: E4M3 is exact in FP32 and FP16, one FP32 multiply by the tensor scale
+    const uint8_t* slab = pages + (page * heads + head) * (int64_t)kFp8Slab;
+    for (int e = 0; e < 8; ++e) {
+      const int d = chunk * 8 + e;
+      o[e] = e4m3_to_f32(slab[dim_major ? d * kPage + t : t * kDim + d]) * ts;
+    }
     return;
   }
   const uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
@@ -145,7 +162,7 @@ extern "C" int msa_launch_kv_insert(const float* k, const float* v, const float*
     s = src;
     np = c->num_pages;
     h = c->num_heads;
-    nv = c->dtype == MSA_NVFP4;
+    nv = c->dtype;
     dm = c->layout == MSA_DIM_MAJOR;
     ts = c->tensor_scale;
     u = c->num_heads * 8;
@@ -173,7 +190,7 @@ extern "C" int msa_launch_debug_dequant(const msa_cache* c, const int32_t* pages
   if (total == 0) return 0;
   int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint8_t*)c->pages,
-                     c->num_pages, c->num_heads, (int32_t)(c->dtype == MSA_NVFP4),
+                     c->num_pages, c->num_heads, (int32_t)c->dtype,
                      (int32_t)(c->layout == MSA_DIM_MAJOR), c->tensor_scale, pages, n_pages, mode, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

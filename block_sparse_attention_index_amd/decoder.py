@@ -18,11 +18,12 @@ GROUPS = 4
 HEADS = 32
 
 
-def make_caches(nvfp4: bool, num_pages: int, tensor_scale: float, device="cuda"):
-    """(k, v, idx) page pools in the layouts the kernels read."""
-    dt = MSA_NVFP4 if nvfp4 else MSA_F32
+def make_caches(dtype, num_pages: int, tensor_scale: float, device="cuda"):
+    """(k, v, idx) page pools in the layouts the kernels read.  dtype: MSA_NVFP4, MSA_FP8_E4M3 or
+    MSA_F32 (True / False stand for NVFP4 / F32)."""
+    dt = (MSA_NVFP4 if dtype else MSA_F32) if isinstance(dtype, bool) else dtype
     k = Cache.empty(dt, MSA_TOKEN_MAJOR, GROUPS, num_pages, tensor_scale, device)
-    v = Cache.empty(dt, MSA_DIM_MAJOR if nvfp4 else MSA_TOKEN_MAJOR, GROUPS, num_pages, tensor_scale, device)
+    v = Cache.empty(dt, MSA_TOKEN_MAJOR if dt == MSA_F32 else MSA_DIM_MAJOR, GROUPS, num_pages, tensor_scale, device)
     idx = Cache.empty(dt, MSA_TOKEN_MAJOR, 1, num_pages, tensor_scale, device)
     return k, v, idx
 
@@ -32,7 +33,7 @@ class MsaDecoder:
                  device="cuda"):
         self.batch, self.k, self.v, self.idx, self.topk = batch, k_cache, v_cache, idx_cache, topk
         B, R, P = batch.B, batch.R, batch.max_pages
-        self.q_dtype = MSA_FP8_E4M3 if k_cache.dtype == MSA_NVFP4 else MSA_F32
+        self.q_dtype = MSA_F32 if k_cache.dtype == MSA_F32 else MSA_FP8_E4M3
         self.block_scores = torch.empty((B, R, GROUPS, P), dtype=torch.float32, device=device)
         self.sel = torch.empty((B, R, GROUPS, topk), dtype=torch.int32, device=device)
         self.cnt = torch.empty((B, R, GROUPS), dtype=torch.int32, device=device)
@@ -66,11 +67,11 @@ class MsaDecoder:
 
     def step(self, q_idx, q, q_scale, sm_scale, new_tokens=None, stream=None, fused=True):
         """new_tokens: optional (k [n][4][128], v [n][4][128], idx [n][128], slots [n]) FP32 rows to insert first.
-        fused (NVFP4 caches): insert + index in one launch and selection + attention in another; the new rows
+        fused (NVFP4 or FP8 caches): insert + index in one launch and selection + attention in another; the new rows
         must then be those of positions L_b - R .. L_b - 1, request-major (their slots follow from the block
         table and are not read)."""
-        nvfp4 = self.k.dtype == MSA_NVFP4
-        if fused and nvfp4 and new_tokens is not None:
+        quant = self.k.dtype != MSA_F32
+        if fused and quant and new_tokens is not None:
             k, v, i, _ = new_tokens
             self.insert_index(k, v, i, q_idx, q_scale, None, stream)
         else:
@@ -78,7 +79,7 @@ class MsaDecoder:
                 k, v, i, s = new_tokens
                 self.insert(k, v, i, s, stream)
             self.index(q_idx, q_scale, None, stream)
-        if fused and nvfp4:
+        if fused and quant:
             self.select_attend(q, q_scale, sm_scale, stream)
         else:
             self.select(stream)

@@ -68,11 +68,17 @@ typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1 } msa_layout;
 #define MSA_NVFP4_GROUP 16
 #define MSA_NVFP4_SLAB_BYTES 9216
 #define MSA_F32_SLAB_BYTES 65536
+#define MSA_FP8_SLAB_BYTES 16384
 
 /*
  * One paged cache tensor of one layer.  Page p, head h is the slab at
  * pages + (p * num_heads + h) * slab_bytes.  Slab layouts:
  *   MSA_F32 (token-major only): float [128 tokens][128 dims], 65,536 B.
+ *   MSA_FP8_E4M3, 16,384 B per slab: one E4M3 byte per element, value =
+ *   e4m3 * tensor_scale (the pages' FP8 cache: 128 B of index keys and
+ *   1,024 B of K+V per token and layer; one FP32 scale per cache tensor).
+ *     MSA_TOKEN_MAJOR (keys, index keys): [128 tokens][128 dims].
+ *     MSA_DIM_MAJOR (values): [128 dims][128 tokens].
  *   MSA_NVFP4, 9,216 B per slab.  Element value = (e2m1 * e4m3_scale) *
  *   tensor_scale; one E4M3 scale per 16 consecutive dims of a token (the
  *   block size that the pages' 34,560-vs-61,440 B per token fixes).

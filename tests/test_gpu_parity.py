@@ -50,7 +50,8 @@ def gpu_setup(M, wl, hold_new=False, shared=True):
     the batch (the indexer then scores them once for all requests)."""
     from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
 
-    k, v, idx = make_caches(wl.cache == "nvfp4", wl.num_pages, wl.tensor_scale)
+    dtype = {"nvfp4": M.MSA_NVFP4, "fp8": M.MSA_FP8_E4M3, "f32": M.MSA_F32}[wl.cache]
+    k, v, idx = make_caches(dtype, wl.num_pages, wl.tensor_scale)
     batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R, wl.prefix_pages if shared else 0)
     dec = MsaDecoder(batch, k, v, idx, wl.topk)
     n_new = wl.B * wl.R
@@ -80,7 +81,7 @@ def gpu_setup(M, wl, hold_new=False, shared=True):
         if wl.num_pages > 4096 and b % 8 == 7:
             print(f"  inserted requests 0..{b}", flush=True)
     qi32, q32 = W.queries(wl)
-    if wl.cache == "nvfp4":
+    if wl.cache != "f32":
         q_idx = M.msa_quantize_e4m3(_dev(qi32), wl.q_scale)
         q = M.msa_quantize_e4m3(_dev(q32), wl.q_scale)
     else:
@@ -111,12 +112,19 @@ CASES = {
     # contexts shorter than, equal to and just past the shared prefix, two rows each
     "prefix_short": lambda: W.make_workload(5, seed=10, len_div=64, R=2,
                                             lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 9000)]),
+    # FP8 caches (E4M3 per element, FP32 tensor scale)
+    "fp8_cfg3_small": lambda: W.make_workload(3, seed=11, B=4, len_div=48, cache="fp8"),
+    "fp8_ragged": lambda: W.make_workload(3, seed=12, lengths=[1, 127, 128, 129, 2047, 2048, 2049, 5000], R=1,
+                                          cache="fp8"),
+    "fp8_ragged_r4": lambda: W.make_workload(4, seed=13, lengths=[0, 2, 3, 4, 131, 2051, 2052, 7000], R=4,
+                                             cache="fp8"),
+    "fp8_r8": lambda: W.make_workload(4, seed=14, B=2, len_div=64, R=8, cache="fp8"),
     "r8": lambda: W.make_workload(4, seed=8, B=2, len_div=64, R=8),
 }
 
 
 # ---------------------------------------------------------------- step 0 / codecs
-@pytest.mark.parametrize("case", ["cfg2_small", "cfg4_small", "cfg5_small", "cfg1_f32"])
+@pytest.mark.parametrize("case", ["cfg2_small", "cfg4_small", "cfg5_small", "cfg1_f32", "fp8_cfg3_small"])
 def test_insert_bytes_bitexact(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -154,6 +162,55 @@ def test_insert_special_values_bitexact(M, oracle):
     assert np.array_equal(k.pages.cpu().numpy(), ok.bytes)
     assert np.array_equal(v.pages.cpu().numpy(), ov.bytes)
     assert np.array_equal(idx.pages.cpu().numpy(), oi.bytes)
+
+
+def test_insert_fp8_special_values_bitexact(M, oracle):
+    """FP8 cache bytes: E4M3(x / ts) over subnormals, exact midpoints, saturation, zeros, -0 and NaN."""
+    print("[case] insert fp8 special values", flush=True)
+    rng = np.random.default_rng(12)
+    n = 384
+    ts = 0.25
+    vals = O.e4m3_value(np.arange(127))
+    mids = (vals[:-1] + vals[1:]) / 2
+    pool = np.concatenate([vals, mids, [449.0, 464.0, 500.0, 1e6, 0.0, -0.0, np.nan, 2.0 ** -10]]) * ts
+    x = rng.choice(np.concatenate([pool, -pool]), size=(n, 4, 128)).astype(np.float32)
+    x[: n // 2] = (rng.standard_normal((n // 2, 4, 128)) * 2.0 ** rng.integers(-12, 9, (n // 2, 4, 1))).astype(
+        np.float32)
+    xi = x[:, 1, :].copy()
+    from block_sparse_attention_index_amd.decoder import make_caches
+
+    npg = n // 128 + 1
+    k, v, idx = make_caches(M.MSA_FP8_E4M3, npg, ts)
+    slots = rng.permutation(npg * 128)[:n].astype(np.int64)
+    M.msa_kv_insert(_dev(x), _dev(x), _dev(xi), _dev(slots), k, v, idx)
+    torch.cuda.synchronize()
+    ok = O.OracleCache(O.FP8_E4M3, O.TOKEN_MAJOR, 4, npg, ts)
+    ov = O.OracleCache(O.FP8_E4M3, O.DIM_MAJOR, 4, npg, ts)
+    oi = O.OracleCache(O.FP8_E4M3, O.TOKEN_MAJOR, 1, npg, ts)
+    ok.write(slots, x), ov.write(slots, x), oi.write(slots, xi)
+    assert np.array_equal(k.pages.cpu().numpy(), ok.bytes)
+    assert np.array_equal(v.pages.cpu().numpy(), ov.bytes)
+    assert np.array_equal(idx.pages.cpu().numpy(), oi.bytes)
+
+
+@pytest.mark.parametrize("layout", ["token_major", "dim_major"])
+def test_debug_dequant_fp8_all_codes(M, oracle, layout):
+    """Every E4M3 byte in both FP8 slab layouts, bit-exact against the oracle (NaN codes give NaN)."""
+    print(f"[case] fp8 dequant {layout}", flush=True)
+    npg = 2
+    raw = (np.arange(npg * 16384) * 7 % 256).astype(np.uint8)
+    dm = layout == "dim_major"
+    c = M.Cache(_dev(raw), M.MSA_FP8_E4M3, M.MSA_DIM_MAJOR if dm else M.MSA_TOKEN_MAJOR, 1, npg, 0.3)
+    oc = O.OracleCache(O.FP8_E4M3, O.DIM_MAJOR if dm else O.TOKEN_MAJOR, 1, npg, 0.3)
+    oc.bytes[:] = raw
+    want = oc.dequant_pages(np.arange(npg))
+    for mode in (0, 1):
+        out = torch.empty((npg, 1, 128, 128), dtype=torch.float32, device="cuda")
+        M.msa_debug_dequant(c, _dev(np.arange(npg, dtype=np.int32)), mode, out)
+        got = out.cpu().numpy()
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], want[~nan])
 
 
 def test_quantize_e4m3_bitexact(M, oracle):
@@ -206,7 +263,8 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 
 # ---------------------------------------------------------------- steps 1+2
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
-                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short"])
+                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
+                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -299,7 +357,7 @@ def _out_err(got, ref):
 
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small",
-                                  "ragged", "ragged_r4", "r3", "r8"])
+                                  "ragged", "ragged_r4", "r3", "r8", "fp8_cfg3_small", "fp8_ragged_r4", "fp8_r8"])
 def test_sparse_decode_on_oracle_selection(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -371,10 +429,10 @@ def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False):
 
 def _sampled_caches(oracle, wl, rows):
     """Oracle caches holding only the pages of the sampled requests (and the shared prefix)."""
-    dt = oracle.F32 if wl.cache == "f32" else oracle.NVFP4
+    dt = {"f32": oracle.F32, "nvfp4": oracle.NVFP4, "fp8": oracle.FP8_E4M3}[wl.cache]
     ci = oracle.OracleCache(dt, oracle.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
     ck = oracle.OracleCache(dt, oracle.TOKEN_MAJOR, 4, wl.num_pages, wl.tensor_scale)
-    cv = oracle.OracleCache(dt, oracle.DIM_MAJOR if dt == oracle.NVFP4 else oracle.TOKEN_MAJOR, 4, wl.num_pages,
+    cv = oracle.OracleCache(dt, oracle.TOKEN_MAJOR if dt == oracle.F32 else oracle.DIM_MAJOR, 4, wl.num_pages,
                             wl.tensor_scale)
     if wl.prefix_tokens:
         pos = np.arange(wl.prefix_tokens, dtype=np.int64)
@@ -390,7 +448,8 @@ def _sampled_caches(oracle, wl, rows):
 
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
-                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short"])
+                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
+                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
@@ -400,7 +459,7 @@ def test_full_step(M, oracle, case, fused):
 
 
 @pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged", "ragged_r4", "r8",
-                                  "prefix_wide"])
+                                  "prefix_wide", "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r8"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step_with_new_rows(M, oracle, case, fused):
     """The step inserts each request's R new rows itself (fused: insert + index in one
@@ -501,6 +560,15 @@ def test_full_size_config4_sampled(M, oracle):
     wl = W.make_workload(4, seed=0)
     _print_case("config 4 full size", wl)
     _check_full_step(M, oracle, wl, sample=[0, 5])
+
+
+def test_full_size_config3_fp8_sampled(M, oracle):
+    """The 128K-context batch in FP8 caches at full size, the step inserting its new rows; the
+    oracle checks two sampled requests end to end."""
+    wl = W.make_workload(3, seed=0, cache="fp8")
+    _print_case("config 3 fp8 full size", wl)
+    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths))]
+    _check_full_step(M, oracle, wl, sample=rows, new_rows=True)
 
 
 def test_full_size_config5_sampled(M, oracle):
