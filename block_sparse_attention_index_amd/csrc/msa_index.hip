@@ -368,6 +368,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
       kw[ch][0] = nt_load4(slab + (16 * ch + n) * kDim + 16 * c);
       kw[ch][1] = nt_load4(slab + (16 * ch + n) * kDim + 64 + 16 * c);
     }
+    // the whole page's loads go out before the first product waits on one
+    // (left alone, the scheduler interleaves them with the products to save
+    // registers and the page arrives in several serial round trips)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
       const v8i Bop = v8i{(int)kw[ch][0].x, (int)kw[ch][0].y, (int)kw[ch][0].z, (int)kw[ch][0].w,
