@@ -10,15 +10,23 @@ namespace {
 
 bool finite_pos(float x) { return isfinite(x) && x > 0.0f; }
 
-int check_cache(const msa_cache* c, int want_heads, bool allow_dim_major, bool require_dim_major) {
+enum Role { KEYS, VALUES, INDEX };
+
+// The one slab layout each (dtype, role) uses.
+int required_layout(int32_t dtype, Role role) {
+  if (dtype == MSA_F32) return MSA_TOKEN_MAJOR;
+  if (role == VALUES) return MSA_DIM_MAJOR;
+  if (role == INDEX && dtype == MSA_FP8_E4M3) return MSA_HALF_ROWS;
+  return MSA_TOKEN_MAJOR;
+}
+
+int check_cache(const msa_cache* c, Role role) {
+  const int want_heads = role == INDEX ? 1 : 4;
   if (!c || !c->pages || c->num_pages < 1 || c->num_heads != want_heads) return MSA_ERR_INVALID_ARG;
   if (c->dtype != MSA_NVFP4 && c->dtype != MSA_FP8_E4M3 && c->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
-  if (c->layout != MSA_TOKEN_MAJOR && c->layout != MSA_DIM_MAJOR) return MSA_ERR_INVALID_ARG;
-  if (c->dtype == MSA_F32 && c->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
-  if (c->dtype != MSA_F32) {  // quantised caches: values dim-major, keys and index keys token-major
-    if (require_dim_major && c->layout != MSA_DIM_MAJOR) return MSA_ERR_UNSUPPORTED;
-    if (!allow_dim_major && c->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
-  }
+  if (c->layout != MSA_TOKEN_MAJOR && c->layout != MSA_DIM_MAJOR && c->layout != MSA_HALF_ROWS)
+    return MSA_ERR_INVALID_ARG;
+  if (c->layout != required_layout(c->dtype, role)) return MSA_ERR_UNSUPPORTED;
   if (!finite_pos(c->tensor_scale)) return MSA_ERR_INVALID_ARG;
   return MSA_OK;
 }
@@ -45,9 +53,9 @@ int insert_impl(const float* k, const float* v, const float* idx_k, const int64_
   if ((k != nullptr) != (kc != nullptr) || (v != nullptr) != (vc != nullptr) || (idx_k != nullptr) != (ic != nullptr))
     return MSA_ERR_INVALID_ARG;
   int st;
-  if (kc && (st = check_cache(kc, 4, false, false)) != MSA_OK) return st;
-  if (vc && (st = check_cache(vc, 4, true, vc->dtype != MSA_F32)) != MSA_OK) return st;
-  if (ic && (st = check_cache(ic, 1, false, false)) != MSA_OK) return st;
+  if (kc && (st = check_cache(kc, KEYS)) != MSA_OK) return st;
+  if (vc && (st = check_cache(vc, VALUES)) != MSA_OK) return st;
+  if (ic && (st = check_cache(ic, INDEX)) != MSA_OK) return st;
   if (nvfp4_only)
     for (const msa_cache* c : {kc, vc, ic})
       if (c && c->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
@@ -81,7 +89,7 @@ int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, 
                     const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream) {
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
-  if ((st = check_cache(idx_cache, 1, false, false)) != MSA_OK) return st;
+  if ((st = check_cache(idx_cache, INDEX)) != MSA_OK) return st;
   if (!q_idx || !block_scores) return MSA_ERR_INVALID_ARG;
   if ((st = query_dtype_ok(q_dtype, idx_cache)) != MSA_OK) return st;
   if (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
@@ -113,8 +121,8 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
                       size_t workspace_bytes, hipStream_t stream) {
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
-  if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype != MSA_F32)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
   if (k_cache->dtype != v_cache->dtype || k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
   if (!q || !sel_blocks || !sel_count || !out || !workspace) return MSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
@@ -133,8 +141,8 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
                       hipStream_t stream) {
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
-  if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype != MSA_F32)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
   if (k_cache->dtype == MSA_F32 || v_cache->dtype != k_cache->dtype) return MSA_ERR_UNSUPPORTED;
   if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
   if (!block_scores || !q || !sel_blocks || !sel_count || !out) return MSA_ERR_INVALID_ARG;
@@ -153,9 +161,9 @@ int msa_insert_index_score(const msa_batch* batch, const float* k_new, const flo
                            float* token_scores, hipStream_t stream) {
   int st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
-  if ((st = check_cache(k_cache, 4, false, false)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, 4, true, v_cache && v_cache->dtype != MSA_F32)) != MSA_OK) return st;
-  if ((st = check_cache(idx_cache, 1, false, false)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
+  if ((st = check_cache(idx_cache, INDEX)) != MSA_OK) return st;
   for (const msa_cache* c : {k_cache, v_cache, idx_cache})
     if (c->dtype == MSA_F32 || c->dtype != k_cache->dtype) return MSA_ERR_UNSUPPORTED;
   if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
@@ -184,6 +192,9 @@ int msa_debug_dequant(const msa_cache* cache, const int32_t* pages, int32_t n_pa
   if (!cache || !cache->pages || cache->num_heads < 1 || cache->num_pages < 1) return MSA_ERR_INVALID_ARG;
   if (cache->dtype != MSA_NVFP4 && cache->dtype != MSA_FP8_E4M3 && cache->dtype != MSA_F32) return MSA_ERR_UNSUPPORTED;
   if (cache->dtype == MSA_F32 && cache->layout != MSA_TOKEN_MAJOR) return MSA_ERR_UNSUPPORTED;
+  if (cache->layout == MSA_HALF_ROWS && cache->dtype != MSA_FP8_E4M3) return MSA_ERR_UNSUPPORTED;
+  if (cache->layout != MSA_TOKEN_MAJOR && cache->layout != MSA_DIM_MAJOR && cache->layout != MSA_HALF_ROWS)
+    return MSA_ERR_INVALID_ARG;
   if (n_pages < 0 || (n_pages > 0 && (!pages || !out)) || (mode != 0 && mode != 1)) return MSA_ERR_INVALID_ARG;
   if (n_pages == 0) return MSA_OK;
   return msa_launch_debug_dequant(cache, pages, n_pages, mode, out, stream) == 0 ? MSA_OK : MSA_ERR_HIP;

@@ -88,6 +88,14 @@ __device__ __forceinline__ h8 e2m1x8_to_h8(uint32_t w) {
 }
 
 // ---------------------------------------------------------------- slabs
+// Byte of token t (0..127), dim d of an FP8 slab in each layout: token-major
+// [t][d], dim-major [d][t], half rows [t/16][d/64][t%16][d%64].
+__device__ __forceinline__ int fp8_offset(int layout, int t, int d) {
+  if (layout == MSA_DIM_MAJOR) return d * kPage + t;
+  if (layout == MSA_HALF_ROWS) return (t >> 4) * 2048 + (d >> 6) * 1024 + (t & 15) * 64 + (d & 63);
+  return t * kDim + d;
+}
+
 // 16-byte load with the streaming (non-temporal) hint: data read once per step.
 __device__ __forceinline__ uint4 nt_load4(const uint8_t* p) {
   typedef unsigned int u4v __attribute__((ext_vector_type(4)));

@@ -283,14 +283,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) multiplies 16 tokens'
 // full 128-dim rows against 16 query rows with exact products: A row 4g + i
 // holds index query (group g, row 4*rp + i), B column n token n of a 16-token
-// chunk.  Lane group c of either operand carries bytes 16c..16c+15 and
-// 64+16c..64+16c+15 of its 128-byte row (the instruction's FP8 operand
-// layout, the same for A and B, so every product pairs equal dims).  Output
+// chunk.  Lane group c of either operand carries dims 16c..16c+15 and
+// 64+16c..64+16c+15 of its row (the instruction's FP8 operand layout, the
+// same for A and B, so every product pairs equal dims).  The index keys are
+// stored in half rows (16 tokens x dims 0..63, then x dims 64..127, 1 KB
+// each), so each of a chunk's two loads reads one whole, contiguous 1 KB.  Output
 // lane (n, c) holds the scores of group c, rows 4*rp .. 4*rp+3, token n; the
 // block max is a 16-lane row reduction.  Grid, chunk order and the fused
 // insert follow index_nvfp4_kernel (one page per wave, 4 per workgroup).
-template <int R, bool kTok, bool INSERT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_fp8_kernel(
+template <int R, bool kTok, bool INSERT, int WPE = 4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_fp8_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages,
     const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
     float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t B, NewRows NR) {
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                       ((int64_t)(valid ? ph : 0) * heads + head) * kFp8Slab;
       const int off = tok & (kPage - 1);
       const float ts = c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i);
-      if (valid) slab[c == 1 ? d * kPage + off : off * kDim + d] = (uint8_t)e4m3_encode(x / ts);
+      const int layout = c == 0 ? MSA_TOKEN_MAJOR : (c == 1 ? MSA_DIM_MAJOR : MSA_HALF_ROWS);
+      if (valid) slab[fp8_offset(layout, off, d)] = (uint8_t)e4m3_encode(x / ts);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
@@ -365,8 +368,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     uint4 kw[8][2];
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
-      kw[ch][0] = nt_load4(slab + (16 * ch + n) * kDim + 16 * c);
-      kw[ch][1] = nt_load4(slab + (16 * ch + n) * kDim + 64 + 16 * c);
+      kw[ch][0] = nt_load4(slab + ch * 2048 + n * 64 + 16 * c);
+      kw[ch][1] = nt_load4(slab + ch * 2048 + 1024 + n * 64 + 16 * c);
     }
     // the whole page's loads go out before the first product waits on one
     // (left alone, the scheduler interleaves them with the products to save

@@ -13,8 +13,8 @@
 // trip) -- tokens inserted together may share that dword.  One element per
 // lane keeps each lane's dependency chain to one quantisation (a single
 // IEEE division instead of sixteen in a row).  FP8 caches: each lane stores
-// its own element, E4M3(x / tensor_scale), one byte, at [token][dim] or
-// [dim][token].
+// its own element, E4M3(x / tensor_scale), one byte, where its slab layout
+// puts it (keys [token][dim], values [dim][token], index keys in half rows).
 #pragma clang fp contract(off)
 
 #include "msa_device.h"
@@ -34,7 +34,7 @@ struct InsertArgs {
   int32_t np0, np1, np2;     // page-pool sizes
   int32_t h0, h1, h2;        // heads
   int32_t nv0, nv1, nv2;     // msa_dtype: MSA_NVFP4, MSA_FP8_E4M3 or MSA_F32
-  int32_t dm0, dm1, dm2;     // 1 = dim-major slab
+  int32_t dm0, dm1, dm2;     // msa_layout of the slab
   float ts0, ts1, ts2;       // tensor scales
   int32_t u0, u1, u2;        // 16-dim groups per token (heads * 8), 0 if absent
 };
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
   const int32_t num_pages = c == 0 ? A.np0 : (c == 1 ? A.np1 : A.np2);
   const int32_t heads = c == 0 ? A.h0 : (c == 1 ? A.h1 : A.h2);
   const int32_t fmt = c == 0 ? A.nv0 : (c == 1 ? A.nv1 : A.nv2);
-  const int32_t dim_major = c == 0 ? A.dm0 : (c == 1 ? A.dm1 : A.dm2);
+  const int32_t layout = c == 0 ? A.dm0 : (c == 1 ? A.dm1 : A.dm2);
   const float ts = c == 0 ? A.ts0 : (c == 1 ? A.ts1 : A.ts2);
   const int head = u >> 3, grp = u & 7;
 
@@ -74,12 +74,13 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
   if (fmt == MSA_FP8_E4M3) {
     uint8_t* slab = pages + (page * heads + head) * (int64_t)kFp8Slab;
     const int d = grp * 16 + i;
-    if (valid) slab[dim_major ? d * kPage + off : off * kDim + d] = (uint8_t)e4m3_encode(x / ts);
+    if (valid) slab[fp8_offset(layout, off, d)] = (uint8_t)e4m3_encode(x / ts);
     return;
   }
   uint32_t code;
   const uint32_t sc = nvfp4_row_quantize(x, ts, code);
-  nvfp4_row_store(pages + (page * heads + head) * (int64_t)kNvSlab, off, grp, i, code, sc, dim_major != 0, valid);
+  nvfp4_row_store(pages + (page * heads + head) * (int64_t)kNvSlab, off, grp, i, code, sc, layout == MSA_DIM_MAJOR,
+                  valid);
 }
 
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* __restrict__ x, int64_t n, float scale,
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* __restr
 
 // One thread per (page, head, token, 8-dim chunk): decodes 8 elements.
 __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __restrict__ pages, int32_t num_pages,
-                                                            int32_t heads, int32_t fmt, int32_t dim_major,
+                                                            int32_t heads, int32_t fmt, int32_t layout,
                                                             float ts, const int32_t* __restrict__ page_ids,
                                                             int32_t n_pages, int32_t mode, float* __restrict__ out) {
   int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -116,14 +117,14 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
     const uint8_t* slab = pages + (page * heads + head) * (int64_t)kFp8Slab;
     for (int e = 0; e < 8; ++e) {
       const int d = chunk * 8 + e;
-      o[e] = e4m3_to_f32(slab[dim_major ? d * kPage + t : t * kDim + d]) * ts;
+      o[e] = e4m3_to_f32(slab[fp8_offset(layout, t, d)]) * ts;
     }
     return;
   }
   const uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
   uint32_t codes = 0;  // 8 nibbles, dim chunk*8 + e at nibble e
   uint8_t sc;
-  if (!dim_major) {
+  if (layout != MSA_DIM_MAJOR) {
     codes = *reinterpret_cast<const uint32_t*>(slab + t * 64 + chunk * 4);
     sc = slab[kScaleOff + t * 8 + chunk / 2];
   } else {
@@ -163,7 +164,7 @@ extern "C" int msa_launch_kv_insert(const float* k, const float* v, const float*
     np = c->num_pages;
     h = c->num_heads;
     nv = c->dtype;
-    dm = c->layout == MSA_DIM_MAJOR;
+    dm = c->layout;
     ts = c->tensor_scale;
     u = c->num_heads * 8;
   };
@@ -191,6 +192,6 @@ extern "C" int msa_launch_debug_dequant(const msa_cache* c, const int32_t* pages
   int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint8_t*)c->pages,
                      c->num_pages, c->num_heads, (int32_t)c->dtype,
-                     (int32_t)(c->layout == MSA_DIM_MAJOR), c->tensor_scale, pages, n_pages, mode, out);
+                     (int32_t)c->layout, c->tensor_scale, pages, n_pages, mode, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

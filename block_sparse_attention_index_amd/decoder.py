@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (MSA_DIM_MAJOR, MSA_F32, MSA_FP8_E4M3, MSA_NVFP4, MSA_TOKEN_MAJOR, Batch, Cache,
+from . import (MSA_DIM_MAJOR, MSA_F32, MSA_FP8_E4M3, MSA_HALF_ROWS, MSA_NVFP4, MSA_TOKEN_MAJOR, Batch, Cache,
                msa_block_maxpool_topk, msa_decode_workspace_bytes, msa_index_score, msa_insert_index_score,
                msa_kv_insert, msa_select_decode, msa_sparse_decode)
 
@@ -24,7 +24,7 @@ def make_caches(dtype, num_pages: int, tensor_scale: float, device="cuda"):
     dt = (MSA_NVFP4 if dtype else MSA_F32) if isinstance(dtype, bool) else dtype
     k = Cache.empty(dt, MSA_TOKEN_MAJOR, GROUPS, num_pages, tensor_scale, device)
     v = Cache.empty(dt, MSA_TOKEN_MAJOR if dt == MSA_F32 else MSA_DIM_MAJOR, GROUPS, num_pages, tensor_scale, device)
-    idx = Cache.empty(dt, MSA_TOKEN_MAJOR, 1, num_pages, tensor_scale, device)
+    idx = Cache.empty(dt, MSA_HALF_ROWS if dt == MSA_FP8_E4M3 else MSA_TOKEN_MAJOR, 1, num_pages, tensor_scale, device)
     return k, v, idx
 
 

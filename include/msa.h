@@ -58,7 +58,7 @@ typedef enum {
 
 typedef enum { MSA_F32 = 0, MSA_FP8_E4M3 = 1, MSA_NVFP4 = 2 } msa_dtype;
 
-typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1 } msa_layout;
+typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1, MSA_HALF_ROWS = 2 } msa_layout;
 
 #define MSA_PAGE_TOKENS 128
 #define MSA_HEAD_DIM 128
@@ -77,8 +77,16 @@ typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1 } msa_layout;
  *   MSA_FP8_E4M3, 16,384 B per slab: one E4M3 byte per element, value =
  *   e4m3 * tensor_scale (the pages' FP8 cache: 128 B of index keys and
  *   1,024 B of K+V per token and layer; one FP32 scale per cache tensor).
- *     MSA_TOKEN_MAJOR (keys, index keys): [128 tokens][128 dims].
+ *     MSA_TOKEN_MAJOR (keys): [128 tokens][128 dims].
  *     MSA_DIM_MAJOR (values): [128 dims][128 tokens].
+ *     MSA_HALF_ROWS (index keys): [8 chunks of 16 tokens][2 halves][16
+ *       tokens][64 dims]: token t, dim d at (t/16)*2048 + (d/64)*1024 +
+ *       (t%16)*64 + d%64.  One 1 KB half is exactly what a 64-lane load of
+ *       the indexer's FP8 matrix operand reads (16 tokens x 64 dims), so every
+ *       load uses whole cache lines.
+ * Required layouts: keys MSA_TOKEN_MAJOR; values MSA_DIM_MAJOR (NVFP4, FP8)
+ * or MSA_TOKEN_MAJOR (F32); index keys MSA_TOKEN_MAJOR (NVFP4, F32) or
+ * MSA_HALF_ROWS (FP8).  Any other combination is MSA_ERR_UNSUPPORTED.
  *   MSA_NVFP4, 9,216 B per slab.  Element value = (e2m1 * e4m3_scale) *
  *   tensor_scale; one E4M3 scale per 16 consecutive dims of a token (the
  *   block size that the pages' 34,560-vs-61,440 B per token fixes).

@@ -21,7 +21,7 @@ import numpy as np
 from . import build as _build
 
 F32, FP8_E4M3, NVFP4 = 0, 1, 2
-TOKEN_MAJOR, DIM_MAJOR = 0, 1
+TOKEN_MAJOR, DIM_MAJOR, HALF_ROWS = 0, 1, 2
 PAGE = 128
 DIM = 128
 NVFP4_SLAB = 9216

@@ -38,7 +38,7 @@
                                             FP8 index-key cost [P2 how MSA works] */
 
 enum { REF_F32 = 0, REF_FP8_E4M3 = 1, REF_NVFP4 = 2 };
-enum { REF_TOKEN_MAJOR = 0, REF_DIM_MAJOR = 1 };
+enum { REF_TOKEN_MAJOR = 0, REF_DIM_MAJOR = 1, REF_HALF_ROWS = 2 };
 
 /* ------------------------------------------------------------------------- */
 /* E4M3 [OCP]: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent 0
@@ -176,8 +176,10 @@ double ref_fp8_value(uint8_t code, float tensor_scale) { return ref_e4m3_value(c
  *   NVFP4 dim-major (V):
  *       codes  [128 dims][64 B]    (byte i of dim d: tokens 2i lo nibble, 2i+1 hi)
  *       scales [8 groups][128 tokens] (byte (j, t): scale of token t, dims 16j..)
- *   FP8 token-major (K and index keys): [128 tokens][128 dims], one E4M3 byte each
+ *   FP8 token-major (K): [128 tokens][128 dims], one E4M3 byte each
  *   FP8 dim-major (V): [128 dims][128 tokens]
+ *   FP8 half rows (index keys): [8 chunks of 16 tokens][2 halves of 64 dims]
+ *       [16 tokens][64 dims] -- a byte placement, the values are unchanged
  * The NVFP4 quantisation group is always 16 consecutive dims of one token;
  * only the placement of the bytes differs between the two layouts.          */
 typedef struct {
@@ -188,6 +190,13 @@ typedef struct {
   float tensor_scale;
   uint8_t* pages;
 } ref_cache;
+
+/* Byte of token t, dim d in an FP8 slab. */
+static int64_t fp8_byte(int layout, int t, int d) {
+  if (layout == REF_DIM_MAJOR) return (int64_t)d * REF_PAGE + t;
+  if (layout == REF_HALF_ROWS) return (int64_t)(t / 16) * 2048 + (d / 64) * 1024 + (t % 16) * 64 + d % 64;
+  return (int64_t)t * REF_DIM + d;
+}
 
 static int64_t slab_bytes(const ref_cache* c) {
   return c->dtype == REF_F32 ? REF_F32_SLAB : (c->dtype == REF_FP8_E4M3 ? REF_FP8_SLAB : REF_NVFP4_SLAB);
@@ -210,11 +219,7 @@ int ref_cache_write(const ref_cache* c, int64_t slot, int head, const float* x) 
   }
   if (c->dtype == REF_FP8_E4M3) {
     for (int d = 0; d < REF_DIM; ++d) {
-      uint8_t code = ref_fp8_quantize(x[d], c->tensor_scale);
-      if (c->layout == REF_TOKEN_MAJOR)
-        s[t * REF_DIM + d] = code;
-      else
-        s[d * REF_PAGE + t] = code;
+      s[fp8_byte(c->layout, t, d)] = ref_fp8_quantize(x[d], c->tensor_scale);
     }
     return 0;
   }
@@ -269,7 +274,7 @@ double ref_cache_value(const ref_cache* c, int64_t page, int head, int t, int d)
     return (double)v;
   }
   if (c->dtype == REF_FP8_E4M3)
-    return ref_fp8_value(c->layout == REF_TOKEN_MAJOR ? s[t * REF_DIM + d] : s[d * REF_PAGE + t], c->tensor_scale);
+    return ref_fp8_value(s[fp8_byte(c->layout, t, d)], c->tensor_scale);
   uint8_t code, sc;
   if (c->layout == REF_TOKEN_MAJOR) {
     uint8_t b = s[t * 64 + d / 2];

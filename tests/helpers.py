@@ -12,7 +12,7 @@ def oracle_caches(o, wl):
     """Fill the oracle's own caches from the seeded FP32 rows (oracle quantiser)."""
     dt = {"f32": o.F32, "nvfp4": o.NVFP4, "fp8": o.FP8_E4M3}[wl.cache]
     vlayout = o.TOKEN_MAJOR if dt == o.F32 else o.DIM_MAJOR
-    idx = o.OracleCache(dt, o.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
+    idx = o.OracleCache(dt, o.HALF_ROWS if dt == o.FP8_E4M3 else o.TOKEN_MAJOR, 1, wl.num_pages, wl.tensor_scale)
     k = o.OracleCache(dt, o.TOKEN_MAJOR, wl.G, wl.num_pages, wl.tensor_scale)
     v = o.OracleCache(dt, vlayout, wl.G, wl.num_pages, wl.tensor_scale)
     slots, xi, xk, xv = W.all_rows(wl)
@@ -96,13 +96,17 @@ def _e4m3_table():
 
 
 def decode_pages_f64(raw, nvfp4: bool, dim_major: bool, heads: int, num_pages: int, tensor_scale: float,
-                     fp8: bool = False):
+                     fp8: bool = False, half_rows: bool = False):
     """Exact float64 values [pages][heads][128 tok][128 dim] of a page pool, decoded from
     its bytes by the documented slab layout (test-side, independent of the oracle).
-    fp8: one E4M3 byte per element, [tok][dim] (token-major) or [dim][tok], times the
-    tensor scale."""
+    fp8: one E4M3 byte per element, [tok][dim] (token-major), [dim][tok] (dim_major) or
+    [tok/16][dim/64][tok%16][dim%64] (half_rows), times the tensor scale."""
     raw = np.asarray(raw, dtype=np.uint8)
     if fp8:
+        if half_rows:
+            b = raw.reshape(num_pages, heads, 8, 2, 16, 64)  # [chunk][half][tok][dim]
+            b = np.transpose(b, (0, 1, 2, 4, 3, 5)).reshape(num_pages, heads, 128, 128)
+            return _e4m3_table()[b] * tensor_scale
         v = _e4m3_table()[raw.reshape(num_pages, heads, 128, 128)] * tensor_scale
         return np.swapaxes(v, -1, -2) if dim_major else v
     if not nvfp4:

@@ -117,3 +117,33 @@ def test_workspace_size_formula(lib):
     b = Batch(32, 1, 1536, 0, fake, fake)
     # 4 splits of 4 blocks for top-16; FP32 route needs 16 splits of 1 block: the larger is reserved
     assert lib.msa_decode_workspace_bytes(C.byref(b), 16) == 32 * 4 * 16 * 8 * 130 * 4
+
+
+def test_layout_rules_without_gpu(lib):
+    """Each (dtype, role) has one slab layout: FP8 index keys in half rows, values dim-major,
+    keys token-major; anything else is refused before any launch."""
+    fake = C.c_void_p(0x1000)  # never dereferenced: validation fails first
+    good = Batch(2, 1, 8, 0, fake, fake)
+    FP8, NV, TM, DM, HR = 1, 2, 0, 1, 2
+    lib.msa_index_score.restype = C.c_int
+    for dt, lay, want in ((FP8, TM, -2), (FP8, DM, -2), (NV, HR, -2), (NV, 7, -1)):
+        idx = Cache(dt, lay, 1, 16, 0.01, fake)
+        assert lib.msa_index_score(C.byref(good), fake, 1, C.c_float(1.0), C.byref(idx), fake, None, None) == want
+    k8, v8, i8 = Cache(FP8, TM, 4, 16, 0.02, fake), Cache(FP8, DM, 4, 16, 0.02, fake), Cache(FP8, HR, 1, 16, 0.02, fake)
+    k8_hr = Cache(FP8, HR, 4, 16, 0.02, fake)
+    v_nv = Cache(NV, DM, 4, 16, 0.01, fake)
+    i_nv = Cache(NV, TM, 1, 16, 0.01, fake)
+    assert lib.msa_sparse_decode(C.byref(good), fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k8_hr),
+                                 C.byref(v8), fake, fake, 16, fake, fake, C.c_size_t(1 << 30), None) == -2
+    # keys and values of one format; the fused insert + index needs all three caches in one format
+    assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k8),
+                                 C.byref(v_nv), fake, fake, fake, None) == -2
+    assert lib.msa_insert_index_score(C.byref(good), fake, fake, fake, fake, 1, C.c_float(1.0), C.byref(k8),
+                                      C.byref(v8), C.byref(i_nv), fake, None, None) == -2
+    assert lib.msa_kv_insert_nvfp4(fake, None, None, fake, 4, C.byref(k8), None, None, None) == -2
+    # FP8 queries only, against FP8 caches
+    assert lib.msa_index_score(C.byref(good), fake, 0, C.c_float(1.0), C.byref(i8), fake, None, None) == -2
+    # the dequantisation aid: half rows exist only for FP8; unknown layouts are invalid
+    lib.msa_debug_dequant.restype = C.c_int
+    assert lib.msa_debug_dequant(C.byref(Cache(NV, HR, 1, 16, 0.01, fake)), fake, 1, 0, fake, None) == -2
+    assert lib.msa_debug_dequant(C.byref(Cache(FP8, 9, 1, 16, 0.01, fake)), fake, 1, 0, fake, None) == -1

@@ -186,22 +186,23 @@ def test_insert_fp8_special_values_bitexact(M, oracle):
     torch.cuda.synchronize()
     ok = O.OracleCache(O.FP8_E4M3, O.TOKEN_MAJOR, 4, npg, ts)
     ov = O.OracleCache(O.FP8_E4M3, O.DIM_MAJOR, 4, npg, ts)
-    oi = O.OracleCache(O.FP8_E4M3, O.TOKEN_MAJOR, 1, npg, ts)
+    oi = O.OracleCache(O.FP8_E4M3, O.HALF_ROWS, 1, npg, ts)
     ok.write(slots, x), ov.write(slots, x), oi.write(slots, xi)
     assert np.array_equal(k.pages.cpu().numpy(), ok.bytes)
     assert np.array_equal(v.pages.cpu().numpy(), ov.bytes)
     assert np.array_equal(idx.pages.cpu().numpy(), oi.bytes)
 
 
-@pytest.mark.parametrize("layout", ["token_major", "dim_major"])
+@pytest.mark.parametrize("layout", ["token_major", "dim_major", "half_rows"])
 def test_debug_dequant_fp8_all_codes(M, oracle, layout):
-    """Every E4M3 byte in both FP8 slab layouts, bit-exact against the oracle (NaN codes give NaN)."""
+    """Every E4M3 byte in the three FP8 slab layouts, bit-exact against the oracle (NaN codes give NaN)."""
     print(f"[case] fp8 dequant {layout}", flush=True)
     npg = 2
     raw = (np.arange(npg * 16384) * 7 % 256).astype(np.uint8)
-    dm = layout == "dim_major"
-    c = M.Cache(_dev(raw), M.MSA_FP8_E4M3, M.MSA_DIM_MAJOR if dm else M.MSA_TOKEN_MAJOR, 1, npg, 0.3)
-    oc = O.OracleCache(O.FP8_E4M3, O.DIM_MAJOR if dm else O.TOKEN_MAJOR, 1, npg, 0.3)
+    lay = {"token_major": (M.MSA_TOKEN_MAJOR, O.TOKEN_MAJOR), "dim_major": (M.MSA_DIM_MAJOR, O.DIM_MAJOR),
+           "half_rows": (M.MSA_HALF_ROWS, O.HALF_ROWS)}[layout]
+    c = M.Cache(_dev(raw), M.MSA_FP8_E4M3, lay[0], 1, npg, 0.3)
+    oc = O.OracleCache(O.FP8_E4M3, lay[1], 1, npg, 0.3)
     oc.bytes[:] = raw
     want = oc.dequant_pages(np.arange(npg))
     for mode in (0, 1):

@@ -274,11 +274,16 @@ def test_fp8_layouts_hold_the_same_values(oracle):
     slots = rng.choice(3 * 128, size=40, replace=False)
     tm = oracle.OracleCache(oracle.FP8_E4M3, oracle.TOKEN_MAJOR, 4, 3, ts)
     dm = oracle.OracleCache(oracle.FP8_E4M3, oracle.DIM_MAJOR, 4, 3, ts)
+    hr = oracle.OracleCache(oracle.FP8_E4M3, oracle.HALF_ROWS, 4, 3, ts)
     tm.write(slots, x)
     dm.write(slots, x)
+    hr.write(slots, x)
     a = tm.bytes.reshape(3, 4, 128, 128)
     b = dm.bytes.reshape(3, 4, 128, 128)
     assert np.array_equal(a, np.swapaxes(b, -1, -2))
+    # half rows: 16-token chunks, each as two 1 KB halves (dims 0..63, then 64..127)
+    h = hr.bytes.reshape(3, 4, 8, 2, 16, 64)
+    assert np.array_equal(a.reshape(3, 4, 8, 16, 2, 64), np.transpose(h, (0, 1, 2, 4, 3, 5)))
     codes = oracle.fp8_quantize(x, ts)
     for i, s in enumerate(slots):
         assert np.array_equal(a[s // 128, :, s % 128, :], codes[i])
@@ -286,5 +291,5 @@ def test_fp8_layouts_hold_the_same_values(oracle):
     for i, s in enumerate(slots[:5]):
         for h in range(4):
             for d in (0, 17, 127):
-                assert tm.value(int(s // 128), h, int(s % 128), d) == vals[codes[i, h, d]] * ts
-                assert dm.value(int(s // 128), h, int(s % 128), d) == vals[codes[i, h, d]] * ts
+                for c in (tm, dm, hr):
+                    assert c.value(int(s // 128), h, int(s % 128), d) == vals[codes[i, h, d]] * ts

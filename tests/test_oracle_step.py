@@ -78,7 +78,7 @@ def test_indexer_fp8_matches_numpy_over_dequantised_pages(oracle):
     _, _, qi, _ = oracle_queries(oracle, wl)
     bt = oracle_batch(oracle, wl)
     ts = oracle.index_scores(bt, qi, ci)
-    deq = decode_pages_f64(ci.bytes, False, False, 1, wl.num_pages, wl.tensor_scale, fp8=True)
+    deq = decode_pages_f64(ci.bytes, False, False, 1, wl.num_pages, wl.tensor_scale, fp8=True, half_rows=True)
     assert np.array_equal(ci.dequant_pages(np.arange(wl.num_pages)), deq.astype(np.float32))
     p = row_positions(wl)
     for b in range(wl.B):
