@@ -210,10 +210,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--config", type=int, default=CONFIG_ID, choices=[2, 3, 4, 5],
+    ap.add_argument("--config", type=int, default=CONFIG_ID, choices=[2, 3, 4, 5, 6],
                     help="workload: 3 = 32 requests at 64K-192K tokens (the default, the metric's own); "
                          "2 = 8 x 32K; 4 = 16 requests x 4 speculative rows; 5 = 64 requests sharing a "
-                         "256K-token prefix")
+                         "256K-token prefix; 6 = prefill, 4 prompts of 64K tokens whose last 2,048 form the chunk")
     ap.add_argument("--kv", choices=["nvfp4", "fp8"], default="nvfp4",
                     help="cache format of keys, values and index keys (default NVFP4, the metric's own)")
     ap.add_argument("--replicas", type=int, default=2)
@@ -293,6 +293,9 @@ def main():
         "decode": lambda d: d.attend(q, wl.q_scale, wl.sm_scale, stream),
         "select_decode": lambda d: d.select_attend(q, wl.q_scale, wl.sm_scale, stream),
     }
+    prefill = wl.R > M.MSA_MAX_ROWS  # a prefill chunk: no fused insert; the indexer is the dense kernel
+    if prefill:
+        del calls["insert_index"]
     P = wl.prefix_pages
     if P:
         # the prefix kernel alone: a batch whose table ends with the shared pages leaves the
@@ -323,7 +326,11 @@ def main():
     cnt = decs[0].cnt.cpu().numpy()
     nbytes = algorithmic_bytes(wl, sel, cnt)
     steps_per_s = 1e3 / ms_step
-    idx_gbps = nbytes["insert_index"] / (us["insert_index"] * 1e-6) / 1e9
+    idx_key = "index" if prefill else "insert_index"
+    idx_gbps = nbytes[idx_key] / (us[idx_key] * 1e-6) / 1e9
+    # prefill: every page of a request against its R*4 index queries (full pages, masked or not)
+    pages_scored = int(sum(-(-int(L) // 128) for L in wl.lengths))
+    prefill_flops = 2 * 128 * 128 * pages_scored * wl.R * 4
     prefix_flops = 2 * 128 * 128 * P * wl.B * wl.R * 4  # dims x tokens x index queries
     step_gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
 
@@ -355,15 +362,21 @@ def main():
                    "topk_blocks": wl.topk, "block_tokens": 128, "parallelism": "single-gpu",
                    "cache_replicas": len(decs), "hip_graph": use_graph,
                    "layer_steps_per_graph": per_graph if use_graph else None},
-        "roofline": {"bound": "hbm", "kernel": f"index_{wl.cache}_kernel with the insert fused in (steps 0-2)",
-                     "achieved": idx_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic() if headline else None,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE x 1, copy-calibrated)",
-                     "bytes_per_launch": nbytes["insert_index"], "avg_launch_us": us["insert_index"],
-                     "plain_scan": {"bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"],
-                                    "achieved": nbytes["index"] / (us["index"] * 1e-6) / 1e9,
-                                    "traffic": recorded_traffic("index-kernel-traffic-bytes-per-launch")
-                                    if headline else None}},
+        "roofline": ({"bound": "mfma", "kernel": "prefill_index_kernel (dense indexer on v_mfma_f32_16x16x32_f16)",
+                      "flops_per_launch": prefill_flops, "avg_launch_us": us["index"],
+                      "achieved": prefill_flops / (us["index"] * 1e-6) / 1e12, "peak": PEAK_F16_MFMA_TFLOPS,
+                      "unit": "TFLOP/s", "frac": prefill_flops / (us["index"] * 1e-6) / 1e12 / PEAK_F16_MFMA_TFLOPS,
+                      "traffic": None, "index_GBps": idx_gbps} if prefill else
+                     {"bound": "hbm", "kernel": f"index_{wl.cache}_kernel with the insert fused in (steps 0-2)",
+                      "achieved": idx_gbps,
+                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS,
+                      "traffic": recorded_traffic() if headline else None,
+                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE x 1, copy-calibrated)",
+                      "bytes_per_launch": nbytes["insert_index"], "avg_launch_us": us["insert_index"],
+                      "plain_scan": {"bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"],
+                                     "achieved": nbytes["index"] / (us["index"] * 1e-6) / 1e9,
+                                     "traffic": recorded_traffic("index-kernel-traffic-bytes-per-launch")
+                                     if headline else None}}),
         "prefix_mfma": None if not P else {
             "kernel": "prefix_index_kernel (shared-prefix scores on v_mfma_f32_16x16x32_f16)",
             "bound": "mfma", "flops_per_launch": prefix_flops, "avg_launch_us": us["prefix"],

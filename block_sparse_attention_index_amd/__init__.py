@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
 MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
 MSA_TOKEN_MAJOR, MSA_DIM_MAJOR, MSA_HALF_ROWS = 0, 1, 2
+MSA_MAX_ROWS, MSA_MAX_PREFILL_ROWS = 8, 8192
 PAGE_TOKENS = 128
 HEAD_DIM = 128
 HEADS_PER_GROUP = 8

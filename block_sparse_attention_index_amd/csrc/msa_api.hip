@@ -31,10 +31,14 @@ int check_cache(const msa_cache* c, Role role) {
   return MSA_OK;
 }
 
-int check_batch(const msa_batch* b) {
+// max_rows: MSA_MAX_ROWS for decode-only calls, MSA_MAX_PREFILL_ROWS where a
+// prefill chunk is accepted.
+int check_batch(const msa_batch* b, int max_rows = MSA_MAX_ROWS) {
   if (!b || !b->block_table || !b->ctx_lens) return MSA_ERR_INVALID_ARG;
-  if (b->num_reqs < 1 || b->rows_per_req < 1 || b->rows_per_req > MSA_MAX_ROWS || b->max_pages_per_req < 1)
+  if (b->num_reqs < 1 || b->rows_per_req < 1 || b->rows_per_req > max_rows || b->max_pages_per_req < 1)
     return MSA_ERR_INVALID_ARG;
+  // (request, row, group) rows are counted in 32-bit integers
+  if ((int64_t)b->num_reqs * b->rows_per_req * 4 > (int64_t)1 << 30) return MSA_ERR_INVALID_ARG;
   if (b->shared_prefix_pages < 0 || b->shared_prefix_pages > b->max_pages_per_req) return MSA_ERR_INVALID_ARG;
   // grid dimensions: y and z are 16-bit on this hardware
   if (b->num_reqs > 65535) return MSA_ERR_INVALID_ARG;
@@ -88,8 +92,9 @@ int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipS
 int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, float q_scale,
                     const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream) {
   int st;
-  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
   if ((st = check_cache(idx_cache, INDEX)) != MSA_OK) return st;
+  if (batch->rows_per_req > MSA_MAX_ROWS && idx_cache->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
   if (!q_idx || !block_scores) return MSA_ERR_INVALID_ARG;
   if ((st = query_dtype_ok(q_dtype, idx_cache)) != MSA_OK) return st;
   if (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
@@ -101,7 +106,7 @@ int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, 
 int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t scores_are_token_level,
                            int32_t topk, int32_t* sel_blocks, int32_t* sel_count, hipStream_t stream) {
   int st;
-  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
   if (!scores || !sel_blocks || !sel_count) return MSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
   if (scores_are_token_level != 0 && scores_are_token_level != 1) return MSA_ERR_INVALID_ARG;
@@ -111,7 +116,7 @@ int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t 
 }
 
 size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk) {
-  if (check_batch(batch) != MSA_OK || topk < 1 || topk > MSA_MAX_TOPK) return 0;
+  if (check_batch(batch, MSA_MAX_PREFILL_ROWS) != MSA_OK || topk < 1 || topk > MSA_MAX_TOPK) return 0;
   return msa_decode_partials_bytes(batch, topk);
 }
 
@@ -120,10 +125,11 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
                       const int32_t* sel_count, int32_t topk, float* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   int st;
-  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
   if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
   if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
   if (k_cache->dtype != v_cache->dtype || k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
+  if (batch->rows_per_req > MSA_MAX_ROWS && k_cache->dtype == MSA_F32) return MSA_ERR_UNSUPPORTED;
   if (!q || !sel_blocks || !sel_count || !out || !workspace) return MSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
   if ((st = query_dtype_ok(q_dtype, k_cache)) != MSA_OK) return st;
@@ -140,7 +146,7 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
                       const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,
                       hipStream_t stream) {
   int st;
-  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
   if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
   if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
   if (k_cache->dtype == MSA_F32 || v_cache->dtype != k_cache->dtype) return MSA_ERR_UNSUPPORTED;

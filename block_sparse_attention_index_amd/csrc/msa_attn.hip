@@ -460,19 +460,31 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
   auto vslab = [&](int ph) { return vpages + ((int64_t)max(ph, 0) * kGroups + g) * kSlab; };
   bool first = true;
   if constexpr (FP8) {
-    // FP8 blocks are twice the register bytes of NVFP4 ones: one block at a time
+    // FP8 blocks are twice the register bytes of NVFP4 ones, so one block's
+    // keys and values are held at a time, rolling: the next block's keys load
+    // once this block's keys are consumed (after S = K Q^T), its values once
+    // this block's P V is done
+    KRegs8 K;
+    VRegs8 V;
+    if (wave < nu) {
+      load_k(kslab(s_phys[wave]), lane, K);
+      load_v(vslab(s_phys[wave]), lane, V);
+    }
     for (int u = wave; u < nu; u += WAVES) {
       const int ph = s_phys[u];
-      KRegs8 K;
-      VRegs8 V;
-      load_k(kslab(ph), lane, K);
-      load_v(vslab(ph), lane, V);
+      const int un = u + WAVES;
+      auto next_k = [&]() {
+        if (un < nu) load_k(kslab(s_phys[un]), lane, K);
+      };
       if (ph >= 0) {
         int lim[QT];
         const bool part = block_lim(s_union[u], lim);
-        attend_block<QT>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, [] {});
+        attend_block<QT>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, next_k);
         first = false;
+      } else {
+        next_k();
       }
+      if (un < nu) load_v(vslab(s_phys[un]), lane, V);
     }
   } else
   // blocks wave, wave + WAVES, ... of the union, two at a time: the second

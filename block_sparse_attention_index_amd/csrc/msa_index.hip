@@ -543,6 +543,8 @@ extern "C" int msa_launch_index_score(const msa_batch* bt, const void* q_idx, in
                          ic->num_pages, block_scores, token_scores);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  if (bt->rows_per_req > MSA_MAX_ROWS)  // a prefill chunk (NVFP4): the dense matrix-core scorer
+    return msa_launch_prefill_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s);
   const float out_scale = ic->tensor_scale * q_scale;
   if (ic->dtype == MSA_FP8_E4M3)  // the shared-prefix declaration is not used with FP8 caches
     return launch_fp8_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, NewRows{}, s);

@@ -21,6 +21,8 @@ int msa_launch_insert_index_score(const msa_batch* b, const float* k_new, const 
                                   const msa_cache* ic, float* block_scores, float* token_scores, hipStream_t stream);
 int msa_launch_prefix_index(const msa_batch* b, const void* q_idx, float q_scale, const msa_cache* ic,
                             float* block_scores, float* token_scores, hipStream_t stream);
+int msa_launch_prefill_index(const msa_batch* b, const void* q_idx, float q_scale, const msa_cache* ic,
+                             float* block_scores, float* token_scores, hipStream_t stream);
 int msa_launch_topk(const msa_batch* b, const float* scores, int32_t token_level, int32_t topk, int32_t* sel,
                     int32_t* cnt, hipStream_t stream);
 size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk);

@@ -165,27 +165,26 @@ __device__ __forceinline__ void score_prefix_page(const h8* __restrict__ img, co
 
 }  // namespace
 
-// grid: one workgroup per (PPW pages, column tile of 64*NTILE), numbered so
-// that the column tiles of one page group fall on the same XCD (workgroups
-// are dealt round-robin to the 8 XCDs): id = 8*ny*(pg/8) + 8*yt + pg%8.
-// pos of column c = (b, r, g): the row's last visible token L_b - R + r.
+// One workgroup's work: pages pg*PPW .. +PPW-1 of table row `trow` (those
+// below n_valid have a table entry; the rest score -inf), for query columns
+// col_lo + 64*NTILE*yt .. (below col_hi).  Column c = (b*R + r)*4 + g is
+// index query (b, r, g); its last visible token is pos = L_b - R + r.
 template <int NTILE, int PPW, bool kTok>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefix_index_kernel(
-    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t B, int32_t R,
-    int32_t prefix_pages, const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages,
-    int32_t num_pages, float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t ny) {
-  __shared__ h8 s_img[2][kPfxImgH8];
+__device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ trow, const int32_t* __restrict__ lens,
+                                                 int32_t max_pages, int32_t R, int32_t n_pages, int32_t n_valid,
+                                                 int32_t col_lo, int32_t col_hi, int pg, int yt,
+                                                 const uint8_t* __restrict__ q_idx, float out_scale,
+                                                 const uint8_t* __restrict__ pages, int32_t num_pages,
+                                                 float* __restrict__ block_scores, float* __restrict__ token_scores,
+                                                 h8 (&s_img)[2][kPfxImgH8]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, a = lane >> 4;
-  const int id = (int)blockIdx.x;
-  const int pg = (id / (8 * ny)) * 8 + (id & 7);
-  const int yt = (id >> 3) % ny;
   const int j0 = pg * PPW;
-  if (j0 >= prefix_pages) return;  // the whole workgroup
-  const int jn = min(PPW, prefix_pages - j0);
-  const int ncols = B * R * kGroups;
-  const int col0 = yt * 64 * NTILE + wave * 16 * NTILE;
+  if (j0 >= n_pages) return;  // the whole workgroup
+  const int jn = min(PPW, n_pages - j0);
+  const int ncols = col_hi;
+  const int col0 = col_lo + yt * 64 * NTILE + wave * 16 * NTILE;
   const bool has_cols = col0 < ncols;  // wave-uniform; a wave without columns still dequantises
   const int64_t T = (int64_t)max_pages * kPage;
 
@@ -206,10 +205,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
   const int pmin = INT_MAX - (int)wave_umax(pkey);
 
-  // physical pages of the workgroup (row 0 of the block table names the shared pages), one per lane
+  // physical pages of the workgroup, one per lane
   int my_phys = -1;
-  if (lane < jn) {
-    my_phys = table[j0 + lane];
+  if (lane < jn && j0 + lane < n_valid) {
+    my_phys = trow[j0 + lane];
     if (my_phys < 0 || my_phys >= num_pages) my_phys = -1;
   }
   auto phys_of = [&](int k) { return __builtin_amdgcn_readfirstlane(__shfl(my_phys, k)); };
@@ -273,6 +272,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 }
 
+
+// Shared prefix: pages 0 .. P-1 of table row 0, every request's columns.
+// grid: one workgroup per (PPW pages, column tile of 64*NTILE), numbered so
+// that the column tiles of one page group fall on the same XCD (workgroups
+// are dealt round-robin to the 8 XCDs): id = 8*ny*(pg/8) + 8*yt + pg%8.
+template <int NTILE, int PPW, bool kTok>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefix_index_kernel(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t B, int32_t R,
+    int32_t prefix_pages, const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages,
+    int32_t num_pages, float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t ny) {
+  __shared__ h8 s_img[2][kPfxImgH8];
+  const int id = (int)blockIdx.x;
+  dense_index_body<NTILE, PPW, kTok>(table, lens, max_pages, R, prefix_pages, prefix_pages, 0, B * R * kGroups,
+                                     (id / (8 * ny)) * 8 + (id & 7), (id >> 3) % ny, q_idx, out_scale, pages,
+                                     num_pages, block_scores, token_scores, s_img);
+}
+
+// Prefill (many query rows per request): request b = blockIdx.y, all its
+// pages (those past its context score -inf) against its R*4 index queries;
+// the rows' causal limits mask the chunk's own pages per column.
+template <int NTILE, int PPW, bool kTok>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_index_kernel(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t R,
+    const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
+    float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t ny) {
+  __shared__ h8 s_img[2][kPfxImgH8];
+  const int id = (int)blockIdx.x, b = (int)blockIdx.y;
+  const int L = clamp_len(lens[b], max_pages);
+  const int ncols = R * kGroups;
+  dense_index_body<NTILE, PPW, kTok>(table + (int64_t)b * max_pages, lens, max_pages, R, max_pages,
+                                     (L + kPage - 1) / kPage, b * ncols, (b + 1) * ncols,
+                                     (id / (8 * ny)) * 8 + (id & 7), (id >> 3) % ny, q_idx, out_scale, pages,
+                                     num_pages, block_scores, token_scores, s_img);
+}
+
 template <int NTILE, int PPW>
 static int launch_prefix_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                              float* ts, hipStream_t s) {
@@ -292,9 +326,36 @@ static int launch_prefix_cfg(const msa_batch* bt, const uint8_t* q, float out_sc
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+template <int NTILE, int PPW>
+static int launch_prefill_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                              float* ts, hipStream_t s) {
+  const int ncols = bt->rows_per_req * kGroups;
+  const int ny = (ncols + 64 * NTILE - 1) / (64 * NTILE);
+  const int npg = (bt->max_pages_per_req + PPW - 1) / PPW;
+  const int npg8 = (npg + 7) / 8 * 8;
+  const dim3 grid((unsigned)(npg8 * ny), (unsigned)bt->num_reqs);
+  if (ts)
+    hipLaunchKernelGGL((prefill_index_kernel<NTILE, PPW, true>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, bt->rows_per_req, q, out_scale, (const uint8_t*)ic->pages,
+                       ic->num_pages, bs, ts, ny);
+  else
+    hipLaunchKernelGGL((prefill_index_kernel<NTILE, PPW, false>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, bt->rows_per_req, q, out_scale, (const uint8_t*)ic->pages,
+                       ic->num_pages, bs, ts, ny);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace msa
 
 using namespace msa;
+
+// Many query rows per request (a prefill chunk): every page of every request
+// scored for the request's R*4 index queries as a dense matrix-core product.
+extern "C" int msa_launch_prefill_index(const msa_batch* bt, const void* q_idx, float q_scale, const msa_cache* ic,
+                                        float* block_scores, float* token_scores, hipStream_t s) {
+  const float out_scale = ic->tensor_scale * q_scale;
+  return launch_prefill_cfg<4, 4>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, s);
+}
 
 // Scores and block maxima of pages [0, shared_prefix_pages) for every
 // (request, row, group); the per-request scan covers the pages after them.

@@ -10,7 +10,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (MSA_DIM_MAJOR, MSA_F32, MSA_FP8_E4M3, MSA_HALF_ROWS, MSA_NVFP4, MSA_TOKEN_MAJOR, Batch, Cache,
+from . import (MSA_DIM_MAJOR, MSA_F32, MSA_FP8_E4M3, MSA_HALF_ROWS, MSA_MAX_ROWS, MSA_NVFP4, MSA_TOKEN_MAJOR,
+               Batch, Cache,
                msa_block_maxpool_topk, msa_decode_workspace_bytes, msa_index_score, msa_insert_index_score,
                msa_kv_insert, msa_select_decode, msa_sparse_decode)
 
@@ -71,7 +72,7 @@ class MsaDecoder:
         must then be those of positions L_b - R .. L_b - 1, request-major (their slots follow from the block
         table and are not read)."""
         quant = self.k.dtype != MSA_F32
-        if fused and quant and new_tokens is not None:
+        if fused and quant and new_tokens is not None and self.batch.R <= MSA_MAX_ROWS:
             k, v, i, _ = new_tokens
             self.insert_index(k, v, i, q_idx, q_scale, None, stream)
         else:

@@ -64,6 +64,7 @@ typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1, MSA_HALF_ROWS = 2 } msa_l
 #define MSA_HEAD_DIM 128
 #define MSA_HEADS_PER_GROUP 8
 #define MSA_MAX_ROWS 8
+#define MSA_MAX_PREFILL_ROWS 8192
 #define MSA_MAX_TOPK 64
 #define MSA_NVFP4_GROUP 16
 #define MSA_NVFP4_SLAB_BYTES 9216
@@ -124,7 +125,9 @@ typedef struct {
  */
 typedef struct {
   int32_t num_reqs;            /* B >= 1                                        */
-  int32_t rows_per_req;        /* R in 1..MSA_MAX_ROWS (speculative rows)       */
+  int32_t rows_per_req;        /* R: 1..MSA_MAX_ROWS (decode, speculative rows); up to
+                                  MSA_MAX_PREFILL_ROWS (a prefill chunk) where a call
+                                  says so                                        */
   int32_t max_pages_per_req;   /* row stride of block_table (>= 1)              */
   int32_t shared_prefix_pages; /* P: leading table entries shared by every row, 0 if none */
   const int32_t* block_table;  /* device [B][max_pages_per_req] physical page ids */
@@ -165,6 +168,10 @@ int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipS
  * q_idx: [B][R][4][128], FP8 E4M3 bytes (times q_scale) with an NVFP4 index
  * cache, or FP32 with an F32 cache.  token_scores (may be NULL; a test aid):
  * [B][R][4][max_pages*128] per-token scores, -inf for invisible tokens.
+ * Prefill: with an NVFP4 index cache R may be up to MSA_MAX_PREFILL_ROWS (the
+ * rows of a prompt chunk at positions L_b - R .. L_b - 1); every page of a
+ * request is then scored for all its R*4 index queries as one dense
+ * matrix-core product (the pages' indexer prefill, vLLM post, "MSA 预填充").
  */
 int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, float q_scale,
                     const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream);
@@ -199,6 +206,7 @@ int msa_insert_index_score(const msa_batch* batch, const float* k_new, const flo
  * logical block ids, -1 padded; sel_count [B][R][4].  scores are block
  * scores [B][R][4][max_pages] (scores_are_token_level = 0) or token scores
  * [B][R][4][max_pages*128] that are max-pooled first (= 1).  1 <= topk <= 64.
+ * R up to MSA_MAX_PREFILL_ROWS.
  */
 int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t scores_are_token_level,
                            int32_t topk, int32_t* sel_blocks, int32_t* sel_count, hipStream_t stream);
@@ -217,6 +225,8 @@ size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk);
  * block get zeros.  workspace: device, >= msa_decode_workspace_bytes() (used
  * by the F32 route for per-block partial results; no initial contents
  * needed).  Two calls that share a workspace must not run concurrently.
+ * With NVFP4 or FP8 caches R may be up to MSA_MAX_PREFILL_ROWS (each row of a
+ * prefill chunk attends to its own selection).
  */
 int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
                       const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,

@@ -112,6 +112,9 @@ CASES = {
     # contexts shorter than, equal to and just past the shared prefix, two rows each
     "prefix_short": lambda: W.make_workload(5, seed=10, len_div=64, R=2,
                                             lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 9000)]),
+    # prefill chunks: many causal rows per request (the dense matrix-core indexer)
+    "prefill_r512": lambda: W.make_workload(6, seed=15, lengths=[8192], R=512),
+    "prefill_ragged": lambda: W.make_workload(6, seed=16, lengths=[3000, 5000, 200], R=300),
     # FP8 caches (E4M3 per element, FP32 tensor scale)
     "fp8_cfg3_small": lambda: W.make_workload(3, seed=11, B=4, len_div=48, cache="fp8"),
     "fp8_ragged": lambda: W.make_workload(3, seed=12, lengths=[1, 127, 128, 129, 2047, 2048, 2049, 5000], R=1,
@@ -265,7 +268,7 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 # ---------------------------------------------------------------- steps 1+2
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
-                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8"])
+                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -358,7 +361,8 @@ def _out_err(got, ref):
 
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small",
-                                  "ragged", "ragged_r4", "r3", "r8", "fp8_cfg3_small", "fp8_ragged_r4", "fp8_r8"])
+                                  "ragged", "ragged_r4", "r3", "r8", "fp8_cfg3_small", "fp8_ragged_r4", "fp8_r8",
+                                  "prefill_ragged"])
 def test_sparse_decode_on_oracle_selection(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -450,7 +454,7 @@ def _sampled_caches(oracle, wl, rows):
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
-                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8"])
+                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""

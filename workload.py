@@ -44,6 +44,8 @@ CONFIGS = {
             table="shuffled"),
     5: dict(name="shared_prefix_b64_256k", B=64, R=1, lens=("uniform", 1024, 8192), prefix=262144,
             cache="nvfp4", table="shuffled"),
+    # prefill: the last 2,048 tokens of 64K-token prompts scored, selected and attended as one chunk
+    6: dict(name="prefill_b4_2k_chunk_64k", B=4, R=2048, lens=("fixed", 65536), cache="nvfp4", table="shuffled"),
 }
 
 
