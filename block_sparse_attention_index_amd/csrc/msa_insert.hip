@@ -77,6 +77,29 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
     if (valid) slab[fp8_offset(layout, off, d)] = (uint8_t)e4m3_encode(x / ts);
     return;
   }
+  if (layout == MSA_DIM_MAJOR) {
+    // A value byte holds the nibbles of tokens 2k and 2k+1 of one dim.  When the
+    // token of an even slot is followed in the batch by the token of the next
+    // slot (a prompt chunk, tokens in order), this row quantises both and
+    // writes whole bytes; the follower's row writes nothing.  Other tokens
+    // merge their nibble into the shared dword with atomics.
+    const int64_t nxt = tok + 1 < n ? slots[tok + 1] : -1;
+    const int64_t prv = tok > 0 ? slots[tok - 1] : -1;
+    if (valid && (slot & 1) && prv == slot - 1) return;  // written by the previous token's row
+    if (valid && !(slot & 1) && nxt == slot + 1) {
+      const float x1 = src[((int64_t)(tok + 1) * heads + head) * kDim + grp * 16 + i];
+      uint32_t c0, c1;
+      const uint32_t s0 = nvfp4_row_quantize(x, ts, c0);
+      const uint32_t s1 = nvfp4_row_quantize(x1, ts, c1);
+      uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
+      slab[(grp * 16 + i) * 64 + (off >> 1)] = (uint8_t)(c0 | (c1 << 4));
+      if (i == 0) {
+        slab[kScaleOff + grp * 128 + off] = (uint8_t)s0;
+        slab[kScaleOff + grp * 128 + off + 1] = (uint8_t)s1;
+      }
+      return;
+    }
+  }
   uint32_t code;
   const uint32_t sc = nvfp4_row_quantize(x, ts, code);
   nvfp4_row_store(pages + (page * heads + head) * (int64_t)kNvSlab, off, grp, i, code, sc, layout == MSA_DIM_MAJOR,
