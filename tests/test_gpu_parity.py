@@ -523,12 +523,14 @@ def test_full_step_deterministic(M, oracle):
     assert torch.equal(a[2].view(torch.int32), dec.out.view(torch.int32))
 
 
+@pytest.mark.parametrize("case", ["cfg3_small", "fp8_cfg3_small", "prefix_wide", "prefill_r512"])
 @pytest.mark.parametrize("new_rows", [False, True])
-def test_graph_replay_matches_eager(M, oracle, new_rows):
+def test_graph_replay_matches_eager(M, oracle, case, new_rows):
     """The step has no memset nodes and no host sync: capture it and replay it several
-    times (with new rows, every replay inserts the same rows again, which is idempotent)."""
-    wl = CASES["cfg3_small"]()
-    _print_case(f"graph replay new_rows={new_rows}", wl)
+    times (with new rows, every replay inserts the same rows again, which is idempotent).
+    NVFP4, FP8, a shared prefix and a prefill chunk (separate insert, dense indexer)."""
+    wl = CASES[case]()
+    _print_case(f"graph replay {case} new_rows={new_rows}", wl)
     if new_rows:
         dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True)
     else:
