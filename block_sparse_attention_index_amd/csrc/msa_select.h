@@ -134,8 +134,8 @@ __device__ __forceinline__ int select_core(const float (&sc)[KMAX > 0 ? KMAX : 1
 // Per-wave LDS scratch of select_fast.
 constexpr int kSelCand = 512;  // candidate capacity (beyond it: the round-based selection)
 struct SelectScratch {
-  uint64_t heads[64];
-  uint64_t cand[kSelCand];
+  uint64_t cand[kSelCand + 64];  // candidates, then one discard slot per lane
+  int pick[64];                  // picked block ids by key rank
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -148,21 +148,40 @@ __device__ __forceinline__ uint64_t lanes_below_mask(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// The same selection as select_core with no serial rounds.  With need =
-// topk - 1 blocks to pick besides the latest:
-//  1. each lane takes the max of its candidate keys (its "head");
-//  2. T0 = the need-th largest head, found by ranking the 64 heads against
-//     each other (keys are distinct; lanes with no candidate hold 0, below
-//     every key, and at least need lanes hold one);
-//  3. every key among the need largest is >= T0 (the need heads >= T0 already
-//     outrank anything below it), and only the need lanes with heads >= T0
-//     can hold such keys, so the keys >= T0 -- compacted by ballot into LDS in
-//     ascending block order -- are at most need * KMAX candidates;
+// Number of lanes in a ballot, as a 32-bit count (kept on the scalar unit).
+__device__ __forceinline__ int ballot_count(uint64_t b) {
+  return __builtin_popcount((uint32_t)b) + __builtin_popcount((uint32_t)(b >> 32));
+}
+
+// The k-th largest (k >= 1) of the wave's 32-bit lane values, all lanes
+// active: bitwise from the top, the largest c with at least k lanes >= c (one
+// ballot count per bit).
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
+  uint32_t th = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = th | (1u << bit);
+    if (ballot_count(__ballot(v >= c)) >= k) th = c;
+  }
+  return th;
+}
+
+// The same selection as select_core with no serial rounds.  Candidate block
+// j (< latest) gets the 32-bit score key ck = order_key + 1 (absent blocks 0)
+// and the 64-bit key (ck, 0xFFFFFFFF - j), ordered as select_core's keys.
+// With need = topk - 1 blocks to pick besides the latest:
+//  1. each lane takes the max of its candidates' score keys (its "head");
+//  2. T = the need-th largest head (wave_kth_largest; at least need lanes
+//     hold a candidate, so T >= 1);
+//  3. the need largest keys all have score keys >= T (the need lanes with
+//     heads >= T hold need keys at least that large), so the keys with
+//     ck >= T -- compacted into LDS -- include them; with distinct scores
+//     they come only from those need lanes;
 //  4. a candidate's rank among the candidates is its rank among all keys: the
-//     need best are picked, and a ballot prefix count gives each its place in
-//     ascending block order.
-// Beyond kSelCand candidates (adversarial scores with KMAX = 0) it runs
-// select_core instead.  S: this wave's scratch.
+//     need best are picked, and each one's place in ascending block order is
+//     the number of picked ids below it.
+// Beyond kSelCand candidates (many equal scores) it runs select_core
+// instead.  S: this wave's scratch.
 template <int KMAX, typename ScoreOf, typename Emit>
 __device__ __forceinline__ int select_fast(const float (&sc)[KMAX > 0 ? KMAX : 1], ScoreOf score_of, int n, int topk,
                                            int lane, SelectScratch* S, Emit emit) {
@@ -176,70 +195,76 @@ __device__ __forceinline__ int select_fast(const float (&sc)[KMAX > 0 ? KMAX : 1
     if (lane == 0) emit(0, latest);
     return 1;
   }
-  auto key_of = [&](int j, float s) {
-    return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-  };
-  auto kmax = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
-  uint64_t keys[KMAX > 0 ? KMAX : 1];
-  uint64_t head = 0;
+  // score key of block j (a candidate, j < latest), or 0; branch-free
+  auto ck_of = [&](int j, float s) { return (order_key(s) + 1u) & (0u - (uint32_t)(j < latest)); };
+  auto key64 = [](uint32_t ck, int j) { return ((uint64_t)ck << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j); };
+  uint32_t ck[KMAX > 0 ? KMAX : 1];
+  uint32_t head = 0;
   if (KMAX > 0) {
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      const int j = lane + 64 * i;
-      keys[i] = j < latest ? key_of(j, sc[i]) : 0ull;
-    }
-    // pairwise tree: independent compares issue back to back
-    uint64_t t[KMAX > 0 ? KMAX : 1];
+    for (int i = 0; i < KMAX; ++i) ck[i] = ck_of(lane + 64 * i, sc[i]);
+    // pairwise tree: independent maxima issue back to back
+    uint32_t t[KMAX > 0 ? KMAX : 1];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) t[i] = keys[i];
+    for (int i = 0; i < KMAX; ++i) t[i] = ck[i];
 #pragma unroll
     for (int w = 1; w < KMAX; w *= 2)
 #pragma unroll
-      for (int i = 0; i + w < KMAX; i += 2 * w) t[i] = kmax(t[i], t[i + w]);
+      for (int i = 0; i + w < KMAX; i += 2 * w) t[i] = max(t[i], t[i + w]);
     head = t[0];
   } else {
-    for (int j = lane; j < latest; j += 64) head = kmax(head, key_of(j, score_of(j)));
+    for (int j = lane; j < latest; j += 64) head = max(head, ck_of(j, score_of(j)));
   }
-  S->heads[lane] = head;
-  wave_lds_sync();
-  int rk = 0;
-#pragma unroll 16
-  for (int i = 0; i < 64; ++i) rk += S->heads[i] > head ? 1 : 0;
-  const uint64_t at = __ballot(rk == need - 1);
-  const int src = __ffsll((unsigned long long)at) - 1;
-  const uint64_t T0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(head >> 32), src) << 32) |
-                      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)head, src);
-  // candidates >= T0 in ascending block order (block j = lane + 64 i: i-major, then lane)
+  const uint32_t T = wave_kth_largest(head, need);
   const uint64_t below = lanes_below_mask(lane);
   int C = 0;
-  auto add = [&](uint64_t k) {
-    const bool c = k >= T0;
-    const uint64_t bal = __ballot(c);
-    const int off = C + __popcll(bal & below);
-    if (c && off < kSelCand) S->cand[off] = k;
-    C += __popcll(bal);
-  };
   if (KMAX > 0) {
+    // each lane's candidates go to consecutive slots after those of the lanes
+    // below it (an exclusive count summed from ballots of the count's bits);
+    // other keys go to the lane's discard slot, so every store is unconditional
+    int mine = 0;
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) add(keys[i]);
+    for (int i = 0; i < KMAX; ++i) mine += ck[i] >= T ? 1 : 0;
+    int off = 0;
+#pragma unroll
+    for (int bit = 0; (1 << bit) <= KMAX; ++bit) {
+      const uint64_t bal = __ballot((mine >> bit) & 1);
+      off += ballot_count(bal & below) << bit;
+      C += ballot_count(bal) << bit;
+    }
+    if (C > kSelCand) return select_core<KMAX>(sc, score_of, n, topk, lane, emit);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      const bool c = ck[i] >= T;
+      S->cand[c ? off : kSelCand + lane] = key64(ck[i], lane + 64 * i);
+      off += c ? 1 : 0;
+    }
   } else {
     for (int base = 0; base < latest; base += 64) {
       const int j = base + lane;
-      add(j < latest ? key_of(j, score_of(min(j, latest - 1))) : 0ull);
+      const uint32_t k = ck_of(j, score_of(min(j, latest - 1)));
+      const bool c = k >= T;
+      const uint64_t bal = __ballot(c);
+      const int off = C + ballot_count(bal & below);
+      if (c && off < kSelCand) S->cand[off] = key64(k, j);
+      C += ballot_count(bal);
     }
+    if (C > kSelCand) return select_core<KMAX>(sc, score_of, n, topk, lane, emit);
   }
-  if (C > kSelCand) return select_core<KMAX>(sc, score_of, n, topk, lane, emit);
   wave_lds_sync();
-  int placed = 0;
   for (int base = 0; base < C; base += 64) {
     const int c = base + lane;
-    const uint64_t mine = c < C ? S->cand[c] : ~0ull;
+    const uint64_t mine = c < C ? S->cand[c] : 0ull;
     int r = 0;
     for (int m = 0; m < C; ++m) r += S->cand[m] > mine ? 1 : 0;
-    const bool pick = c < C && r < need;
-    const uint64_t bal = __ballot(pick);
-    if (pick) emit(placed + __popcll(bal & below), (int)(0xFFFFFFFFu - (uint32_t)mine));
-    placed += __popcll(bal);
+    if (c < C && r < need) S->pick[r] = (int)(0xFFFFFFFFu - (uint32_t)mine);
+  }
+  wave_lds_sync();
+  if (lane < need) {
+    const int id = S->pick[lane];
+    int pos = 0;
+    for (int m = 0; m < need; ++m) pos += S->pick[m] < id ? 1 : 0;
+    emit(pos, id);
   }
   if (lane == 0) emit(need, latest);
   return topk;
