@@ -15,7 +15,10 @@
 // scores, while the block-table row and the queries load.  With one row per
 // request, the 8 heads of a group share each dequantised K/V element (GQA);
 // with 4 speculative rows the 32 query vectors of a group fill two 16-column
-// query tiles.
+// query tiles.  Prefill chunks (more than 8 rows) take one row per workgroup
+// of 4 waves, one block per wave at a time, three workgroups per CU: their
+// rows select independently, so a row group's union would only multiply the
+// work.
 //
 // Per block and wave:
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16.  K codes go through the exact
@@ -210,33 +213,37 @@ struct ScaleSlot {
   h8 v[128];    // V scales in FP16, [group][token]
 };
 
+// NVFP4 value scales of one block to FP16 in the wave's LDS slot ([group][token]).
+__device__ __forceinline__ void stage_vscales(const VRegs& vr, ScaleSlot* slot, int lane) {
+  const uint32_t w[4] = {vr.vsc.x, vr.vsc.y, vr.vsc.z, vr.vsc.w};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const h2 s0 = e4m3x2_to_h2<false>(w[2 * i]), s1 = e4m3x2_to_h2<true>(w[2 * i]);
+    const h2 s2 = e4m3x2_to_h2<false>(w[2 * i + 1]), s3 = e4m3x2_to_h2<true>(w[2 * i + 1]);
+    slot->v[2 * lane + i] = h8{s0[0], s0[1], s1[0], s1[1], s2[0], s2[1], s3[0], s3[1]};
+  }
+}
+__device__ __forceinline__ void stage_vscales(const VRegs8&, ScaleSlot*, int) {}
+
 // One 128-token block: S^T = K Q^T, online-softmax update of `st`, O += P V.
 // lim[qt]: last visible token of the block for this lane's query column (-1:
 // none); `partial` (wave-uniform) says whether any lim is below 127; `first`
 // (wave-uniform) says the state is still empty, so nothing needs rescaling.
 // after_qk() runs once the key registers are consumed (the caller issues the
 // next block's loads there).
-template <int QT, typename KR, typename VR, typename AfterQK>
+template <int QT, bool LATE_VSC = false, typename KR, typename VR, typename AfterQK>
 __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h8 (&Q)[QT][4],
                                              const int (&lim)[QT], bool partial, bool first, float qk2, int lane,
                                              ScaleSlot* slot, AttnState<QT>& st, AfterQK after_qk) {
   constexpr bool FP8 = __is_same(KR, KRegs8);
   const int n = lane & 15, a = lane >> 4;
-  // ---- NVFP4 scales through LDS: each lane needs scales that other lanes of this wave loaded
+  // ---- NVFP4 scales through LDS: each lane needs scales that other lanes of
+  // this wave loaded.  Value scales go with the key scales, or with LATE_VSC
+  // after the softmax (the caller issues the value loads in after_qk)
   if constexpr (!FP8) {
-  slot->k[lane] = kr.ksc;
-  {
-    const uint32_t w[4] = {vr.vsc.x, vr.vsc.y, vr.vsc.z, vr.vsc.w};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const h2 s0 = e4m3x2_to_h2<false>(w[2 * i]), s1 = e4m3x2_to_h2<true>(w[2 * i]);
-      const h2 s2 = e4m3x2_to_h2<false>(w[2 * i + 1]), s3 = e4m3x2_to_h2<true>(w[2 * i + 1]);
-      slot->v[2 * lane + i] = h8{s0[0], s0[1], s1[0], s1[1], s2[0], s2[1], s3[0], s3[1]};
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    slot->k[lane] = kr.ksc;
+    if constexpr (!LATE_VSC) stage_vscales(vr, slot, lane);
+    wave_lds_sync();
   }
   const uint8_t* kraw = reinterpret_cast<const uint8_t*>(slot->k);
 
@@ -268,6 +275,8 @@ __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h
         Sacc[qt][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, Q[qt][ks], Sacc[qt][m], 0, 0, 0);
     }
   }
+  // with LATE_VSC the value loads issue here: keep them behind the key registers' last use
+  if constexpr (LATE_VSC) __builtin_amdgcn_sched_barrier(0);
   after_qk();
 
   // ---- online softmax, base 2 (token of Sacc[qt][m][q] = 32a + 8(m/2) + 4(m%2) + q)
@@ -316,6 +325,11 @@ __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h
     st.m[qt] = m_new;
   }
 
+  if constexpr (!FP8 && LATE_VSC) {
+    stage_vscales(vr, slot, lane);
+    wave_lds_sync();
+  }
+
   // ---- denominators: L += P . 1 (row sums of the FP16 P that the numerator uses)
   const h8 ones = h8{1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
@@ -350,15 +364,22 @@ constexpr int kTabLds = 2048;  // block-table rows up to this width are staged i
 // WAVES per workgroup: 8 with one query tile; 4 with two, so that each wave can
 // hold the doubled accumulators in registers (one wave per SIMD).
 // FP8: FP8 caches (one E4M3 byte per element), else NVFP4.
-template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8>
-__global__ __launch_bounds__(WAVES * 64) void attend_kernel(
+// PREFILL (NVFP4, one query tile, 4 waves): one row per workgroup and one
+// block per wave at a time (keys, then values once S = K Q^T is done), within
+// 128 registers, so that four workgroups share a CU and hide each other's
+// load latency -- the throughput form for chunks of thousands of rows, whose
+// rows select independently (no union to share).
+template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8, bool PREFILL = false>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREFILL ? 3 : 1))) void attend_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t R, int32_t max_pages,
     const uint8_t* __restrict__ q, float qk2, float v_scale, const uint8_t* __restrict__ kpages,
     const uint8_t* __restrict__ vpages, int32_t num_pages, const float* __restrict__ block_scores,
     int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t topk, float* __restrict__ out) {
+  static_assert(!PREFILL || (QT == 1 && WAVES == 4 && !FP8), "the prefill form is NVFP4, one tile, 4 waves");
   constexpr int NT = WAVES * 64;
   constexpr int NQ = QT * 16;  // query columns of the workgroup (rows nq.. are padding)
-  __shared__ int s_tab[kTabLds];
+  constexpr int RPW = PREFILL ? 1 : 4;  // rows per workgroup
+  __shared__ int s_tab[PREFILL ? 1 : kTabLds];
   __shared__ int s_rowsel[4 * MSA_MAX_TOPK];
   __shared__ int s_first[4 * MSA_MAX_TOPK];
   __shared__ int s_union[4 * MSA_MAX_TOPK];
@@ -369,13 +390,13 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
   __shared__ float s_fac[WAVES][NQ];  // each wave's factor exp2(m_w - M) per query row
   __shared__ float s_inv[NQ];         // v_scale / denominator per query row
   __shared__ ScaleSlot s_slot[FP8 ? 1 : WAVES];  // NVFP4: scales of each wave's current block
-  __shared__ SelectScratch s_sel[SELECT ? 4 : 1];  // selection scratch of waves 0..nr-1
+  __shared__ SelectScratch s_sel[SELECT ? RPW : 1];  // selection scratch of waves 0..nr-1
   __shared__ float s_o[WAVES][NQ / 2][kDim];  // each wave's rescaled output rows (half the columns at a time)
 
-  const int RG = (R + 3) / 4;
+  const int RG = (R + RPW - 1) / RPW;
   const int g = blockIdx.x / RG, rg = blockIdx.x % RG;
   const int b = blockIdx.y;
-  const int r0 = rg * 4, nr = min(4, R - r0);
+  const int r0 = rg * RPW, nr = min(RPW, R - r0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, a = lane >> 4;
 
@@ -387,7 +408,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
   h8 Q[QT][4];
   load_q<QT>(q, b, R, r0, nr, g, lane, Q);
   const int32_t* trow = table + (int64_t)b * max_pages;
-  const bool tab_lds = max_pages <= kTabLds;
+  const bool tab_lds = !PREFILL && max_pages <= kTabLds;
   if (tab_lds) {
     constexpr int PER = kTabLds / NT;
     int tv[PER];
@@ -459,7 +480,21 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
   auto kslab = [&](int ph) { return kpages + ((int64_t)max(ph, 0) * kGroups + g) * kSlab; };
   auto vslab = [&](int ph) { return vpages + ((int64_t)max(ph, 0) * kGroups + g) * kSlab; };
   bool first = true;
-  if constexpr (FP8) {
+  if constexpr (PREFILL) {
+    // one block at a time: its keys, then its values once the keys are consumed
+    for (int u = wave; u < nu; u += WAVES) {
+      const int ph = s_phys[u];
+      if (ph < 0) continue;
+      KRegs K;
+      VRegs V;
+      load_k(kslab(ph), lane, K);
+      int lim[QT];
+      const bool part = block_lim(s_union[u], lim);
+      attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[wave], st,
+                             [&] { load_v(vslab(ph), lane, V); });
+      first = false;
+    }
+  } else if constexpr (FP8) {
     // FP8 blocks are twice the register bytes of NVFP4 ones, so one block's
     // keys and values are held at a time, rolling: the next block's keys load
     // once this block's keys are consumed (after S = K Q^T), its values once
@@ -693,12 +728,26 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
   // scores enter the kernel's softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   const dim3 grid(kGroups * RG, bt->num_reqs);
+  const int km = SELECT ? select_kmax(P) : 8;
+  if (!FP8 && R > MSA_MAX_ROWS) {  // prefill chunk: one row per workgroup
+    const dim3 pgrid(kGroups * R, bt->num_reqs);
+#define MSA_PREFILL(K)                                                                                          \
+  hipLaunchKernelGGL((attend_kernel<1, SELECT, K, 4, false, true>), pgrid, dim3(256), 0, s, bt->block_table,      \
+                     bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,                     \
+                     (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out)
+    switch (km) {  // 48 candidates per lane do not fit the prefill form's registers: read them on demand
+      case 8: MSA_PREFILL(8); break;
+      case 24: MSA_PREFILL(24); break;
+      default: MSA_PREFILL(0); break;
+    }
+#undef MSA_PREFILL
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
 #define MSA_ATTEND(QT, K)                                                                                      \
   hipLaunchKernelGGL((attend_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4), FP8>), grid, dim3((QT == 1 ? 8 : 4) * 64),   \
                      0, s, bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale,                   \
                      (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt,  \
                      topk, out)
-  const int km = SELECT ? select_kmax(P) : 8;
   if (R <= 2) {
     switch (km) {
       case 8: MSA_ATTEND(1, 8); break;
