@@ -39,6 +39,7 @@
 //  * K and V are read with non-temporal 16-byte loads (each selected block is
 //    read once per step).
 #include <algorithm>
+#include <type_traits>
 
 #include "msa_device.h"
 #include "msa_kernels.h"
@@ -230,11 +231,16 @@ __device__ __forceinline__ void stage_vscales(const VRegs8&, ScaleSlot*, int) {}
 // none); `partial` (wave-uniform) says whether any lim is below 127; `first`
 // (wave-uniform) says the state is still empty, so nothing needs rescaling.
 // after_qk() runs once the key registers are consumed (the caller issues the
-// next block's loads there).
-template <int QT, bool LATE_VSC = false, typename KR, typename VR, typename AfterQK>
+// next block's loads there); before_pv() once the scores are consumed too.
+struct NoOp {
+  __device__ void operator()() const {}
+};
+
+template <int QT, bool LATE_VSC = false, typename KR, typename VR, typename AfterQK, typename BeforePV = NoOp>
 __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h8 (&Q)[QT][4],
                                              const int (&lim)[QT], bool partial, bool first, float qk2, int lane,
-                                             ScaleSlot* slot, AttnState<QT>& st, AfterQK after_qk) {
+                                             ScaleSlot* slot, AttnState<QT>& st, AfterQK after_qk,
+                                             BeforePV before_pv = {}) {
   constexpr bool FP8 = __is_same(KR, KRegs8);
   const int n = lane & 15, a = lane >> 4;
   // ---- NVFP4 scales through LDS: each lane needs scales that other lanes of
@@ -325,6 +331,8 @@ __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h
     st.m[qt] = m_new;
   }
 
+  if constexpr (LATE_VSC) __builtin_amdgcn_sched_barrier(0);
+  before_pv();
   if constexpr (!FP8 && LATE_VSC) {
     stage_vscales(vr, slot, lane);
     wave_lds_sync();
@@ -364,7 +372,7 @@ constexpr int kTabLds = 2048;  // block-table rows up to this width are staged i
 // WAVES per workgroup: 8 with one query tile; 4 with two, so that each wave can
 // hold the doubled accumulators in registers (one wave per SIMD).
 // FP8: FP8 caches (one E4M3 byte per element), else NVFP4.
-// PREFILL (NVFP4, one query tile, 4 waves): one row per workgroup and one
+// PREFILL (one query tile, 4 waves): one row per workgroup and one
 // block per wave at a time (keys, then values once S = K Q^T is done), within
 // 128 registers, so that four workgroups share a CU and hide each other's
 // load latency -- the throughput form for chunks of thousands of rows, whose
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
     const uint8_t* __restrict__ q, float qk2, float v_scale, const uint8_t* __restrict__ kpages,
     const uint8_t* __restrict__ vpages, int32_t num_pages, const float* __restrict__ block_scores,
     int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t topk, float* __restrict__ out) {
-  static_assert(!PREFILL || (QT == 1 && WAVES == 4 && !FP8), "the prefill form is NVFP4, one tile, 4 waves");
+  static_assert(!PREFILL || (QT == 1 && WAVES == 4), "the prefill form has one query tile and 4 waves");
   constexpr int NT = WAVES * 64;
   constexpr int NQ = QT * 16;  // query columns of the workgroup (rows nq.. are padding)
   constexpr int RPW = PREFILL ? 1 : 4;  // rows per workgroup
@@ -485,13 +493,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
     for (int u = wave; u < nu; u += WAVES) {
       const int ph = s_phys[u];
       if (ph < 0) continue;
-      KRegs K;
-      VRegs V;
+      std::conditional_t<FP8, KRegs8, KRegs> K;
+      std::conditional_t<FP8, VRegs8, VRegs> V;
       load_k(kslab(ph), lane, K);
       int lim[QT];
       const bool part = block_lim(s_union[u], lim);
-      attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[wave], st,
-                             [&] { load_v(vslab(ph), lane, V); });
+      // NVFP4 values load during the softmax; FP8 values (twice the
+      // registers) once the scores are consumed
+      auto ld_v = [&] { load_v(vslab(ph), lane, V); };
+      if constexpr (FP8)
+        attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, NoOp{}, ld_v);
+      else
+        attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[wave], st, ld_v);
       first = false;
     }
   } else if constexpr (FP8) {
@@ -729,10 +742,10 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   const dim3 grid(kGroups * RG, bt->num_reqs);
   const int km = SELECT ? select_kmax(P) : 8;
-  if (!FP8 && R > MSA_MAX_ROWS) {  // prefill chunk: one row per workgroup
+  if (R > MSA_MAX_ROWS) {  // prefill chunk: one row per workgroup
     const dim3 pgrid(kGroups * R, bt->num_reqs);
 #define MSA_PREFILL(K)                                                                                          \
-  hipLaunchKernelGGL((attend_kernel<1, SELECT, K, 4, false, true>), pgrid, dim3(256), 0, s, bt->block_table,      \
+  hipLaunchKernelGGL((attend_kernel<1, SELECT, K, 4, FP8, true>), pgrid, dim3(256), 0, s, bt->block_table,        \
                      bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,                     \
                      (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out)
     switch (km) {  // 48 candidates per lane do not fit the prefill form's registers: read them on demand

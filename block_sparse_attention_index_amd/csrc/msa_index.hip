@@ -313,28 +313,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int lo = chunk * 4 * kPage;
     const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * kPage);
     constexpr int kPerTok = 9 * kDim;
-    for (int e = threadIdx.x; e < (t1 - t0) * kPerTok; e += 256) {
-      const int tok = t0 + e / kPerTok;
-      int u = e % kPerTok;
-      const int c = u < 4 * kDim ? 0 : (u < 8 * kDim ? 1 : 2);
-      u -= c * 4 * kDim;
-      const int heads = c == 2 ? 1 : kGroups;
-      const int head = u / kDim, d = u % kDim;
-      const int r = tok - (L - R);
-      const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
-      const float x = src[(((int64_t)b * R + r) * heads + head) * kDim + d];
-      const int ph = table[(int64_t)b * max_pages + tok / kPage];
-      const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
-      uint8_t* slab = (c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages)) +
-                      ((int64_t)(valid ? ph : 0) * heads + head) * kFp8Slab;
-      const int off = tok & (kPage - 1);
-      const float ts = c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i);
-      const int layout = c == 0 ? MSA_TOKEN_MAJOR : (c == 1 ? MSA_DIM_MAJOR : MSA_HALF_ROWS);
-      if (valid) slab[fp8_offset(layout, off, d)] = (uint8_t)e4m3_encode(x / ts);
+    if (t0 < t1) {  // uniform over the workgroup
+      for (int e = threadIdx.x; e < (t1 - t0) * kPerTok; e += 256) {
+        const int tok = t0 + e / kPerTok;
+        int u = e % kPerTok;
+        const int c = u < 4 * kDim ? 0 : (u < 8 * kDim ? 1 : 2);
+        u -= c * 4 * kDim;
+        const int heads = c == 2 ? 1 : kGroups;
+        const int head = u / kDim, d = u % kDim;
+        const int r = tok - (L - R);
+        const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
+        const float x = src[(((int64_t)b * R + r) * heads + head) * kDim + d];
+        const int ph = table[(int64_t)b * max_pages + tok / kPage];
+        const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
+        uint8_t* slab = (c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages)) +
+                        ((int64_t)(valid ? ph : 0) * heads + head) * kFp8Slab;
+        const int off = tok & (kPage - 1);
+        const float ts = c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i);
+        const int layout = c == 0 ? MSA_TOKEN_MAJOR : (c == 1 ? MSA_DIM_MAJOR : MSA_HALF_ROWS);
+        if (valid) slab[fp8_offset(layout, off, d)] = (uint8_t)e4m3_encode(x / ts);
+      }
+      // the index keys just written are read back by this workgroup's waves
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
   const int j = chunk * 4 + wave;
   if (j >= max_pages) return;

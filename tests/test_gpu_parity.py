@@ -122,6 +122,8 @@ CASES = {
     "fp8_ragged_r4": lambda: W.make_workload(4, seed=13, lengths=[0, 2, 3, 4, 131, 2051, 2052, 7000], R=4,
                                              cache="fp8"),
     "fp8_r8": lambda: W.make_workload(4, seed=14, B=2, len_div=64, R=8, cache="fp8"),
+    # a prefill chunk in FP8 caches (attention only: FP8 prefill indexing is not offered)
+    "fp8_prefill": lambda: W.make_workload(6, seed=17, lengths=[3000, 1000, 130], R=300, cache="fp8"),
     "r8": lambda: W.make_workload(4, seed=8, B=2, len_div=64, R=8),
 }
 
@@ -362,7 +364,7 @@ def _out_err(got, ref):
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small",
                                   "ragged", "ragged_r4", "r3", "r8", "fp8_cfg3_small", "fp8_ragged_r4", "fp8_r8",
-                                  "prefill_ragged"])
+                                  "prefill_ragged", "fp8_prefill"])
 def test_sparse_decode_on_oracle_selection(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -510,6 +512,39 @@ def test_select_decode_equals_separate_calls(M, oracle, case):
     torch.cuda.synchronize()
     assert torch.equal(dec.cnt, cnt_a) and torch.equal(dec.sel, sel_a)
     assert torch.equal(dec.out.view(torch.int32), out_a.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", ["prefill_ragged", "fp8_prefill"])
+def test_prefill_select_decode_on_oracle_scores(M, oracle, case):
+    """Prefill chunks (one row per workgroup): from the oracle's block scores rounded to FP32,
+    the fused selection + attention equals msa_block_maxpool_topk + msa_sparse_decode bitwise,
+    the selection equals the oracle's on the same FP32 scores, and the output matches the
+    oracle's attention on it."""
+    wl = CASES[case]()
+    _print_case(case, wl)
+    dec, q_idx, q = gpu_setup(M, wl)
+    ci, ck, cv = oracle_caches(oracle, wl)
+    _, _, qi, qd = oracle_queries(oracle, wl)
+    bt = oracle_batch(oracle, wl)
+    bs32 = oracle.block_maxpool(bt, oracle.index_scores(bt, qi, ci)).astype(np.float32)
+    dec.block_scores.copy_(_dev(bs32))
+    dec.select()
+    dec.attend(q, wl.q_scale, wl.sm_scale)
+    sel_a, cnt_a, out_a = dec.sel.clone(), dec.cnt.clone(), dec.out.clone()
+    dec.sel.fill_(-5), dec.cnt.fill_(-5), dec.out.fill_(7.0)
+    dec.select_attend(q, wl.q_scale, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dec.cnt, cnt_a) and torch.equal(dec.sel, sel_a)
+    assert torch.equal(dec.out.view(torch.int32), out_a.view(torch.int32))
+    rs, rc = oracle.select(bt, bs32.astype(np.float64), wl.topk)
+    assert np.array_equal(cnt_a.cpu().numpy(), rc) and np.array_equal(sel_a.cpu().numpy(), rs)
+    ref = oracle.attention(bt, qd, wl.sm_scale, ck, cv, rs, rc)
+    got = out_a.cpu().numpy().astype(np.float64)
+    empty = np.repeat(rc == 0, 8, axis=2)
+    assert (got[empty] == 0).all()
+    err = _out_err(got, ref)
+    print(f"  max per-vector relative error {err[~empty].max() if (~empty).any() else 0:.3e}", flush=True)
+    assert err[~empty].max(initial=0.0) <= OUT_TOL
 
 
 def test_full_step_deterministic(M, oracle):
