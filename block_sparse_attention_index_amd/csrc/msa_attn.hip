@@ -377,16 +377,18 @@ constexpr int kTabLds = 2048;  // block-table rows up to this width are staged i
 // 128 registers, so that four workgroups share a CU and hide each other's
 // load latency -- the throughput form for chunks of thousands of rows, whose
 // rows select independently (no union to share).
-template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8, bool PREFILL = false>
+// RPW: rows per workgroup, 4 (the union of a row group) or 1 (each row on
+// its own, more workgroups: used while the batch leaves CUs idle).
+template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8, int RPW, bool PREFILL = false>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREFILL ? 3 : 1))) void attend_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t R, int32_t max_pages,
     const uint8_t* __restrict__ q, float qk2, float v_scale, const uint8_t* __restrict__ kpages,
     const uint8_t* __restrict__ vpages, int32_t num_pages, const float* __restrict__ block_scores,
     int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t topk, float* __restrict__ out) {
-  static_assert(!PREFILL || (QT == 1 && WAVES == 4), "the prefill form has one query tile and 4 waves");
+  static_assert(!PREFILL || (QT == 1 && WAVES == 4 && RPW == 1), "the prefill form: one tile, 4 waves, one row");
+  static_assert(RPW == 1 || RPW == 4, "rows per workgroup: 1 or 4");
   constexpr int NT = WAVES * 64;
   constexpr int NQ = QT * 16;  // query columns of the workgroup (rows nq.. are padding)
-  constexpr int RPW = PREFILL ? 1 : 4;  // rows per workgroup
   __shared__ int s_tab[PREFILL ? 1 : kTabLds];
   __shared__ int s_rowsel[4 * MSA_MAX_TOPK];
   __shared__ int s_first[4 * MSA_MAX_TOPK];
@@ -731,21 +733,32 @@ extern "C" size_t msa_decode_partials_bytes(const msa_batch* bt, int32_t topk) {
   return q * (kDim + 2) * sizeof(float);
 }
 
+// Compute units of the current device (queried once per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // NVFP4 and FP8 route: one launch, selection fused in when block_scores != NULL.
 template <bool SELECT, bool FP8>
 static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, float sm_scale,
                                const msa_cache* kc, const msa_cache* vc, const float* block_scores, int32_t* sel,
                                int32_t* cnt, int32_t topk, float* out, hipStream_t s) {
   const int R = bt->rows_per_req, P = bt->max_pages_per_req;
-  const int RG = (R + 3) / 4;
   // scores enter the kernel's softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
-  const dim3 grid(kGroups * RG, bt->num_reqs);
   const int km = SELECT ? select_kmax(P) : 8;
   if (R > MSA_MAX_ROWS) {  // prefill chunk: one row per workgroup
     const dim3 pgrid(kGroups * R, bt->num_reqs);
 #define MSA_PREFILL(K)                                                                                          \
-  hipLaunchKernelGGL((attend_kernel<1, SELECT, K, 4, FP8, true>), pgrid, dim3(256), 0, s, bt->block_table,        \
+  hipLaunchKernelGGL((attend_kernel<1, SELECT, K, 4, FP8, 1, true>), pgrid, dim3(256), 0, s, bt->block_table,     \
                      bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,                     \
                      (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out)
     switch (km) {  // 48 candidates per lane do not fit the prefill form's registers: read them on demand
@@ -756,26 +769,33 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
 #undef MSA_PREFILL
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-#define MSA_ATTEND(QT, K)                                                                                      \
-  hipLaunchKernelGGL((attend_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4), FP8>), grid, dim3((QT == 1 ? 8 : 4) * 64),   \
-                     0, s, bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale,                   \
-                     (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt,  \
-                     topk, out)
-  if (R <= 2) {
-    switch (km) {
-      case 8: MSA_ATTEND(1, 8); break;
-      case 24: MSA_ATTEND(1, 24); break;
-      case 48: MSA_ATTEND(1, 48); break;
-      default: MSA_ATTEND(1, 0); break;
-    }
-  } else {
-    switch (km) {
-      case 8: MSA_ATTEND(2, 8); break;
-      case 24: MSA_ATTEND(2, 24); break;
-      case 48: MSA_ATTEND(2, 48); break;
-      default: MSA_ATTEND(2, 0); break;
-    }
+  // Several rows per request: one workgroup per row while that grid does not
+  // exceed the CU count (a small batch, latency-bound: rows that select
+  // independently share few blocks, so a row group's union is nearly R times
+  // one row's work on one CU); beyond it, one workgroup per group of up to 4
+  // rows walking the union of their sets (rows that select alike share the
+  // reads and the dequantisation).
+  const bool per_row = R == 1 || (int64_t)bt->num_reqs * R * kGroups <= cu_count();
+#define MSA_ATTEND(QT, K, RPW)                                                                                  \
+  hipLaunchKernelGGL((attend_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4), FP8, RPW>),                              \
+                     dim3(kGroups * ((R + RPW - 1) / RPW), bt->num_reqs), dim3((QT == 1 ? 8 : 4) * 64), 0, s,       \
+                     bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,    \
+                     (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out)
+#define MSA_ATTEND_K(QT, RPW)           \
+  switch (km) {                         \
+    case 8: MSA_ATTEND(QT, 8, RPW); break;   \
+    case 24: MSA_ATTEND(QT, 24, RPW); break; \
+    case 48: MSA_ATTEND(QT, 48, RPW); break; \
+    default: MSA_ATTEND(QT, 0, RPW); break;  \
   }
+  if (per_row) {
+    MSA_ATTEND_K(1, 1)
+  } else if (R <= 2) {
+    MSA_ATTEND_K(1, 4)
+  } else {
+    MSA_ATTEND_K(2, 4)
+  }
+#undef MSA_ATTEND_K
 #undef MSA_ATTEND
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -131,6 +131,8 @@ __device__ __forceinline__ int select_core(const float (&sc)[KMAX > 0 ? KMAX : 1
   return topk;
 }
 
+constexpr float kNoScores[1] = {0.f};  // select_core<0> reads its scores through score_of
+
 // Per-wave LDS scratch of select_fast.
 constexpr int kSelCand = 512;  // candidate capacity (beyond it: the round-based selection)
 struct SelectScratch {
@@ -181,7 +183,8 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
 //     need best are picked, and each one's place in ascending block order is
 //     the number of picked ids below it.
 // Beyond kSelCand candidates (many equal scores) it runs select_core
-// instead.  S: this wave's scratch.
+// instead, reading the scores again through score_of (so that the register
+// copies need not stay live).  S: this wave's scratch.
 template <int KMAX, typename ScoreOf, typename Emit>
 __device__ __forceinline__ int select_fast(const float (&sc)[KMAX > 0 ? KMAX : 1], ScoreOf score_of, int n, int topk,
                                            int lane, SelectScratch* S, Emit emit) {
@@ -232,7 +235,7 @@ __device__ __forceinline__ int select_fast(const float (&sc)[KMAX > 0 ? KMAX : 1
       off += ballot_count(bal & below) << bit;
       C += ballot_count(bal) << bit;
     }
-    if (C > kSelCand) return select_core<KMAX>(sc, score_of, n, topk, lane, emit);
+    if (C > kSelCand) return select_core<0>(kNoScores, score_of, n, topk, lane, emit);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       const bool c = ck[i] >= T;
@@ -249,7 +252,7 @@ __device__ __forceinline__ int select_fast(const float (&sc)[KMAX > 0 ? KMAX : 1
       if (c && off < kSelCand) S->cand[off] = key64(k, j);
       C += ballot_count(bal);
     }
-    if (C > kSelCand) return select_core<KMAX>(sc, score_of, n, topk, lane, emit);
+    if (C > kSelCand) return select_core<0>(kNoScores, score_of, n, topk, lane, emit);
   }
   wave_lds_sync();
   for (int base = 0; base < C; base += 64) {

@@ -125,6 +125,10 @@ CASES = {
     # a prefill chunk in FP8 caches (attention only: FP8 prefill indexing is not offered)
     "fp8_prefill": lambda: W.make_workload(6, seed=17, lengths=[3000, 1000, 130], R=300, cache="fp8"),
     "r8": lambda: W.make_workload(4, seed=8, B=2, len_div=64, R=8),
+    # batches whose B*R*4 workgroup rows exceed the 256 CUs: attention walks row-group unions
+    # (two query tiles for R=4, one for R=2) instead of one workgroup per row
+    "union_r4": lambda: W.make_workload(4, seed=18, B=20, len_div=64, R=4),
+    "union_r2": lambda: W.make_workload(4, seed=19, B=40, len_div=128, R=2),
 }
 
 
@@ -456,7 +460,8 @@ def _sampled_caches(oracle, wl, rows):
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
-                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged"])
+                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
+                                  "union_r4", "union_r2"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
@@ -496,7 +501,7 @@ def test_insert_index_equals_separate_calls(M, oracle, case):
     assert torch.equal(dec_a.block_scores.view(torch.int32), dec_b.block_scores.view(torch.int32))
 
 
-@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8"])
+@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8", "union_r4", "union_r2"])
 def test_select_decode_equals_separate_calls(M, oracle, case):
     """msa_select_decode: same selection as msa_block_maxpool_topk and bitwise the same
     output as msa_sparse_decode on that selection."""
