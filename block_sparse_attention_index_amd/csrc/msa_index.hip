@@ -117,6 +117,92 @@ __device__ __forceinline__ void score_page(const PageRegs& pr, const v8i (&A)[R]
   }
 }
 
+// FP16 form for several rows (R >= 3): the page's keys are converted exactly
+// to FP16 (E2M1 code x E4M3 group scale has at most 6 significant bits) and
+// S^T = K Q^T runs on v_mfma_f32_16x16x32_f16 with 16 index queries per tile
+// (query 4r + g = column of the tile), instead of two masked FP4 products per
+// row.  The contraction dims are taken in the order the page registers hold
+// them: in k-step ks, lane group a carries dims 32a + 8ks .. 32a + 8ks + 7 of
+// both operands.  Output lane (n, a) holds tokens 4a .. 4a+3 of the chunk for
+// query n; the block max is a running max over the chunks, then a reduction
+// over the four lane groups.  Writes the block scores (and token scores) of
+// page j itself.
+template <int R>
+constexpr int f16_tiles() { return (R * kGroups + 15) / 16; }
+
+template <int R>
+__device__ __forceinline__ void load_queries_f16(const uint8_t* __restrict__ q_idx, int b, int lane,
+                                                 h8 (&Q)[f16_tiles<R>()][4]) {
+  const int n = lane & 15, a = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < f16_tiles<R>(); ++qt) {
+    const int qi = 16 * qt + n;  // (row qi / 4, group qi % 4)
+    const bool ok = qi < R * kGroups;
+    const uint8_t* q = q_idx + ((int64_t)b * R * kGroups + (ok ? qi : 0)) * kDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint2 w = *reinterpret_cast<const uint2*>(q + 32 * a + 8 * ks);
+      w = ok ? w : make_uint2(0, 0);
+      const h2 x0 = e4m3x2_to_h2<false>(w.x), x1 = e4m3x2_to_h2<true>(w.x);
+      const h2 x2 = e4m3x2_to_h2<false>(w.y), x3 = e4m3x2_to_h2<true>(w.y);
+      Q[qt][ks] = h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+    }
+  }
+}
+
+template <int R, bool kTok>
+__device__ __forceinline__ void score_page_f16(const PageRegs& pr, const h8 (&Q)[f16_tiles<R>()][4], int L, int j,
+                                               int b, int lane, int max_pages, float out_scale, int64_t T,
+                                               float* __restrict__ block_scores, float* __restrict__ token_scores) {
+  constexpr int QT = f16_tiles<R>();
+  const int n = lane & 15, a = lane >> 4;
+  float mx[QT];
+  int plim[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    mx[qt] = -__builtin_inff();
+    plim[qt] = L - R + (16 * qt + n) / kGroups;  // last visible position of this column's row
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // this lane's dims 32a .. 32a+31 are scale groups 2a and 2a+1 of its token
+    const h2 sc = e4m3x2_to_h2<false>(a < 2 ? pr.sw[c].x >> (16 * a) : pr.sw[c].y >> (16 * (a - 2)));
+    const uint32_t w[4] = {pr.cw[c].x, pr.cw[c].y, pr.cw[c].z, pr.cw[c].w};
+    h8 kv[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const _Float16 s1 = ks < 2 ? sc[0] : sc[1];
+      kv[ks] = e2m1x8_to_h8(w[ks]) * h8{s1, s1, s1, s1, s1, s1, s1, s1};
+    }
+    const int t0 = j * kPage + 16 * c + 4 * a;  // token of this lane's first output row
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[ks], Q[qt][ks], acc, 0, 0, 0);
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = t0 + i <= plim[qt];
+        v[i] = vis ? acc[i] : -__builtin_inff();
+        if (vis) mx[qt] = fmaxf(mx[qt], acc[i]);
+      }
+      const int qi = 16 * qt + n;
+      if (kTok && qi < R * kGroups)
+        *reinterpret_cast<float4*>(&token_scores[((int64_t)b * R * kGroups + qi) * T + t0]) =
+            make_float4(v[0] * out_scale, v[1] * out_scale, v[2] * out_scale, v[3] * out_scale);
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float m = mx[qt];
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const int qi = 16 * qt + n;
+    if (a == 0 && qi < R * kGroups) block_scores[((int64_t)b * R * kGroups + qi) * max_pages + j] = m * out_scale;
+  }
+}
+
 // The step's new tokens, for the insert fused into the index launch: rows of
 // positions L_b - R .. L_b - 1 of every request ([B][R][4][128] keys and
 // values, [B][R][128] index keys, FP32), written into the NVFP4 caches (keys
@@ -149,7 +235,7 @@ struct NewRows {
 // 16-element group, as the insert kernel does) and makes them visible to its
 // own waves before any page is read.
 template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1, bool INSERT = false,
-          bool WIDE = false>
+          bool WIDE = false, bool F16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_nvfp4_kernel(const int32_t* __restrict__ table,
                                                           const int32_t* __restrict__ lens, int32_t max_pages,
                                                           const uint8_t* __restrict__ q_idx, float out_scale,
@@ -212,9 +298,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (my_phys >= num_pages) my_phys = -1;
   }
 
-  // A operands: queries of row r masked to one scale group per MFMA row.
-  v8i A[R][2];
-  {
+  // A operands: queries of row r masked to one scale group per MFMA row
+  // (FP16 form: 16 index queries per tile instead).
+  v8i A[F16 ? 1 : R][2];
+  h8 Qh[F16 ? f16_tiles<R>() : 1][4];
+  if constexpr (F16) load_queries_f16<R>(q_idx, b, lane, Qh);
+  if constexpr (!F16) {
     const int i = lane & 15;
     const int gq = i >> 2, jj = i & 3;
     const bool on = (jj == grp);
@@ -268,9 +357,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (PREFETCH && phys_next >= 0 && j + 1 < j1)
       load_page<NT>(buf[(k + 1) & 1], pages + (int64_t)phys_next * kNvSlab, col, grp);
     if (phys_cur >= 0) {
-      float m[R];
-      score_page<R, kTok>(cur, A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
-      finish(j, m);
+      if constexpr (F16) {
+        score_page_f16<R, kTok>(cur, Qh, L, j, b, lane, max_pages, out_scale, T, block_scores, token_scores);
+      } else {
+        float m[R];
+        score_page<R, kTok>(cur, A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
+        finish(j, m);
+      }
     } else {
       empty_page(j);
     }
@@ -480,7 +573,7 @@ __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restric
     block_scores[((int64_t)b * R * kGroups + rg) * max_pages + j] = fmaxf(red[0][rg], red[1][rg]);
 }
 
-template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT, bool WIDE>
+template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT, bool WIDE, bool F16 = false>
 static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                              float* ts, const NewRows& nr, hipStream_t s) {
   const int p0 = ic->dtype == MSA_NVFP4 ? bt->shared_prefix_pages : 0;
@@ -488,11 +581,11 @@ static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_sc
   if (chunks <= 0) return;  // every page is shared: the prefix kernel scored them all
   const dim3 grid((unsigned)(chunks * bt->num_reqs));
   if (ts)
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT, WIDE>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
                        (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
   else
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
                        (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
 }
@@ -503,11 +596,15 @@ static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_sc
 // lane instead of eight 8-byte ones ~4.5%; many short waves balance the
 // ragged contexts better than a deeper per-wave pipeline, and 4-6 waves per
 // SIMD are equal while 8 thrash).
+// Three rows or more: the FP16 form (the masked FP4 products grow with R and
+// bound the scan from R = 3 on).
 template <int R, bool INSERT>
 static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                          float* ts, const NewRows& nr, hipStream_t s) {
-  launch_nvfp4_cfg<R, 1, false, true, (R <= 2 ? 4 : (R <= 4 ? 3 : 2)), INSERT, true>(bt, q, out_scale, ic, bs, ts, nr,
-                                                                                    s);
+  if constexpr (R <= 2)
+    launch_nvfp4_cfg<R, 1, false, true, 4, INSERT, true>(bt, q, out_scale, ic, bs, ts, nr, s);
+  else
+    launch_nvfp4_cfg<R, 1, false, true, 4, INSERT, true, true>(bt, q, out_scale, ic, bs, ts, nr, s);
 }
 
 template <bool INSERT>
