@@ -260,23 +260,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (t0 < t1) {
       const int i = threadIdx.x & 15;
       const int nrow = (t1 - t0) * 72;  // 16-dim groups: 32 keys, 32 values, 8 index keys per token
-      for (int rr = threadIdx.x >> 4; rr < nrow; rr += 16) {
-        const int tok = t0 + rr / 72;
+      // row rr: token t0 + rr / 72, then 32 key, 32 value and 8 index-key groups
+      auto locate = [&](int rr, int& tok, int& c, int& head, int& grp) {
+        tok = t0 + rr / 72;
         int u = rr % 72;
-        const int c = u < 32 ? 0 : (u < 64 ? 1 : 2);
+        c = u < 32 ? 0 : (u < 64 ? 1 : 2);
         u -= 32 * c;
-        const int heads = c == 2 ? 1 : kGroups;
-        const int head = u >> 3, grp = u & 7;
-        const int r = tok - (L - R);
-        const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
-        const float x = src[(((int64_t)b * R + r) * heads + head) * kDim + grp * 16 + i];
-        const int ph = table[(int64_t)b * max_pages + tok / kPage];
-        const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
-        uint8_t* base = c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages);
-        uint32_t code;
-        const uint32_t sc = nvfp4_row_quantize(x, c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i), code);
-        nvfp4_row_store(base + ((int64_t)(valid ? ph : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i,
-                        code, sc, c == 1, valid);
+        head = u >> 3;
+        grp = u & 7;
+      };
+      // a batch of rows per 16-lane row of threads: every source load issues
+      // before the first store (which could alias them) -- one memory round
+      constexpr int kBatch = 5;
+      for (int rb = threadIdx.x >> 4; rb < nrow; rb += 16 * kBatch) {
+        float x[kBatch];
+        int ph[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          int tok, c, head, grp;
+          locate(min(rb + 16 * k, nrow - 1), tok, c, head, grp);
+          const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
+          x[k] = src[(((int64_t)b * R + tok - (L - R)) * (c == 2 ? 1 : kGroups) + head) * kDim + grp * 16 + i];
+          ph[k] = table[(int64_t)b * max_pages + tok / kPage];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          if (rb + 16 * k >= nrow) break;  // uniform over the 16-lane row
+          int tok, c, head, grp;
+          locate(rb + 16 * k, tok, c, head, grp);
+          const int heads = c == 2 ? 1 : kGroups;
+          const bool valid = ph[k] >= 0 && ph[k] < (c == 2 ? num_pages : NR.kv_num_pages);
+          uint8_t* base = c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages);
+          uint32_t code;
+          const uint32_t sc = nvfp4_row_quantize(x[k], c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i), code);
+          nvfp4_row_store(base + ((int64_t)(valid ? ph[k] : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i,
+                          code, sc, c == 1, valid);
+        }
       }
       // the index keys just written are read back by this workgroup's waves
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
