@@ -8,7 +8,8 @@ on the device.
 
 A step is one pass of the whole path over the batch: insert of the B*R new
 tokens (NVFP4 quantisation into the pages), indexer score + block max-pool,
-top-16 selection with the latest block kept, sparse attention + split merge.
+top-16 selection with the latest block kept, sparse attention (each
+workgroup's waves merge their softmax states on chip).
 Inputs sit in HBM before timing starts; the caches rotate over replicas so
 that consecutive steps cannot serve the index scan from the 256 MB Infinity
 Cache.
@@ -227,8 +228,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the context-parallel indexer design is documented, not built).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the context-parallel indexer is a design, not code).", file=sys.stderr)
         sys.exit(2)
 
     st = setup(args.seed, args.replicas, args.config, args.kv)
