@@ -297,7 +297,7 @@ def test_shared_prefix_equals_private_copies(oracle):
 def test_index_scan_is_one_eighth_of_dense_kv_bytes():
     facts = {r[0]: int(r[1]) for r in read_golden("page_facts.txt")}
     assert facts["index_bytes_per_token_fp8"] * 8 == facts["dense_kv_bytes_per_token_fp8"]
-    # NVFP4 (this build's cache): 72 B index per token vs 576 B of K+V (4 heads x 128 x 2 x 0.5625)
+    # NVFP4 caches: 72 B index per token vs 576 B of K+V (4 heads x 128 x 2 x 0.5625)
     nv_index = 128 * 0.5625
     nv_kv = facts["kv_heads"] * facts["head_dim"] * 2 * 0.5625
     assert nv_index * 8 == nv_kv
