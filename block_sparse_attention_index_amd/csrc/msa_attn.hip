@@ -733,17 +733,14 @@ extern "C" size_t msa_decode_partials_bytes(const msa_batch* bt, int32_t topk) {
   return q * (kDim + 2) * sizeof(float);
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (the runtime answers from its cached
+// device properties; 256, the MI355X's count, if it cannot).
 static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 // NVFP4 and FP8 route: one launch, selection fused in when block_scores != NULL.
