@@ -157,18 +157,29 @@ __device__ __forceinline__ constexpr int tile_token(int m, int i) {
   return 32 * (i >> 2) + 8 * (m >> 1) + 4 * (m & 1) + (i & 3);
 }
 
+// K/V loads: with the streaming hint where each selected block is read once
+// (decode); NT = false where other rows read the same block again soon
+// (prefill chunks), so that the caches may keep it.
+template <bool NT>
+__device__ __forceinline__ uint4 kv_load4(const uint8_t* p) {
+  if constexpr (NT) return nt_load4(p);
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <bool NT = true>
 __device__ __forceinline__ void load_k(const uint8_t* __restrict__ ks_, int lane, KRegs& r) {
   const int n = lane & 15, a = lane >> 4;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) r.kc[m] = nt_load4(ks_ + tile_token(m, n) * 64 + 16 * a);
-  r.ksc = nt_load4(ks_ + kScaleOff + 16 * lane);
+  for (int m = 0; m < 8; ++m) r.kc[m] = kv_load4<NT>(ks_ + tile_token(m, n) * 64 + 16 * a);
+  r.ksc = kv_load4<NT>(ks_ + kScaleOff + 16 * lane);
 }
 
+template <bool NT = true>
 __device__ __forceinline__ void load_v(const uint8_t* __restrict__ vs_, int lane, VRegs& r) {
   const int n = lane & 15, a = lane >> 4;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) r.vw[nt] = nt_load4(vs_ + (16 * nt + n) * 64 + 16 * a);
-  r.vsc = nt_load4(vs_ + kScaleOff + 16 * lane);
+  for (int nt = 0; nt < 8; ++nt) r.vw[nt] = kv_load4<NT>(vs_ + (16 * nt + n) * 64 + 16 * a);
+  r.vsc = kv_load4<NT>(vs_ + kScaleOff + 16 * lane);
 }
 
 // FP8 caches: a lane's 32 bytes per M-tile (keys) or per 16-dim tile
@@ -181,21 +192,23 @@ struct VRegs8 {
   uint4 vw[8][2];  // V bytes of dim 16nt + n: tokens 32a .. 32a+15, 32a+16 .. 32a+31
 };
 
+template <bool NT = true>
 __device__ __forceinline__ void load_k(const uint8_t* __restrict__ ks_, int lane, KRegs8& r) {
   const int n = lane & 15, a = lane >> 4;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    r.kc[m][0] = nt_load4(ks_ + tile_token(m, n) * kDim + 32 * a);
-    r.kc[m][1] = nt_load4(ks_ + tile_token(m, n) * kDim + 32 * a + 16);
+    r.kc[m][0] = kv_load4<NT>(ks_ + tile_token(m, n) * kDim + 32 * a);
+    r.kc[m][1] = kv_load4<NT>(ks_ + tile_token(m, n) * kDim + 32 * a + 16);
   }
 }
 
+template <bool NT = true>
 __device__ __forceinline__ void load_v(const uint8_t* __restrict__ vs_, int lane, VRegs8& r) {
   const int n = lane & 15, a = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    r.vw[nt][0] = nt_load4(vs_ + (16 * nt + n) * kPage + 32 * a);
-    r.vw[nt][1] = nt_load4(vs_ + (16 * nt + n) * kPage + 32 * a + 16);
+    r.vw[nt][0] = kv_load4<NT>(vs_ + (16 * nt + n) * kPage + 32 * a);
+    r.vw[nt][1] = kv_load4<NT>(vs_ + (16 * nt + n) * kPage + 32 * a + 16);
   }
 }
 
@@ -497,12 +510,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
       if (ph < 0) continue;
       std::conditional_t<FP8, KRegs8, KRegs> K;
       std::conditional_t<FP8, VRegs8, VRegs> V;
-      load_k(kslab(ph), lane, K);
+      load_k<false>(kslab(ph), lane, K);
       int lim[QT];
       const bool part = block_lim(s_union[u], lim);
       // NVFP4 values load during the softmax; FP8 values (twice the
       // registers) once the scores are consumed
-      auto ld_v = [&] { load_v(vslab(ph), lane, V); };
+      auto ld_v = [&] { load_v<false>(vslab(ph), lane, V); };
       if constexpr (FP8)
         attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, NoOp{}, ld_v);
       else
