@@ -94,7 +94,7 @@ int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, 
   int st;
   if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
   if ((st = check_cache(idx_cache, INDEX)) != MSA_OK) return st;
-  if (batch->rows_per_req > MSA_MAX_ROWS && idx_cache->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (batch->rows_per_req > MSA_MAX_ROWS && idx_cache->dtype == MSA_F32) return MSA_ERR_UNSUPPORTED;
   if (!q_idx || !block_scores) return MSA_ERR_INVALID_ARG;
   if ((st = query_dtype_ok(q_dtype, idx_cache)) != MSA_OK) return st;
   if (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;

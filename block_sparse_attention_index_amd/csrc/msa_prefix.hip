@@ -31,6 +31,7 @@
 // column n: the block max is kept per lane over the eight M-tiles and
 // finished across the four lane groups.
 #include <climits>
+#include <type_traits>
 
 #include "msa_device.h"
 #include "msa_kernels.h"
@@ -88,6 +89,40 @@ __device__ __forceinline__ void store_prefix_part(const PrefixPart& p, int wave,
       const uint32_t w = ks == 0 ? p.kc[h].x : ks == 1 ? p.kc[h].y : ks == 2 ? p.kc[h].z : p.kc[h].w;
       const _Float16 s = ks < 2 ? sc[0] : sc[1];
       img[(m * 4 + ks) * 64 + lane] = e2m1x8_to_h8(w) * h8{s, s, s, s, s, s, s, s};
+    }
+  }
+}
+
+// FP8 index cache (E4M3 per element, half-rows slab: [t/16][d/64][t%16][d%64]):
+// the same part of a page, token 16m + n, dims 32a .. 32a+31 -- 32 bytes at
+// one place of the slab; E4M3 is exact in FP16 and the tensor scale is
+// applied to the FP32 result, as for NVFP4.
+struct PrefixPart8 {
+  uint4 kc[2][2];
+};
+
+__device__ __forceinline__ void load_prefix_part(const uint8_t* __restrict__ slab, int wave, int n, int a,
+                                                 PrefixPart8& p) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int m = wave + 4 * h;
+    const uint8_t* src = slab + m * 2048 + (a >> 1) * 1024 + n * 64 + (a & 1) * 32;
+    p.kc[h][0] = nt_load4(src);
+    p.kc[h][1] = nt_load4(src + 16);
+  }
+}
+
+__device__ __forceinline__ void store_prefix_part(const PrefixPart8& p, int wave, int lane, h8* __restrict__ img) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int m = wave + 4 * h;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4& q = p.kc[h][ks >> 1];
+      const uint32_t lo = (ks & 1) ? q.z : q.x, hi = (ks & 1) ? q.w : q.y;
+      const h2 x0 = e4m3x2_to_h2<false>(lo), x1 = e4m3x2_to_h2<true>(lo);
+      const h2 x2 = e4m3x2_to_h2<false>(hi), x3 = e4m3x2_to_h2<true>(hi);
+      img[(m * 4 + ks) * 64 + lane] = h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
     }
   }
 }
@@ -169,7 +204,7 @@ __device__ __forceinline__ void score_prefix_page(const h8* __restrict__ img, co
 // below n_valid have a table entry; the rest score -inf), for query columns
 // col_lo + 64*NTILE*yt .. (below col_hi).  Column c = (b*R + r)*4 + g is
 // index query (b, r, g); its last visible token is pos = L_b - R + r.
-template <int NTILE, int PPW, bool kTok>
+template <int NTILE, int PPW, bool kTok, bool FP8 = false>
 __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ trow, const int32_t* __restrict__ lens,
                                                  int32_t max_pages, int32_t R, int32_t n_pages, int32_t n_valid,
                                                  int32_t col_lo, int32_t col_hi, int pg, int yt,
@@ -216,13 +251,14 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
   // Register ring of page parts: the load of page k+2 is issued before page k
   // is multiplied, and page k+1 is dequantised into the other LDS image after
   // it, so every load has two pages of matrix work to land.
-  PrefixPart part[2];
+  constexpr int kSlab = FP8 ? kFp8Slab : kNvSlab;
+  std::conditional_t<FP8, PrefixPart8, PrefixPart> part[2];
   int phys[PPW];
 #pragma unroll
   for (int k = 0; k < PPW; ++k) phys[k] = k < jn ? phys_of(k) : -1;
 #pragma unroll
   for (int k = 0; k < 2 && k < PPW; ++k)
-    if (phys[k] >= 0) load_prefix_part(pages + (int64_t)phys[k] * kNvSlab, wave, n, a, part[k]);
+    if (phys[k] >= 0) load_prefix_part(pages + (int64_t)phys[k] * kSlab, wave, n, a, part[k]);
   if (phys[0] >= 0) store_prefix_part(part[0], wave, lane, s_img[0]);
   __syncthreads();
 #pragma unroll
@@ -230,7 +266,7 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
     if (k >= jn) break;
     const int j = j0 + k;
     if (k + 2 < PPW && phys[k + 2] >= 0)  // slot k%2 held page k, already in LDS
-      load_prefix_part(pages + (int64_t)phys[k + 2] * kNvSlab, wave, n, a, part[k & 1]);
+      load_prefix_part(pages + (int64_t)phys[k + 2] * kSlab, wave, n, a, part[k & 1]);
     if (has_cols) {
       float mx[NTILE];
       if (phys[k] >= 0) {
@@ -292,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // Prefill (many query rows per request): request b = blockIdx.y, all its
 // pages (those past its context score -inf) against its R*4 index queries;
 // the rows' causal limits mask the chunk's own pages per column.
-template <int NTILE, int PPW, bool kTok>
+template <int NTILE, int PPW, bool kTok, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_index_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t R,
     const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
@@ -301,7 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int id = (int)blockIdx.x, b = (int)blockIdx.y;
   const int L = clamp_len(lens[b], max_pages);
   const int ncols = R * kGroups;
-  dense_index_body<NTILE, PPW, kTok>(table + (int64_t)b * max_pages, lens, max_pages, R, max_pages,
+  dense_index_body<NTILE, PPW, kTok, FP8>(table + (int64_t)b * max_pages, lens, max_pages, R, max_pages,
                                      (L + kPage - 1) / kPage, b * ncols, (b + 1) * ncols,
                                      (id / (8 * ny)) * 8 + (id & 7), (id >> 3) % ny, q_idx, out_scale, pages,
                                      num_pages, block_scores, token_scores, s_img);
@@ -334,14 +370,17 @@ static int launch_prefill_cfg(const msa_batch* bt, const uint8_t* q, float out_s
   const int npg = (bt->max_pages_per_req + PPW - 1) / PPW;
   const int npg8 = (npg + 7) / 8 * 8;
   const dim3 grid((unsigned)(npg8 * ny), (unsigned)bt->num_reqs);
-  if (ts)
-    hipLaunchKernelGGL((prefill_index_kernel<NTILE, PPW, true>), grid, dim3(256), 0, s, bt->block_table,
-                       bt->ctx_lens, bt->max_pages_per_req, bt->rows_per_req, q, out_scale, (const uint8_t*)ic->pages,
-                       ic->num_pages, bs, ts, ny);
-  else
-    hipLaunchKernelGGL((prefill_index_kernel<NTILE, PPW, false>), grid, dim3(256), 0, s, bt->block_table,
-                       bt->ctx_lens, bt->max_pages_per_req, bt->rows_per_req, q, out_scale, (const uint8_t*)ic->pages,
-                       ic->num_pages, bs, ts, ny);
+#define MSA_PREFILL_INDEX(TOK, FP8)                                                                             \
+  hipLaunchKernelGGL((prefill_index_kernel<NTILE, PPW, TOK, FP8>), grid, dim3(256), 0, s, bt->block_table,      \
+                     bt->ctx_lens, bt->max_pages_per_req, bt->rows_per_req, q, out_scale, (const uint8_t*)ic->pages, \
+                     ic->num_pages, bs, ts, ny)
+  const bool fp8 = ic->dtype == MSA_FP8_E4M3;
+  if (ts) {
+    if (fp8) MSA_PREFILL_INDEX(true, true); else MSA_PREFILL_INDEX(true, false);
+  } else {
+    if (fp8) MSA_PREFILL_INDEX(false, true); else MSA_PREFILL_INDEX(false, false);
+  }
+#undef MSA_PREFILL_INDEX
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -168,10 +168,11 @@ int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipS
  * q_idx: [B][R][4][128], FP8 E4M3 bytes (times q_scale) with an NVFP4 index
  * cache, or FP32 with an F32 cache.  token_scores (may be NULL; a test aid):
  * [B][R][4][max_pages*128] per-token scores, -inf for invisible tokens.
- * Prefill: with an NVFP4 index cache R may be up to MSA_MAX_PREFILL_ROWS (the
- * rows of a prompt chunk at positions L_b - R .. L_b - 1); every page of a
- * request is then scored for all its R*4 index queries as one dense
- * matrix-core product (the pages' indexer prefill, vLLM post, "MSA 预填充").
+ * Prefill: with an NVFP4 or FP8 index cache R may be up to
+ * MSA_MAX_PREFILL_ROWS (the rows of a prompt chunk at positions L_b - R ..
+ * L_b - 1); every page of a request is then scored for all its R*4 index
+ * queries as one dense matrix-core product (the pages' indexer prefill, vLLM
+ * post, "MSA 预填充").
  */
 int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, float q_scale,
                     const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream);

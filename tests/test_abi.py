@@ -65,13 +65,13 @@ def test_host_validation_without_gpu(lib):
     # too many rows (beyond a prefill chunk), bad tensor scale, FP32 queries against an NVFP4 cache
     bad_rows = Batch(2, 8193, 8, 0, fake, fake)
     assert lib.msa_index_score(C.byref(bad_rows), fake, 1, C.c_float(1.0), C.byref(idx), fake, None, None) == -1
-    # more than 8 rows: refused by the decode-only fused insert + index, and for FP8 / F32 index caches
+    # more than 8 rows: refused by the decode-only fused insert + index, and for F32 index caches
     rows9 = Batch(2, 9, 8, 0, fake, fake)
     k9, v9 = Cache(2, 0, 4, 16, 0.01, fake), Cache(2, 1, 4, 16, 0.01, fake)
     assert lib.msa_insert_index_score(C.byref(rows9), fake, fake, fake, fake, 1, C.c_float(1.0), C.byref(k9),
                                       C.byref(v9), C.byref(idx), fake, None, None) == -1
-    i8 = Cache(1, 2, 1, 16, 0.02, fake)
-    assert lib.msa_index_score(C.byref(rows9), fake, 1, C.c_float(1.0), C.byref(i8), fake, None, None) == -2
+    i32 = Cache(0, 0, 1, 16, 1.0, fake)
+    assert lib.msa_index_score(C.byref(rows9), fake, 0, C.c_float(1.0), C.byref(i32), fake, None, None) == -2
     f32k9, f32v9 = Cache(0, 0, 4, 16, 1.0, fake), Cache(0, 0, 4, 16, 1.0, fake)
     assert lib.msa_sparse_decode(C.byref(rows9), fake, 0, C.c_float(1.0), C.c_float(0.088), C.byref(f32k9),
                                  C.byref(f32v9), fake, fake, 16, fake, fake, C.c_size_t(1 << 40), None) == -2

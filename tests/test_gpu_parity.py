@@ -122,8 +122,9 @@ CASES = {
     "fp8_ragged_r4": lambda: W.make_workload(4, seed=13, lengths=[0, 2, 3, 4, 131, 2051, 2052, 7000], R=4,
                                              cache="fp8"),
     "fp8_r8": lambda: W.make_workload(4, seed=14, B=2, len_div=64, R=8, cache="fp8"),
-    # a prefill chunk in FP8 caches (attention only: FP8 prefill indexing is not offered)
+    # prefill chunks in FP8 caches
     "fp8_prefill": lambda: W.make_workload(6, seed=17, lengths=[3000, 1000, 130], R=300, cache="fp8"),
+    "fp8_prefill_r512": lambda: W.make_workload(6, seed=20, lengths=[8192], R=512, cache="fp8"),
     "r8": lambda: W.make_workload(4, seed=8, B=2, len_div=64, R=8),
     # batches whose B*R*4 workgroup rows exceed the 256 CUs: attention walks row-group unions
     # (two query tiles for R=4, one for R=2) instead of one workgroup per row
@@ -274,7 +275,8 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 # ---------------------------------------------------------------- steps 1+2
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
-                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged"])
+                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
+                                  "fp8_prefill", "fp8_prefill_r512"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -461,7 +463,7 @@ def _sampled_caches(oracle, wl, rows):
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
-                                  "union_r4", "union_r2"])
+                                  "union_r4", "union_r2", "fp8_prefill", "fp8_prefill_r512"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
