@@ -631,6 +631,49 @@ def test_full_size_config5_sampled(M, oracle):
 
 
 
+def test_full_size_config6_sampled(M, oracle):
+    """The prefill workload at full size (4 prompts of 64K tokens, the last 2,048 of each a
+    chunk of causal rows), the step inserting the chunk's rows, in the bench's launch
+    configuration.  The oracle checks 12 sampled rows of one request, each as a one-row
+    request of its own: context p + 1 for the row at position p (it sees tokens 0..p, as in
+    the chunk), the same block-table row and caches."""
+    wl = W.make_workload(6, seed=0)
+    _print_case("config 6 full size", wl)
+    dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True)
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = dec.sel.cpu().numpy(), dec.cnt.cpu().numpy()
+    g_out = dec.out.cpu().numpy().astype(np.float64)
+    g_bs = dec.block_scores.cpu().numpy().astype(np.float64)
+    b = 1
+    rows = np.array([0, 1, 127, 128, 500, 1023, 1024, 1500, 1919, 1920, 2046, 2047])
+    ci, ck, cv = _sampled_caches(oracle, wl, np.array([b]))
+    _, _, qi, qd = oracle_queries(oracle, wl)
+    p = int(wl.lengths[b]) - wl.R + rows  # positions of the sampled rows
+    n = rows.size
+    table = np.repeat(wl.block_table[b:b + 1], n, axis=0)
+    bt = oracle.OracleBatch(table, (p + 1).astype(np.int32), 1)
+    qi_s, qd_s = qi[b, rows][:, None], qd[b, rows][:, None]  # [n][1][4][128], [n][1][32][128]
+    res = oracle.decode_step(bt, qi_s, qd_s, wl.sm_scale, ci, ck, cv, wl.topk)
+    ts, ab = oracle.index_scores(bt, qi_s, ci, with_abs=True)
+    absmax = ab.reshape(ab.shape[:3] + (wl.max_pages, 128)).max(-1)
+    ref_bs, got_bs = res["block_scores"][:, 0], g_bs[b, rows]
+    fin = np.isfinite(ref_bs)
+    assert np.array_equal(np.isfinite(got_bs), fin)
+    assert (np.abs(got_bs[fin] - ref_bs[fin]) <= SCORE_TOL * absmax[:, 0][fin] + 1e-30).all()
+    mism = 0
+    for i in range(n):
+        for g in range(4):
+            ok, _ = selection_guard_ok(res["block_scores"][i, 0, g], res["sel"][i, 0, g], res["cnt"][i, 0, g],
+                                       g_sel[b, rows[i], g], g_cnt[b, rows[i], g], p[i], wl.topk)
+            mism += not ok
+    assert mism == 0
+    ref_own = oracle.attention(bt, qd_s, wl.sm_scale, ck, cv, g_sel[b, rows][:, None], g_cnt[b, rows][:, None])
+    err = _out_err(g_out[b, rows][:, None], ref_own)
+    print(f"  {n} rows: max per-vector relative error {err.max():.3e}", flush=True)
+    assert err.max() <= OUT_TOL
+
+
 def test_abi_errors_on_device(M):
     print("[case] abi errors", flush=True)
     wl = CASES["cfg2_small"]()
