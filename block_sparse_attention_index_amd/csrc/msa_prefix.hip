@@ -49,12 +49,19 @@ __device__ __forceinline__ void load_prefix_queries(const uint8_t* __restrict__ 
     const int c = col0 + 16 * nt + n;
     const bool ok = c < ncols;
     const uint8_t* q = q_idx + (int64_t)(ok ? c : 0) * kDim;
+    // the lane's 32 bytes in two 16-byte loads (every workgroup reads the same
+    // queries at its start: fewer, wider requests)
+    uint4 w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w[h] = *reinterpret_cast<const uint4*>(q + 32 * a + 16 * h);
+      w[h] = ok ? w[h] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint2 w = *reinterpret_cast<const uint2*>(q + 32 * a + 8 * ks);
-      w = ok ? w : make_uint2(0, 0);
-      const h2 x0 = e4m3x2_to_h2<false>(w.x), x1 = e4m3x2_to_h2<true>(w.x);
-      const h2 x2 = e4m3x2_to_h2<false>(w.y), x3 = e4m3x2_to_h2<true>(w.y);
+      const uint32_t lo = (ks & 1) ? w[ks >> 1].z : w[ks >> 1].x, hi = (ks & 1) ? w[ks >> 1].w : w[ks >> 1].y;
+      const h2 x0 = e4m3x2_to_h2<false>(lo), x1 = e4m3x2_to_h2<true>(lo);
+      const h2 x2 = e4m3x2_to_h2<false>(hi), x3 = e4m3x2_to_h2<true>(hi);
       Q[nt][ks] = h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
     }
   }
@@ -223,6 +230,31 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
   const bool has_cols = col0 < ncols;  // wave-uniform; a wave without columns still dequantises
   const int64_t T = (int64_t)max_pages * kPage;
 
+  // Order of the start-up loads: the page table, then (once it has arrived)
+  // the first two pages, and only then the queries and context lengths, whose
+  // conversion waits on them -- so the page loads do not queue behind it.
+  int my_phys = -1;
+  if (lane < jn && j0 + lane < n_valid) {
+    my_phys = trow[j0 + lane];
+    if (my_phys < 0 || my_phys >= num_pages) my_phys = -1;
+  }
+  auto phys_of = [&](int k) { return __builtin_amdgcn_readfirstlane(__shfl(my_phys, k)); };
+
+  // Register ring of page parts: the load of page k+2 is issued before page k
+  // is multiplied, and page k+1 is dequantised into the other LDS image after
+  // it, so every load has two pages of matrix work to land.  Loads and
+  // dequantisation are unconditional (page 0 of the pool stands in for a
+  // missing page, whose image is then never read), so that each wait covers
+  // exactly the loads it needs.
+  constexpr int kSlab = FP8 ? kFp8Slab : kNvSlab;
+  std::conditional_t<FP8, PrefixPart8, PrefixPart> part[2];
+  int phys[PPW];
+#pragma unroll
+  for (int k = 0; k < PPW; ++k) phys[k] = k < jn ? phys_of(k) : -1;
+  auto slab_of = [&](int k) { return pages + (int64_t)max(phys[k], 0) * kSlab; };
+#pragma unroll
+  for (int k = 0; k < 2 && k < PPW; ++k) load_prefix_part(slab_of(k), wave, n, a, part[k]);
+
   h8 Q[NTILE][4];
   load_prefix_queries<NTILE>(q_idx, col0, ncols, n, a, Q);
   int pos[NTILE];
@@ -240,33 +272,14 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
   }
   const int pmin = INT_MAX - (int)wave_umax(pkey);
 
-  // physical pages of the workgroup, one per lane
-  int my_phys = -1;
-  if (lane < jn && j0 + lane < n_valid) {
-    my_phys = trow[j0 + lane];
-    if (my_phys < 0 || my_phys >= num_pages) my_phys = -1;
-  }
-  auto phys_of = [&](int k) { return __builtin_amdgcn_readfirstlane(__shfl(my_phys, k)); };
-
-  // Register ring of page parts: the load of page k+2 is issued before page k
-  // is multiplied, and page k+1 is dequantised into the other LDS image after
-  // it, so every load has two pages of matrix work to land.
-  constexpr int kSlab = FP8 ? kFp8Slab : kNvSlab;
-  std::conditional_t<FP8, PrefixPart8, PrefixPart> part[2];
-  int phys[PPW];
-#pragma unroll
-  for (int k = 0; k < PPW; ++k) phys[k] = k < jn ? phys_of(k) : -1;
-#pragma unroll
-  for (int k = 0; k < 2 && k < PPW; ++k)
-    if (phys[k] >= 0) load_prefix_part(pages + (int64_t)phys[k] * kSlab, wave, n, a, part[k]);
-  if (phys[0] >= 0) store_prefix_part(part[0], wave, lane, s_img[0]);
+  store_prefix_part(part[0], wave, lane, s_img[0]);
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < PPW; ++k) {
     if (k >= jn) break;
     const int j = j0 + k;
-    if (k + 2 < PPW && phys[k + 2] >= 0)  // slot k%2 held page k, already in LDS
-      load_prefix_part(pages + (int64_t)phys[k + 2] * kSlab, wave, n, a, part[k & 1]);
+    if (k + 2 < PPW)  // slot k%2 held page k, already in LDS
+      load_prefix_part(slab_of(k + 2), wave, n, a, part[k & 1]);
     if (has_cols) {
       float mx[NTILE];
       if (phys[k] >= 0) {
@@ -303,7 +316,7 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
       }
     }
     // page k+1 -> the other image (last read before the previous barrier)
-    if (k + 1 < PPW && phys[k + 1] >= 0) store_prefix_part(part[(k + 1) & 1], wave, lane, s_img[(k + 1) & 1]);
+    if (k + 1 < PPW) store_prefix_part(part[(k + 1) & 1], wave, lane, s_img[(k + 1) & 1]);
     __syncthreads();
   }
 }
