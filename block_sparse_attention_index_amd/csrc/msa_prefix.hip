@@ -257,14 +257,23 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
 
   h8 Q[NTILE][4];
   load_prefix_queries<NTILE>(q_idx, col0, ncols, n, a, Q);
+  // context lengths of the columns' requests: all loads first (unconditional,
+  // clamped), then one wait
+  int lb[NTILE];
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt) lb[nt] = lens[min(col0 + 16 * nt + n, ncols - 1) / (R * kGroups)];
+  // (keeps the compiler from sinking a load into the page loop, where its wait
+  // would also wait for the page loads issued there)
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt) asm volatile("" : : "v"(lb[nt]));
   int pos[NTILE];
   uint32_t pkey = 0;  // max of (INT_MAX - pos) over valid columns: the wave's smallest pos
 #pragma unroll
   for (int nt = 0; nt < NTILE; ++nt) {
     const int c = col0 + 16 * nt + n;
     if (c < ncols) {
-      const int b = c / (R * kGroups), r = (c / kGroups) % R;
-      pos[nt] = clamp_len(lens[b], max_pages) - R + r;
+      const int r = (c / kGroups) % R;
+      pos[nt] = clamp_len(lb[nt], max_pages) - R + r;
       pkey = max(pkey, (uint32_t)(INT_MAX - pos[nt]));
     } else {
       pos[nt] = -1;
