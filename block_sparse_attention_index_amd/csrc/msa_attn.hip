@@ -4,21 +4,21 @@
 // of a group attends to the group's selected blocks), alone or fused with
 // step 3 (the selection) in one launch.
 //
-// Work split (NVFP4): one workgroup of 8 waves (4 with two query tiles) per
-// (request, group, group of up to 4 rows).  The waves walk the union of the
-// rows' selected blocks, two 128-token blocks at a time with both blocks'
-// loads in flight, each wave keeping an online softmax (running max,
-// denominator, unnormalised output); the waves then merge through LDS and
-// the workgroup writes the normalised output -- no partial results leave the
-// chip and no second launch merges them.  With the selection fused in, waves
-// 0..nr-1 first run the top-k of one row each (msa_select.h) from the block
-// scores, while the block-table row and the queries load.  With one row per
-// request, the 8 heads of a group share each dequantised K/V element (GQA);
-// with 4 speculative rows the 32 query vectors of a group fill two 16-column
-// query tiles.  Prefill chunks (more than 8 rows) take one row per workgroup
-// of 4 waves, one block per wave at a time, three workgroups per CU: their
-// rows select independently, so a row group's union would only multiply the
-// work.
+// Work split (NVFP4 and FP8): one workgroup of 8 waves per (request, group,
+// row) while the batch's rows x groups fit the CUs; beyond that, one per
+// (request, group, group of up to 4 rows), the waves walking the union of the
+// rows' selected blocks (4 waves with two query tiles when R > 2).  The waves
+// take the blocks two at a time with both blocks' loads in flight, each
+// keeping an online softmax (running max, denominator, unnormalised output);
+// they then merge through LDS and the workgroup writes the normalised output
+// -- no partial results leave the chip and no second launch merges them.
+// With the selection fused in, waves 0..nr-1 first run the top-k of one row
+// each (msa_select.h) from the block scores, while the block-table row and
+// the queries load.  The 8 heads of a group share each dequantised K/V
+// element (GQA); 4 rows' 32 query vectors fill two 16-column query tiles.
+// Prefill chunks (more than 8 rows) take one row per workgroup of 4 waves,
+// one block per wave at a time, three workgroups per CU: their rows select
+// independently, so a row group's union would only multiply the work.
 //
 // Per block and wave:
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16.  K codes go through the exact
@@ -36,8 +36,9 @@
 //    more MFMA against a ones operand, so the denominator adds exactly the P
 //    that the numerator uses.  V codes are scaled per token by their E4M3
 //    group scale in FP16 (converted once per block into LDS).
-//  * K and V are read with non-temporal 16-byte loads (each selected block is
-//    read once per step).
+//  * K and V are read with 16-byte loads, non-temporal in decode (each
+//    selected block is read once per step), cacheable in prefill (the other
+//    rows of the chunk read the same blocks).
 #include <algorithm>
 #include <type_traits>
 
