@@ -106,6 +106,105 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(InsertArgs A, const int6
                   valid);
 }
 
+// The same NVFP4 insert with one lane per 16-element group, for large
+// batches (a prompt chunk): the group's amax and E4M3 scale are derived once
+// per group instead of once per element, so the vector work per element is
+// about a quarter.  Every step is the same FP32 operation on the same
+// values as nvfp4_row_quantize (the maximum of |x| over the group does not
+// depend on the order), so the bytes written are identical.  All three
+// caches NVFP4.
+__device__ __forceinline__ uint32_t nvfp4_group_quantize(const float (&x)[16], float ts, uint32_t (&code)[16]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(x[i]), 0.0f));
+  const float t1 = amax / 6.0f;
+  const float s32 = t1 / ts;
+  const uint32_t sc = e4m3_encode(s32);
+  const float sv = e4m3_to_f32(sc);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = 0;
+  if (sv != 0.0f) {
+    const float denom = sv * ts;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float y = x[i] / denom;
+      code[i] = e2m1_mag(fabsf(y)) | ((__float_as_uint(x[i]) >> 28) & 0x8u);
+    }
+  }
+  return sc;
+}
+
+__device__ __forceinline__ void load_group(const float* __restrict__ p, float (&x)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = reinterpret_cast<const float4*>(p)[q];
+    x[4 * q] = v.x, x[4 * q + 1] = v.y, x[4 * q + 2] = v.z, x[4 * q + 3] = v.w;
+  }
+}
+
+__global__ __launch_bounds__(256) void kv_insert_group_kernel(InsertArgs A, const int64_t* __restrict__ slots,
+                                                              int32_t n) {
+  const int32_t units = A.u0 + A.u1 + A.u2;
+  const int64_t gunit = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (token, group)
+  if (gunit >= (int64_t)n * units) return;
+  const int32_t tok = (int32_t)(gunit / units);
+  int32_t u = (int32_t)(gunit - (int64_t)tok * units);
+  const int c = u < A.u0 ? 0 : (u < A.u0 + A.u1 ? 1 : 2);
+  u -= c == 0 ? 0 : (c == 1 ? A.u0 : A.u0 + A.u1);
+  uint8_t* pages = c == 0 ? A.pages0 : (c == 1 ? A.pages1 : A.pages2);
+  const float* src = c == 0 ? A.src0 : (c == 1 ? A.src1 : A.src2);
+  const int32_t num_pages = c == 0 ? A.np0 : (c == 1 ? A.np1 : A.np2);
+  const int32_t heads = c == 0 ? A.h0 : (c == 1 ? A.h1 : A.h2);
+  const int32_t layout = c == 0 ? A.dm0 : (c == 1 ? A.dm1 : A.dm2);
+  const float ts = c == 0 ? A.ts0 : (c == 1 ? A.ts1 : A.ts2);
+  const int head = u >> 3, grp = u & 7;
+  const int64_t slot = slots[tok];
+  const bool valid = slot >= 0 && slot < (int64_t)num_pages * kPage;
+  if (!valid) return;
+  const int64_t page = slot >> 7;
+  const int off = (int)(slot & 127);
+  uint8_t* slab = pages + (page * heads + head) * (int64_t)kNvSlab;
+  float x[16];
+  load_group(src + ((int64_t)tok * heads + head) * kDim + grp * 16, x);
+  uint32_t code[16];
+  if (layout != MSA_DIM_MAJOR) {
+    const uint32_t sc = nvfp4_group_quantize(x, ts, code);
+    uint2 w = make_uint2(0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w.x |= code[i] << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w.y |= code[8 + i] << (4 * i);
+    *reinterpret_cast<uint2*>(slab + off * 64 + grp * 8) = w;
+    slab[kScaleOff + off * 8 + grp] = (uint8_t)sc;
+    return;
+  }
+  // dim-major values: as kv_insert_kernel, a token of an even slot followed in
+  // the batch by the next slot writes both tokens' nibbles as whole bytes
+  const int64_t nxt = tok + 1 < n ? slots[tok + 1] : -1;
+  const int64_t prv = tok > 0 ? slots[tok - 1] : -1;
+  if ((slot & 1) && prv == slot - 1) return;  // written by the previous token's lane
+  const uint32_t sc = nvfp4_group_quantize(x, ts, code);
+  if (!(slot & 1) && nxt == slot + 1) {
+    float x1[16];
+    load_group(src + ((int64_t)(tok + 1) * heads + head) * kDim + grp * 16, x1);
+    uint32_t code1[16];
+    const uint32_t sc1 = nvfp4_group_quantize(x1, ts, code1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) slab[(grp * 16 + i) * 64 + (off >> 1)] = (uint8_t)(code[i] | (code1[i] << 4));
+    slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
+    slab[kScaleOff + grp * 128 + off + 1] = (uint8_t)sc1;
+    return;
+  }
+  const unsigned int sh = 4u * (unsigned)(off & 7);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    unsigned int* word = reinterpret_cast<unsigned int*>(slab + (grp * 16 + i) * 64 + (off >> 3) * 4);
+    atomicAnd(word, ~(0xFu << sh));
+    atomicOr(word, code[i] << sh);
+  }
+  slab[kScaleOff + grp * 128 + off] = (uint8_t)sc;
+}
+
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* __restrict__ x, int64_t n, float scale,
                                                             uint8_t* __restrict__ out) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -194,10 +293,20 @@ extern "C" int msa_launch_kv_insert(const float* k, const float* v, const float*
   fill(kc, k, A.pages0, A.src0, A.np0, A.h0, A.nv0, A.dm0, A.ts0, A.u0);
   fill(vc, v, A.pages1, A.src1, A.np1, A.h1, A.nv1, A.dm1, A.ts1, A.u1);
   fill(ic, idx_k, A.pages2, A.src2, A.np2, A.h2, A.nv2, A.dm2, A.ts2, A.u2);
-  const int64_t total = (int64_t)n * (A.u0 + A.u1 + A.u2) * 16;  // one 16-lane row per (token, group)
-  if (total == 0) return 0;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(kv_insert_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A, slots, n);
+  const int64_t groups = (int64_t)n * (A.u0 + A.u1 + A.u2);
+  if (groups == 0) return 0;
+  // a prompt chunk with every cache NVFP4: one lane per group; otherwise (and
+  // for a decode step's few tokens, where a 16-lane row per group is faster)
+  // one 16-lane row per (token, group)
+  const bool nv = (!A.pages0 || A.nv0 == MSA_NVFP4) && (!A.pages1 || A.nv1 == MSA_NVFP4) &&
+                  (!A.pages2 || A.nv2 == MSA_NVFP4);
+  if (nv && n >= 512) {
+    hipLaunchKernelGGL(kv_insert_group_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, A,
+                       slots, n);
+  } else {
+    const int64_t total = groups * 16;
+    hipLaunchKernelGGL(kv_insert_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, A, slots, n);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -145,11 +145,13 @@ def test_insert_bytes_bitexact(M, oracle, case):
     assert np.array_equal(dec.v.pages.cpu().numpy(), cv.bytes)
 
 
-def test_insert_special_values_bitexact(M, oracle):
-    """Groups spanning subnormal scales, saturation, exact zeros, -0 and E2M1 ties."""
-    print("[case] insert special values", flush=True)
-    rng = np.random.default_rng(11)
-    n = 512
+@pytest.mark.parametrize("n,consecutive", [(300, False), (512, False), (1030, True)])
+def test_insert_special_values_bitexact(M, oracle, n, consecutive):
+    """Groups spanning subnormal scales, saturation, exact zeros, -0 and E2M1 ties.  Below 512
+    tokens the insert quantises on a 16-lane row per group, from 512 on with one lane per group;
+    consecutive slots (a prompt chunk) write value bytes of token pairs whole."""
+    print(f"[case] insert special values n={n} consecutive={consecutive}", flush=True)
+    rng = np.random.default_rng(11 + n)
     x = rng.standard_normal((n, 4, 128)).astype(np.float32)
     x *= (2.0 ** rng.integers(-24, 14, size=(n, 4, 8, 1))).repeat(16, -1).reshape(n, 4, 128).astype(np.float32)
     x[::7, :, :16] = 0.0
@@ -162,7 +164,8 @@ def test_insert_special_values_bitexact(M, oracle):
 
     npg = n // 128 + 1
     k, v, idx = make_caches(True, npg, ts)
-    slots = rng.permutation(npg * 128)[:n].astype(np.int64)
+    slots = (np.arange(n) + 3) if consecutive else rng.permutation(npg * 128)[:n]
+    slots = slots.astype(np.int64)
     M.msa_kv_insert(_dev(x), _dev(x), _dev(xi), _dev(slots), k, v, idx)
     torch.cuda.synchronize()
     ok = O.OracleCache(O.NVFP4, O.TOKEN_MAJOR, 4, npg, ts)
