@@ -76,6 +76,20 @@ __device__ __forceinline__ void stage_scales(PageRegs& pr, uint4* slot, int lane
   __builtin_amdgcn_wave_barrier();
 }
 
+// Inclusive prefix sum over the wave's 64 lanes: within each 16-lane row by
+// row shifts (a lane shifted in from outside the row reads 0), then the
+// totals of the rows before, read as scalars.
+__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  const int r = lane >> 4;
+  return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
+}
+
 // Scores of one resident page for all R rows; returns per-row maxima (unscaled).
 template <int R, bool kTok>
 __device__ __forceinline__ void score_page(const PageRegs& pr, const v8i (&A)[R][2], const int (&pos_lim)[R], int j,
@@ -230,12 +244,19 @@ struct NewRows {
 // B + b*(C-1) + i then takes chunk i of request b, skipping the newest one
 // (i >= latest_b -> chunk i + 1).  Each request's remaining chunks are
 // consecutive workgroups, which the dispatcher deals round-robin to the 8
-// XCDs, and the chunks past a context (nothing to score) close its run.  With INSERT the workgroup first writes
+// XCDs, and the chunks past a context (nothing to score) close its run.
+// COMPACT (B <= 64, block scores only): workgroups B.. are instead packed to
+// the chunks below each request's newest, in the same order, from a prefix
+// sum of all B lengths; the chunks past a context get no workgroup (their
+// -inf is written by the newest chunk's waves after their own pages), and the
+// leftover workgroups at the grid's end exit after the length load.  On a
+// ragged batch the scan no longer spends workgroup slots on empty chunks
+// between the real ones.  With INSERT the workgroup first writes
 // the new tokens that fall in its chunk into the caches (one 16-lane row per
 // 16-element group, as the insert kernel does) and makes them visible to its
 // own waves before any page is read.
 template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1, bool INSERT = false,
-          bool WIDE = false, bool F16 = false>
+          bool WIDE = false, bool F16 = false, bool COMPACT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_nvfp4_kernel(const int32_t* __restrict__ table,
                                                           const int32_t* __restrict__ lens, int32_t max_pages,
                                                           const uint8_t* __restrict__ q_idx, float out_scale,
@@ -245,14 +266,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                                           int32_t p0, NewRows NR) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int C = (max_pages - p0 + 4 * PPW - 1) / (4 * PPW);
   const int id = (int)blockIdx.x;
-  const int b = id < B ? id : (id - B) / max(C - 1, 1);
-  const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
-  const int L = clamp_len(lens[b], max_pages);
+  int b, L, latest, chunk;
+  if (COMPACT && id >= B) {
+    // B <= 64 and no per-token output: workgroups B.. take only the chunks
+    // below each request's newest one, packed request after request, and the
+    // workgroups left over at the end of the grid exit after one load.  Lane
+    // l holds request l's count of such chunks; every wave derives the same map.
+    int Ll = 0, nl = 0;
+    if (lane < B) {
+      Ll = clamp_len(lens[lane], max_pages);
+      const int np = (Ll + kPage - 1) / kPage;
+      nl = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
+    }
+    const int incl = wave_incl_sum(nl, lane);
+    const int k = id - B;
+    if (k >= __builtin_amdgcn_readlane(incl, 63)) return;
+    b = (int)__popcll(__ballot(incl <= k));  // requests whose chunks all lie before k
+    if (b >= B) return;                      // (never, with k below the total: keeps b in range)
+    chunk = k - __builtin_amdgcn_readlane(incl - nl, b);
+    L = __builtin_amdgcn_readlane(Ll, b);
+    latest = __builtin_amdgcn_readlane(nl, b);
+    if (chunk < 0 || chunk >= latest) return;
+  } else {
+    // the newest chunk of request id (id < B; also the packed form's), or
+    // chunk i_rest of (C - 1) per request, skipping the newest
+    const int C = (max_pages - p0 + 4 * PPW - 1) / (4 * PPW);
+    b = id < B ? id : (id - B) / max(C - 1, 1);
+    const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
+    L = clamp_len(lens[b], max_pages);
+    const int np = (L + kPage - 1) / kPage;
+    latest = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
+    chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
+  }
   const int npb = (L + kPage - 1) / kPage;
-  const int latest = npb > p0 ? (npb - 1 - p0) / (4 * PPW) : 0;
-  const int chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
   if (INSERT) {
     // new tokens [max(L - R, 0), L) that lie in this chunk's token range
     const int lo = (p0 + chunk * 4 * PPW) * kPage;
@@ -303,8 +350,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   }
+  // COMPACT: the chunks past the newest have no workgroup; the newest chunk's
+  // waves write their -inf block scores once their own pages are done
+  auto fill_past = [&] {
+    if (!COMPACT || id >= B) return;
+    const int jf = min(p0 + (latest + 1) * 4 * PPW, max_pages);
+    for (int rg = 0; rg < R * kGroups; ++rg) {
+      float* row = block_scores + ((int64_t)b * R * kGroups + rg) * max_pages;
+      for (int j = jf + (int)threadIdx.x; j < max_pages; j += 256) row[j] = -__builtin_inff();
+    }
+  };
   const int j0 = p0 + (chunk * 4 + wave) * PPW;
-  if (j0 >= max_pages) return;
+  if (j0 >= max_pages) {
+    fill_past();
+    return;
+  }
   const int j1 = min(j0 + PPW, max_pages);
   const int grp = lane >> 4;  // this lane's query group (output) and fp4 lane group
   const int col = lane & 15;  // token within a 16-token chunk
@@ -388,6 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
     phys_cur = phys_next;
   }
+  fill_past();
 }
 
 // FP8 caches (one E4M3 byte per element, FP32 tensor scale): the same scan
@@ -602,6 +663,10 @@ static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_sc
   if (ts)
     hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16>), grid, dim3(256), 0, s,
                        bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
+                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
+  else if (bt->num_reqs <= 64)
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16, true>), grid, dim3(256),
+                       0, s, bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
                        (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
   else
     hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16>), grid, dim3(256), 0, s,

@@ -130,6 +130,8 @@ CASES = {
     # (two query tiles for R=4, one for R=2) instead of one workgroup per row
     "union_r4": lambda: W.make_workload(4, seed=18, B=20, len_div=64, R=4),
     "union_r2": lambda: W.make_workload(4, seed=19, B=40, len_div=128, R=2),
+    # more than 64 requests: the scan's grid is not packed to the contexts (the per-lane map covers 64)
+    "many_reqs": lambda: W.make_workload(3, seed=21, B=80, len_div=256),
 }
 
 
@@ -279,7 +281,7 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
-                                  "fp8_prefill", "fp8_prefill_r512"])
+                                  "fp8_prefill", "fp8_prefill_r512", "many_reqs"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -307,7 +309,9 @@ def test_index_scores(M, oracle, case):
     assert np.array_equal(np.isneginf(got_blk), binv)
     pooled = got_tok.reshape(got_tok.shape[:3] + (wl.max_pages, 128)).max(-1)
     assert np.array_equal(got_blk, pooled)
-    # same kernel without the token-score output
+    # same kernel without the token-score output (which packs its grid to the contexts and
+    # writes the -inf of the pages past them separately): every entry must be rewritten
+    dec.block_scores.fill_(3.0)
     dec.index(q_idx, wl.q_scale, None)
     assert np.array_equal(dec.block_scores.cpu().numpy().astype(np.float64), got_blk)
 
@@ -486,7 +490,7 @@ def test_full_step_with_new_rows(M, oracle, case, fused):
     _check_full_step(M, oracle, wl, fused=fused, new_rows=True)
 
 
-@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8"])
+@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8", "many_reqs"])
 def test_insert_index_equals_separate_calls(M, oracle, case):
     """msa_insert_index_score: the caches bitwise as msa_kv_insert_nvfp4 writes them (and as
     the oracle writes them), and bitwise the block scores of msa_index_score after that insert."""
