@@ -90,6 +90,54 @@ __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
   return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
 }
 
+// The chunk of workgroup id (pages p0 + 4*PPW*chunk ..) and its request b,
+// with b's clamped length L and newest chunk.  Workgroups 0..B-1 take each
+// request's newest chunk.  Unpacked, workgroup B + b*(C-1) + i takes chunk i
+// of request b, skipping the newest (C chunks per table row; the chunks past
+// a context are empty).  Packed (COMPACT, B <= 64), workgroups B.. take only
+// the chunks below each newest one, request after request, from a prefix sum
+// of the B lengths held one per lane; false for the leftovers at the end.
+template <bool COMPACT, int PPW>
+__device__ __forceinline__ bool chunk_of(int id, int B, const int32_t* __restrict__ lens, int max_pages, int p0,
+                                         int lane, int& b, int& L, int& latest, int& chunk) {
+  if (COMPACT && id >= B) {
+    int Ll = 0, nl = 0;
+    if (lane < B) {
+      Ll = clamp_len(lens[lane], max_pages);
+      const int np = (Ll + kPage - 1) / kPage;
+      nl = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
+    }
+    const int incl = wave_incl_sum(nl, lane);
+    const int k = id - B;
+    if (k >= __builtin_amdgcn_readlane(incl, 63)) return false;
+    b = (int)__popcll(__ballot(incl <= k));  // requests whose chunks all lie before k
+    if (b >= B) return false;                // (never, with k below the total: keeps b in range)
+    chunk = k - __builtin_amdgcn_readlane(incl - nl, b);
+    L = __builtin_amdgcn_readlane(Ll, b);
+    latest = __builtin_amdgcn_readlane(nl, b);
+    return chunk >= 0 && chunk < latest;
+  }
+  const int C = (max_pages - p0 + 4 * PPW - 1) / (4 * PPW);
+  b = id < B ? id : (id - B) / max(C - 1, 1);
+  const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
+  L = clamp_len(lens[b], max_pages);  // id < B: a scalar load, first in the newest chunk's chain
+  const int np = (L + kPage - 1) / kPage;
+  latest = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
+  chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
+  return true;
+}
+
+// Packed grid: the pages past request b's newest chunk (from page jf on) have
+// no workgroup; the newest chunk's waves write their -inf block scores, each
+// wave its share of every row, after its own pages.
+template <int R>
+__device__ __forceinline__ void fill_past_chunks(float* __restrict__ block_scores, int b, int jf, int max_pages) {
+  for (int rg = 0; rg < R * kGroups; ++rg) {
+    float* row = block_scores + ((int64_t)b * R * kGroups + rg) * max_pages;
+    for (int j = jf + (int)threadIdx.x; j < max_pages; j += 256) row[j] = -__builtin_inff();
+  }
+}
+
 // Scores of one resident page for all R rows; returns per-row maxima (unscaled).
 template <int R, bool kTok>
 __device__ __forceinline__ void score_page(const PageRegs& pr, const v8i (&A)[R][2], const int (&pos_lim)[R], int j,
@@ -239,19 +287,13 @@ struct NewRows {
 // leading pages are shared by all requests and scored once, by
 // prefix_index_kernel); chunk i is pages p0 + 4*PPW*i ...
 // One-dimensional grid of B x C workgroups (C = page chunks per request row of
-// the table past p0).  Workgroups 0..B-1 take the chunk holding each request's newest
-// tokens, so the chunks that insert the step's tokens start first; workgroup
-// B + b*(C-1) + i then takes chunk i of request b, skipping the newest one
-// (i >= latest_b -> chunk i + 1).  Each request's remaining chunks are
-// consecutive workgroups, which the dispatcher deals round-robin to the 8
-// XCDs, and the chunks past a context (nothing to score) close its run.
-// COMPACT (B <= 64, block scores only): workgroups B.. are instead packed to
-// the chunks below each request's newest, in the same order, from a prefix
-// sum of all B lengths; the chunks past a context get no workgroup (their
-// -inf is written by the newest chunk's waves after their own pages), and the
-// leftover workgroups at the grid's end exit after the length load.  On a
-// ragged batch the scan no longer spends workgroup slots on empty chunks
-// between the real ones.  With INSERT the workgroup first writes
+// the table past p0), mapped to chunks by chunk_of.  Workgroups 0..B-1 take
+// the chunk holding each request's newest tokens, so the chunks that insert
+// the step's tokens start first.  Each request's other chunks are consecutive
+// workgroups, which the dispatcher deals round-robin to the 8 XCDs.  Unpacked,
+// the chunks past a context (nothing to score) close its run; packed
+// (COMPACT: B <= 64, block scores only) they get no workgroup, so a ragged
+// batch no longer spends workgroup slots on them between the real chunks.  With INSERT the workgroup first writes
 // the new tokens that fall in its chunk into the caches (one 16-lane row per
 // 16-element group, as the insert kernel does) and makes them visible to its
 // own waves before any page is read.
@@ -268,37 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int wave = threadIdx.x >> 6;
   const int id = (int)blockIdx.x;
   int b, L, latest, chunk;
-  if (COMPACT && id >= B) {
-    // B <= 64 and no per-token output: workgroups B.. take only the chunks
-    // below each request's newest one, packed request after request, and the
-    // workgroups left over at the end of the grid exit after one load.  Lane
-    // l holds request l's count of such chunks; every wave derives the same map.
-    int Ll = 0, nl = 0;
-    if (lane < B) {
-      Ll = clamp_len(lens[lane], max_pages);
-      const int np = (Ll + kPage - 1) / kPage;
-      nl = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
-    }
-    const int incl = wave_incl_sum(nl, lane);
-    const int k = id - B;
-    if (k >= __builtin_amdgcn_readlane(incl, 63)) return;
-    b = (int)__popcll(__ballot(incl <= k));  // requests whose chunks all lie before k
-    if (b >= B) return;                      // (never, with k below the total: keeps b in range)
-    chunk = k - __builtin_amdgcn_readlane(incl - nl, b);
-    L = __builtin_amdgcn_readlane(Ll, b);
-    latest = __builtin_amdgcn_readlane(nl, b);
-    if (chunk < 0 || chunk >= latest) return;
-  } else {
-    // the newest chunk of request id (id < B; also the packed form's), or
-    // chunk i_rest of (C - 1) per request, skipping the newest
-    const int C = (max_pages - p0 + 4 * PPW - 1) / (4 * PPW);
-    b = id < B ? id : (id - B) / max(C - 1, 1);
-    const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
-    L = clamp_len(lens[b], max_pages);
-    const int np = (L + kPage - 1) / kPage;
-    latest = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
-    chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
-  }
+  if (!chunk_of<COMPACT, PPW>(id, B, lens, max_pages, p0, lane, b, L, latest, chunk)) return;
   const int npb = (L + kPage - 1) / kPage;
   if (INSERT) {
     // new tokens [max(L - R, 0), L) that lie in this chunk's token range
@@ -350,15 +362,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   }
-  // COMPACT: the chunks past the newest have no workgroup; the newest chunk's
-  // waves write their -inf block scores once their own pages are done
   auto fill_past = [&] {
-    if (!COMPACT || id >= B) return;
-    const int jf = min(p0 + (latest + 1) * 4 * PPW, max_pages);
-    for (int rg = 0; rg < R * kGroups; ++rg) {
-      float* row = block_scores + ((int64_t)b * R * kGroups + rg) * max_pages;
-      for (int j = jf + (int)threadIdx.x; j < max_pages; j += 256) row[j] = -__builtin_inff();
-    }
+    if (COMPACT && id < B) fill_past_chunks<R>(block_scores, b, min(p0 + (latest + 1) * 4 * PPW, max_pages), max_pages);
   };
   const int j0 = p0 + (chunk * 4 + wave) * PPW;
   if (j0 >= max_pages) {
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 // lane (n, c) holds the scores of group c, rows 4*rp .. 4*rp+3, token n; the
 // block max is a 16-lane row reduction.  Grid, chunk order and the fused
 // insert follow index_nvfp4_kernel (one page per wave, 4 per workgroup).
-template <int R, bool kTok, bool INSERT, int WPE = 4>
+template <int R, bool kTok, bool INSERT, int WPE = 4, bool COMPACT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_fp8_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages,
     const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
@@ -472,14 +477,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   constexpr int RP = (R + 3) / 4;  // MFMAs per 16-token chunk (4 rows each)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int C = (max_pages + 3) / 4;
   const int id = (int)blockIdx.x;
-  const int b = id < B ? id : (id - B) / max(C - 1, 1);
-  const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
-  const int L = clamp_len(lens[b], max_pages);
+  int b, L, latest, chunk;
+  if (!chunk_of<COMPACT, 1>(id, B, lens, max_pages, 0, lane, b, L, latest, chunk)) return;
   const int npb = (L + kPage - 1) / kPage;
-  const int latest = npb > 0 ? (npb - 1) / 4 : 0;
-  const int chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
   if (INSERT) {
     // new tokens [max(L - R, 0), L) in this chunk: one thread per element
     // (4 x 128 keys, 4 x 128 values, 128 index keys per token)
@@ -512,8 +513,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   }
+  const bool fill = COMPACT && id < B;
   const int j = chunk * 4 + wave;
-  if (j >= max_pages) return;
+  if (j >= max_pages) {
+    if (fill) fill_past_chunks<R>(block_scores, b, min((latest + 1) * 4, max_pages), max_pages);
+    return;
+  }
   const int n = lane & 15, c = lane >> 4;
   const int64_t T = (int64_t)max_pages * kPage;
 
@@ -582,6 +587,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const float mm = wave_max16(m[r]);
     if (n == 0) block_scores[(((int64_t)b * R + r) * kGroups + c) * max_pages + j] = mm * out_scale;
   }
+  if (fill) fill_past_chunks<R>(block_scores, b, min((latest + 1) * 4, max_pages), max_pages);
 }
 
 template <int R, bool INSERT>
@@ -592,6 +598,10 @@ static void launch_fp8(const msa_batch* bt, const uint8_t* q, float out_scale, c
     hipLaunchKernelGGL((index_fp8_kernel<R, true, INSERT>), grid, dim3(256), 0, s, bt->block_table, bt->ctx_lens,
                        bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs, ts,
                        bt->num_reqs, nr);
+  else if (bt->num_reqs <= 64)
+    hipLaunchKernelGGL((index_fp8_kernel<R, false, INSERT, 4, true>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs,
+                       ts, bt->num_reqs, nr);
   else
     hipLaunchKernelGGL((index_fp8_kernel<R, false, INSERT>), grid, dim3(256), 0, s, bt->block_table, bt->ctx_lens,
                        bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs, ts,

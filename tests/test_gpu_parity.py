@@ -132,6 +132,7 @@ CASES = {
     "union_r2": lambda: W.make_workload(4, seed=19, B=40, len_div=128, R=2),
     # more than 64 requests: the scan's grid is not packed to the contexts (the per-lane map covers 64)
     "many_reqs": lambda: W.make_workload(3, seed=21, B=80, len_div=256),
+    "fp8_many_reqs": lambda: W.make_workload(3, seed=22, B=80, len_div=256, cache="fp8"),
 }
 
 
@@ -281,7 +282,7 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
-                                  "fp8_prefill", "fp8_prefill_r512", "many_reqs"])
+                                  "fp8_prefill", "fp8_prefill_r512", "many_reqs", "fp8_many_reqs"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
