@@ -122,6 +122,105 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
                       f"scaled by context tokens"}
 
 
+QKV_HEADS = 45  # 32 query heads, 4 key, 4 value, 4 index queries, 1 index key
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+
+
+def qkv_algorithmic(n, hidden):
+    """(bytes, flops) of one fused projection + norm + RoPE + insert launch: weights and
+    hidden states once, the rotary rows of n positions, FP8 queries and index queries out,
+    72 B per token per NVFP4 head written (4 key, 4 value, 1 index-key head)."""
+    nbytes = (QKV_HEADS * 128 * hidden * 2 + n * hidden * 2 + n * 128 * 4 + n * 36 * 128 + n * 9 * 72
+              + 4 * 128 * 4 + n * 12)
+    return nbytes, 2.0 * n * QKV_HEADS * 128 * hidden
+
+
+def bench_qkv(args):
+    """The fused projection of n new rows at model width `hidden` (the pages give no width;
+    3,072 by default): HIP events around a graph of back-to-back launches."""
+    import torch
+
+    import block_sparse_attention_index_amd as M
+    import workload as W
+
+    n, hidden = args.qkv, args.hidden
+    q = W.make_qkv_inputs(args.seed, n, hidden, max_pos=200_000, num_pages=max(1, -(-n // 128)) + 1)
+    if n >= 512:  # a prompt chunk: consecutive slots
+        q.slots = np.arange(n, dtype=np.int64) + 64
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x, w = dev(q.x.view(np.int16)), dev(W.pack_qkv_weights(q.w).view(np.int16))
+    g, rope, pos, slots = dev(q.norm_weight), dev(q.rope), dev(q.positions), dev(q.slots)
+    kc = M.Cache.empty(M.MSA_NVFP4, M.MSA_TOKEN_MAJOR, 4, q.num_pages, q.tensor_scale)
+    vc = M.Cache.empty(M.MSA_NVFP4, M.MSA_DIM_MAJOR, 4, q.num_pages, q.tensor_scale)
+    ic = M.Cache.empty(M.MSA_NVFP4, M.MSA_TOKEN_MAJOR, 1, q.num_pages, q.tensor_scale)
+    q_out = torch.empty((n, 32, 128), dtype=torch.uint8, device="cuda")
+    qi_out = torch.empty((n, 4, 128), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    hbm = n <= 256  # the weights dominate: a stream; else the products do
+    # a few new rows: rotate over weight copies larger together than the 256 MB Infinity
+    # Cache, as the layers of a model would, so that no launch finds its weights cached
+    ws = [w] + [w.clone() for _ in range((8 if hbm else 1) - 1)]
+
+    def launch(i):
+        M.msa_qkv_project_insert(x, ws[i % len(ws)], g, q.eps, rope, pos, slots, q.q_scale, q_out, qi_out, kc, vc,
+                                 ic, stream=stream)
+
+    per_graph = 24
+    reps = max(1, args.steps // per_graph)
+    with torch.cuda.stream(stream):
+        for i in range(max(1, args.warmup)):
+            launch(i)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(per_graph):
+                launch(i)
+        graph.replay()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a_.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    us = a_.elapsed_time(b_) * 1e3 / (reps * per_graph)
+    nbytes, flops = qkv_algorithmic(n, hidden)
+    if hbm:
+        roof = {"bound": "hbm", "kernel": "qkv_insert_kernel", "achieved": nbytes / us / 1e3, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "bytes_per_launch": nbytes}
+    else:
+        roof = {"bound": "mfma", "kernel": "qkv_insert_kernel (v_mfma_f32_16x16x32_bf16)",
+                "achieved": flops / us / 1e6, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "flops_per_launch": flops}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["avg_launch_us"] = us
+    roof["traffic"] = None
+    log(f"qkv n={n} hidden={hidden}: {us:.1f} us per launch")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        k = min(n, 16)
+        reps_c, t0 = 0, time.perf_counter()
+        while True:
+            O.qkv_project(q.x[:k], q.w, q.norm_weight, q.eps, q.rope, q.positions[:k])
+            reps_c += 1
+            el = time.perf_counter() - t0
+            if el >= 5.0:
+                break
+        cpu = {"value": k * reps_c / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"projection + norm + rotary of {k} of {n} tokens x{reps_c} in {el:.1f} s "
+                         f"(quantisation not included)"}
+    line = {"metric": "fused QKV projection + norm + RoPE + NVFP4 insert, tokens/s", "value": n / us * 1e6,
+            "unit": "tokens/s", "n_gpus": 1, "steps": reps * per_graph, "warmup": args.warmup,
+            "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16 x bf16 (f32 accumulate) -> fp8 q, nvfp4 kv", "data": "synthetic N(0,1), seeded",
+            "config": {"workload": f"qkv_project_insert_n{n}_hidden{hidden}", "tokens": n, "hidden": hidden,
+                       "heads": "32 q + 4 k + 4 v + 4 index q + 1 index k, dim 128", "parallelism": "single-gpu",
+                       "hip_graph": True, "launches_per_graph": per_graph, "weight_copies": len(ws)},
+            "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_nvfp4_long_ctx_b32_64k_192k_hbm_traffic.md")
 INDEX_KERNEL_SOURCES = ["include/msa.h", "block_sparse_attention_index_amd/csrc/msa_device.h",
                         "block_sparse_attention_index_amd/csrc/msa_index.hip"]
@@ -225,12 +324,20 @@ def main():
                          "--steps not above this value is used")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the oracle's timed sample")
+    ap.add_argument("--qkv", type=int, default=0, metavar="N",
+                    help="instead of the step: the fused projection + norm + RoPE + insert of N new rows "
+                         "(32 = the default workload's decode step, 8192 = the prefill chunk)")
+    ap.add_argument("--hidden", type=int, default=3072, help="model width for --qkv (the pages give none)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the context-parallel indexer is a design, not code).", file=sys.stderr)
         sys.exit(2)
+
+    if args.qkv:
+        bench_qkv(args)
+        return
 
     st = setup(args.seed, args.replicas, args.config, args.kv)
     headline = args.config == CONFIG_ID and args.kv == "nvfp4"

@@ -62,6 +62,8 @@ def _load() -> C.CDLL:
                                         vp, vp, vp]),
         "msa_insert_index_score": (C.c_int, [P(msa_batch), vp, vp, vp, vp, i32, f32, P(msa_cache), P(msa_cache),
                                              P(msa_cache), vp, vp, vp]),
+        "msa_qkv_project_insert": (C.c_int, [vp, vp, i32, i32, vp, f32, vp, i32, vp, vp, f32, vp, vp, P(msa_cache),
+                                             P(msa_cache), P(msa_cache), vp, vp]),
         "msa_status_str": (C.c_char_p, [C.c_int]),
         "msa_debug_dequant": (C.c_int, [P(msa_cache), vp, i32, i32, vp, vp]),
     }
@@ -165,6 +167,18 @@ def msa_kv_insert_nvfp4(k, v, idx_k, slot_mapping, k_cache, v_cache, idx_cache, 
     n = slot_mapping.shape[0]
     _check(lib.msa_kv_insert_nvfp4(_ptr(k), _ptr(v), _ptr(idx_k), _ptr(slot_mapping), n, _cref(k_cache),
                                    _cref(v_cache), _cref(idx_cache), _stream(stream)), "msa_kv_insert_nvfp4")
+
+
+def msa_qkv_project_insert(x, w, norm_weight, eps: float, rope_cos_sin, positions, slot_mapping, q_scale: float,
+                           q_out, q_idx_out, k_cache, v_cache, idx_cache, pre_quant=None, stream=None) -> None:
+    """x [n][hidden] BF16 bit patterns (int16/uint16/bfloat16 tensor); w the BF16 weights in the
+    library's 32-k blocked layout, [45][hidden/32][128][32]."""
+    n, hidden = x.shape
+    _check(lib.msa_qkv_project_insert(_ptr(x), _ptr(w), n, hidden, _ptr(norm_weight), float(eps), _ptr(rope_cos_sin),
+                                      rope_cos_sin.shape[0], _ptr(positions), _ptr(slot_mapping), float(q_scale),
+                                      _ptr(q_out), _ptr(q_idx_out), _cref(k_cache), _cref(v_cache), _cref(idx_cache),
+                                      _ptr(pre_quant), _stream(stream)),
+           "msa_qkv_project_insert")
 
 
 def msa_quantize_e4m3(x: torch.Tensor, scale: float = 1.0, out: torch.Tensor | None = None, stream=None):

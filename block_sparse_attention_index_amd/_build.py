@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["msa_api.hip", "msa_insert.hip", "msa_index.hip", "msa_prefix.hip", "msa_topk.hip", "msa_attn.hip"]
+SOURCES = ["msa_api.hip", "msa_insert.hip", "msa_index.hip", "msa_prefix.hip", "msa_topk.hip", "msa_attn.hip",
+           "msa_qkv.hip"]
 # Per-file flags.  msa_prefix.hip: max-pooling of matrix-core results is
 # compiled without NaN canonicalisation (every fmaxf there would otherwise
 # first quieten its operand with an extra v_max x, x); the hardware maximum

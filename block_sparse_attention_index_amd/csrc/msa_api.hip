@@ -83,6 +83,30 @@ int msa_kv_insert_nvfp4(const float* k, const float* v, const float* idx_k, cons
   return insert_impl(k, v, idx_k, slot_mapping, n, k_cache, v_cache, idx_cache, stream, true);
 }
 
+int msa_qkv_project_insert(const uint16_t* x, const uint16_t* w, int32_t n, int32_t hidden,
+                           const float* norm_weight, float eps, const float* rope_cos_sin, int32_t rope_rows,
+                           const int32_t* positions, const int64_t* slot_mapping, float q_scale, uint8_t* q_out,
+                           uint8_t* q_idx_out, const msa_cache* k_cache, const msa_cache* v_cache,
+                           const msa_cache* idx_cache, float* pre_quant, hipStream_t stream) {
+  if (n < 0 || hidden < 256 || hidden % 256 != 0 || hidden > (1 << 16)) return MSA_ERR_INVALID_ARG;
+  if (!isfinite(eps) || eps < 0.0f || !finite_pos(q_scale) || rope_rows < 1) return MSA_ERR_INVALID_ARG;
+  int st;
+  if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
+  if ((st = check_cache(idx_cache, INDEX)) != MSA_OK) return st;
+  for (const msa_cache* c : {k_cache, v_cache, idx_cache})
+    if (c->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (n == 0) return MSA_OK;
+  if (!x || !w || !norm_weight || !rope_cos_sin || !positions || !slot_mapping || !q_out || !q_idx_out)
+    return MSA_ERR_INVALID_ARG;
+  if ((n + 63) / 64 > 65535) return MSA_ERR_INVALID_ARG;  // grid y: 64 tokens per workgroup past 64 rows
+  QkvArgs A{x, w, n, hidden, norm_weight, eps, rope_cos_sin, rope_rows, positions, slot_mapping, q_scale, q_out,
+            q_idx_out, (uint8_t*)k_cache->pages, (uint8_t*)v_cache->pages, (uint8_t*)idx_cache->pages,
+            k_cache->num_pages, v_cache->num_pages, idx_cache->num_pages, k_cache->tensor_scale,
+            v_cache->tensor_scale, idx_cache->tensor_scale, pre_quant};
+  return msa_launch_qkv_insert(&A, stream) == 0 ? MSA_OK : MSA_ERR_HIP;
+}
+
 int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!x || !out)) || !finite_pos(scale)) return MSA_ERR_INVALID_ARG;
   if (n == 0) return MSA_OK;

@@ -8,7 +8,28 @@
 
 #include "msa.h"
 
+// Arguments of msa_qkv_project_insert after validation (caches unpacked).
+struct QkvArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  int32_t n, hidden;
+  const float* norm_weight;  // [4][128]
+  float eps;
+  const float* rope;  // [rope_rows][128]: cos, then sin
+  int32_t rope_rows;
+  const int32_t* pos;
+  const int64_t* slots;
+  float q_scale;
+  uint8_t* q_out;
+  uint8_t* qidx_out;
+  uint8_t *kpages, *vpages, *ipages;
+  int32_t knp, vnp, inp;
+  float kts, vts, its;
+  float* pre;
+};
+
 extern "C" {
+int msa_launch_qkv_insert(const QkvArgs* args, hipStream_t stream);
 int msa_launch_kv_insert(const float* k, const float* v, const float* idx_k, const int64_t* slots, int32_t n,
                          const msa_cache* kc, const msa_cache* vc, const msa_cache* ic, hipStream_t stream);
 int msa_launch_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream);

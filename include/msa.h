@@ -70,6 +70,7 @@ typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1, MSA_HALF_ROWS = 2 } msa_l
 #define MSA_NVFP4_SLAB_BYTES 9216
 #define MSA_F32_SLAB_BYTES 65536
 #define MSA_FP8_SLAB_BYTES 16384
+#define MSA_QKV_HEADS 45
 
 /*
  * One paged cache tensor of one layer.  Page p, head h is the slab at
@@ -154,6 +155,42 @@ int msa_kv_insert(const float* k, const float* v, const float* idx_k, const int6
 int msa_kv_insert_nvfp4(const float* k, const float* v, const float* idx_k, const int64_t* slot_mapping,
                         int32_t n, const msa_cache* k_cache, const msa_cache* v_cache,
                         const msa_cache* idx_cache, hipStream_t stream);
+
+/*
+ * The projection that produces a step's new rows, fused with step 0 (vLLM
+ * post, "QKV GEMM + norm + RoPE + KV 插入融合": the GEMM's epilogue takes the
+ * FP32 accumulators head by head, applies norm and RoPE to the queries and
+ * index queries, quantises K, V and the index key to NVFP4 and writes them
+ * into the caches; the projected rows never reach HBM).
+ *   x: [n][hidden] BF16 hidden states; w: BF16 projection weights in 32-k
+ *   blocks, w[h][k/32][r][k%32] = W[128 h + r][k], where output column c is
+ *   sum_k x[t][k] W[c][k] (a layout the weights are packed into once; each
+ *   16-row operand of the matrix cores is then one contiguous 1 KB).  Columns
+ *   are 45 heads of 128: query heads 0..31, key heads 32..35, value heads 36..39,
+ *   index queries 40..43 (one per group), index key 44.  hidden: a multiple
+ *   of 256, at most 65536.  The products accumulate in FP32.
+ * The pages state no norm or rotary detail; the reading taken: for every
+ * head but the values, y = h / sqrt(mean(h^2) + eps) * norm_weight[kind][d]
+ * over the head's 128 values (kind 0 queries, 1 keys, 2 index queries,
+ * 3 index key; norm_weight: [4][128] FP32), then rotate-half rotary
+ * embedding: for i < 64, with c = rope_cos_sin[p][i], s = rope_cos_sin[p][64+i]
+ * (rope_cos_sin: [rope_rows][128] FP32, p = positions[t]),
+ *   out_i = y_i c - y_{i+64} s,  out_{i+64} = y_{i+64} c + y_i s.
+ * Values are stored as projected.  Queries go to q_out [n][32][128] and index
+ * queries to q_idx_out [n][4][128] as E4M3(out / q_scale); keys, values and
+ * the index key go to slot_mapping[t] of the three NVFP4 caches by the
+ * quantiser of msa_kv_insert.  A token whose position lies outside
+ * [0, rope_rows) is skipped: nothing of it is written.  A token whose slot
+ * lies outside the page pools writes its queries but no cache bytes.
+ * pre_quant (may be NULL; a test aid): [n][45][128] FP32, the values just
+ * before quantisation.  Every cache must be NVFP4 (MSA_ERR_UNSUPPORTED).
+ * n: at most 64 * 65535 rows.
+ */
+int msa_qkv_project_insert(const uint16_t* x, const uint16_t* w, int32_t n, int32_t hidden,
+                           const float* norm_weight, float eps, const float* rope_cos_sin, int32_t rope_rows,
+                           const int32_t* positions, const int64_t* slot_mapping, float q_scale, uint8_t* q_out,
+                           uint8_t* q_idx_out, const msa_cache* k_cache, const msa_cache* v_cache,
+                           const msa_cache* idx_cache, float* pre_quant, hipStream_t stream);
 
 /* FP32 -> FP8 E4M3 (OCP) query bytes: out[i] = E4M3_sat_RNE(x[i] / scale), NaN -> 0x7F|sign.
  * Queries stay FP8 while the cache is NVFP4 (vLLM post, Blackwell section). scale > 0. */

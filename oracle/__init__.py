@@ -57,6 +57,9 @@ def lib() -> C.CDLL:
         L.ref_index_scores.restype, L.ref_index_scores.argtypes = None, [vp, C.c_int, vp, vp, vp, vp]
         L.ref_block_maxpool.restype, L.ref_block_maxpool.argtypes = None, [vp, C.c_int, vp, vp]
         L.ref_select.restype, L.ref_select.argtypes = None, [vp, C.c_int, vp, C.c_int, vp, vp]
+        L.ref_bf16_value.restype, L.ref_bf16_value.argtypes = f64, [C.c_uint16]
+        L.ref_qkv_project.restype = None
+        L.ref_qkv_project.argtypes = [vp, vp, i32, i32, vp, f32, vp, i32, vp, vp]
         L.ref_attention.restype = None
         L.ref_attention.argtypes = [vp, C.c_int, C.c_int, vp, f64, vp, vp, vp, vp, C.c_int, vp]
         _lib = L
@@ -140,6 +143,30 @@ def decode_queries(q, dtype: int, q_scale: float = 1.0) -> np.ndarray:
     q = np.ascontiguousarray(q)
     out = np.zeros(q.shape, dtype=np.float64)
     lib().ref_decode_queries(_ptr(q), dtype, C.c_float(q_scale), q.size, _ptr(out))
+    return out
+
+
+QKV_HEADS = 45  # query heads 0..31, keys 32..35, values 36..39, index queries 40..43, index key 44
+
+
+def bf16_value(bits: int) -> float:
+    return lib().ref_bf16_value(int(bits))
+
+
+def qkv_project(x_bits, w_bits, norm_weight, eps: float, rope, positions) -> np.ndarray:
+    """The rows a step's projection produces after norm and rotary embedding (values as
+    projected): [n][45][128] FP32.  x_bits [n][hidden], w_bits [45*128][hidden] BF16 bit
+    patterns (uint16); norm_weight [4][128]; rope [rows][128] (cos, then sin); positions [n]."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    g = np.ascontiguousarray(norm_weight, dtype=np.float32)
+    rp = np.ascontiguousarray(rope, dtype=np.float32)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    n, hidden = x.shape
+    assert w.shape == (QKV_HEADS * DIM, hidden) and g.shape == (4, DIM) and rp.shape[1] == DIM
+    out = np.zeros((n, QKV_HEADS, DIM), dtype=np.float32)
+    lib().ref_qkv_project(_ptr(x), _ptr(w), n, hidden, _ptr(g), C.c_float(eps), _ptr(rp), rp.shape[0], _ptr(pos),
+                          _ptr(out))
     return out
 
 

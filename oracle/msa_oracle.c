@@ -504,3 +504,75 @@ void ref_decode_step(const ref_batch* bt, int H, int G, const double* q_idx, con
   ref_select(bt, G, block_scores, topk, sel, cnt);
   ref_attention(bt, H, G, q, sm_scale, kc, vc, sel, cnt, topk, out);
 }
+
+/* ------------------------------------------------------------------------- */
+/* The projection that produces a step's new rows and the norm and rotary
+ * embedding applied to them before they are quantised ([P2] section
+ * "QKV GEMM + norm + RoPE + KV 插入融合": the projection's output is taken
+ * head by head; queries and index queries get norm and RoPE; K, V and the
+ * index key are quantised into the caches).  The pages state neither the
+ * norm nor the rotary detail.  Readings taken: a per-head RMS norm with one
+ * learned weight vector per head kind, then rotate-half rotary embedding of
+ * dims (i, i + 64) from a caller-supplied cos/sin table, applied to every
+ * head except the values (keys need the same rotation as the queries for the
+ * scores to depend on relative position).
+ *
+ * Output columns: 45 heads of 128 -- query heads 0..31, key heads 32..35,
+ * value heads 36..39, index queries 40..43, index key 44.  Head kinds for the
+ * norm weight: 0 queries, 1 keys, 2 index queries, 3 index key. */
+#define REF_QKV_HEADS 45
+
+/* BF16: the upper 16 bits of an IEEE binary32. */
+double ref_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* x: [n][hidden] BF16, w: [45*128][hidden] BF16 (row c produces column c),
+ * norm_weight: [4][128], rope: [rope_rows][128] (cos of the 64 frequencies,
+ * then their sin), pos: [n].  out: [n][45][128] FP32, each value rounded once
+ * from double; a token whose position is outside [0, rope_rows) gets NaN. */
+void ref_qkv_project(const uint16_t* x, const uint16_t* w, int32_t n, int32_t hidden, const float* norm_weight,
+                     float eps, const float* rope, int32_t rope_rows, const int32_t* pos, float* out) {
+  double h[REF_DIM], y[REF_DIM];
+  for (int32_t t = 0; t < n; ++t) {
+    const int p = pos[t];
+    for (int hd = 0; hd < REF_QKV_HEADS; ++hd) {
+      float* o = out + ((int64_t)t * REF_QKV_HEADS + hd) * REF_DIM;
+      if (p < 0 || p >= rope_rows) {
+        for (int d = 0; d < REF_DIM; ++d) o[d] = NAN;
+        continue;
+      }
+      /* the projection: h_d = sum_k x[t][k] w[hd*128 + d][k] */
+      for (int d = 0; d < REF_DIM; ++d) {
+        const uint16_t* wr = w + ((int64_t)hd * REF_DIM + d) * hidden;
+        const uint16_t* xr = x + (int64_t)t * hidden;
+        double acc = 0.0;
+        for (int k = 0; k < hidden; ++k) acc += ref_bf16_value(xr[k]) * ref_bf16_value(wr[k]);
+        h[d] = acc;
+      }
+      const int is_value = hd >= 36 && hd < 40;
+      if (is_value) {
+        for (int d = 0; d < REF_DIM; ++d) o[d] = (float)h[d];
+        continue;
+      }
+      const int kind = hd < 32 ? 0 : hd < 36 ? 1 : hd < 44 ? 2 : 3;
+      /* RMS norm over the head's 128 values, times the kind's weight */
+      double ms = 0.0;
+      for (int d = 0; d < REF_DIM; ++d) ms += h[d] * h[d];
+      ms /= REF_DIM;
+      const double inv = 1.0 / sqrt(ms + (double)eps);
+      for (int d = 0; d < REF_DIM; ++d) y[d] = h[d] * inv * (double)norm_weight[kind * REF_DIM + d];
+      /* rotate-half: the pair (i, i + 64) turns by the angle whose cos and sin
+       * are the table's entries i and 64 + i at the token's position */
+      const float* cs = rope + (int64_t)p * REF_DIM;
+      for (int i = 0; i < REF_DIM / 2; ++i) {
+        const double c = cs[i], s = cs[REF_DIM / 2 + i];
+        o[i] = (float)(y[i] * c - y[i + REF_DIM / 2] * s);
+        o[i + REF_DIM / 2] = (float)(y[i + REF_DIM / 2] * c + y[i] * s);
+      }
+    }
+  }
+}

@@ -157,3 +157,36 @@ def test_layout_rules_without_gpu(lib):
     lib.msa_debug_dequant.restype = C.c_int
     assert lib.msa_debug_dequant(C.byref(Cache(NV, HR, 1, 16, 0.01, fake)), fake, 1, 0, fake, None) == -2
     assert lib.msa_debug_dequant(C.byref(Cache(FP8, 9, 1, 16, 0.01, fake)), fake, 1, 0, fake, None) == -1
+
+
+def test_qkv_project_insert_validation(lib):
+    """Every call here fails validation (or has nothing to do) before any launch."""
+    fake = C.c_void_p(0x1000)
+    k = Cache(2, 0, 4, 16, 0.01, fake)
+    v = Cache(2, 1, 4, 16, 0.01, fake)
+    i = Cache(2, 0, 1, 16, 0.01, fake)
+    f = lib.msa_qkv_project_insert
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_float, C.c_void_p, C.c_int32,
+                  C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.POINTER(Cache), C.POINTER(Cache),
+                  C.POINTER(Cache), C.c_void_p, C.c_void_p]
+
+    def call(n=4, hidden=512, eps=1e-6, rope_rows=16, q_scale=1.0, kc=k, vc=v, ic=i, x=fake):
+        return f(x, fake, n, hidden, fake, eps, fake, rope_rows, fake, fake, q_scale, fake, fake,
+                 C.byref(kc), C.byref(vc), C.byref(ic), None, None)
+
+    assert call(hidden=384) == -1          # not a multiple of 256
+    assert call(hidden=0) == -1
+    assert call(hidden=1 << 17) == -1
+    assert call(n=-1) == -1
+    assert call(eps=-1.0) == -1
+    assert call(eps=float("nan")) == -1
+    assert call(q_scale=0.0) == -1
+    assert call(rope_rows=0) == -1
+    assert call(x=None) == -1              # n > 0 needs every pointer
+    assert call(n=64 * 65536) == -1        # grid rows
+    k8 = Cache(1, 0, 4, 16, 0.01, fake)
+    assert call(kc=k8) == -2               # NVFP4 caches only
+    assert call(vc=Cache(2, 0, 4, 16, 0.01, fake)) == -2   # values must be dim-major
+    assert call(ic=Cache(2, 0, 4, 16, 0.01, fake)) == -1   # one index head
+    assert call(n=0) == 0                  # nothing to do, nothing launched

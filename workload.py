@@ -195,3 +195,64 @@ def torch_rows(wl: Workload, b: int, device, prefix: bool = False):
     k = torch.randn((n, wl.G, wl.D), generator=gen, device=device, dtype=torch.float32)
     v = torch.randn((n, wl.G, wl.D), generator=gen, device=device, dtype=torch.float32)
     return idx, k, v
+
+
+# --------------------------------------------------------------------------- projection inputs
+QKV_HEADS = 45  # query heads 0..31, key heads 32..35, value heads 36..39, index queries 40..43, index key 44
+ROPE_THETA = 10000.0  # rotary base of the synthetic cos/sin table (the pages give none)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """FP32 values -> BF16 bit patterns, round to nearest even: how the synthetic hidden
+    states and weights are drawn as BF16 numbers."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+@dataclass
+class QkvInputs:
+    x: np.ndarray            # [n][hidden] BF16 bits (uint16): hidden states of the step's new rows
+    w: np.ndarray            # [45*128][hidden] BF16 bits: projection weights, row c -> column c
+    norm_weight: np.ndarray  # [4][128] FP32: queries, keys, index queries, index key
+    rope: np.ndarray         # [rows][128] FP32: cos of the 64 frequencies, then sin
+    positions: np.ndarray    # [n] int32
+    slots: np.ndarray        # [n] int64
+    num_pages: int
+    eps: float = 1e-6
+    q_scale: float = 1.0
+    tensor_scale: float = 4.5 / (6 * 448)  # |normalised values| and |projected values| stay below ~4.5
+
+
+def pack_qkv_weights(w: np.ndarray) -> np.ndarray:
+    """[45*128][hidden] -> the library's 32-k blocked layout [45][hidden/32][128][32] (a
+    permutation of the BF16 words, done once per model)."""
+    rows, hidden = w.shape
+    return np.ascontiguousarray(w.reshape(QKV_HEADS, DIM, hidden // 32, 32).transpose(0, 2, 1, 3))
+
+
+def rope_table(rows: int) -> np.ndarray:
+    """cos/sin of position x theta^(-2i/128), i < 64, computed in float64, stored FP32."""
+    inv = ROPE_THETA ** (-np.arange(64, dtype=np.float64) * 2.0 / DIM)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_qkv_inputs(seed: int, n: int, hidden: int, max_pos: int = 4096, num_pages: int | None = None,
+                    bad_positions: int = 0, bad_slots: int = 0) -> QkvInputs:
+    """Seeded inputs of the fused projection: x ~ N(0,1), w ~ N(0, 1/hidden) (projected values
+    ~ N(0,1)), norm weights 1 + 0.1 N(0,1), positions uniform in [0, max_pos), distinct slots
+    drawn from the page pool; the first `bad_positions` tokens get a position past the table
+    and the next `bad_slots` tokens a slot outside the pool."""
+    rng = np.random.default_rng([seed, 7])
+    x = bf16_bits(rng.standard_normal((n, hidden), dtype=np.float32))
+    w = bf16_bits(rng.standard_normal((QKV_HEADS * DIM, hidden), dtype=np.float32) / np.float32(np.sqrt(hidden)))
+    g = (1.0 + 0.1 * rng.standard_normal((4, DIM))).astype(np.float32)
+    pos = rng.integers(0, max_pos, size=n).astype(np.int32)
+    if num_pages is None:
+        num_pages = max(1, -(-2 * n // PAGE))
+    slots = rng.permutation(num_pages * PAGE)[:n].astype(np.int64)
+    pos[:bad_positions] = max_pos + np.arange(bad_positions, dtype=np.int32)
+    slots[bad_positions:bad_positions + bad_slots] = np.where(np.arange(bad_slots) % 2 == 0, -1,
+                                                              num_pages * PAGE + np.arange(bad_slots))
+    return QkvInputs(x=x, w=w, norm_weight=g, rope=rope_table(max_pos), positions=pos, slots=slots,
+                     num_pages=num_pages)
