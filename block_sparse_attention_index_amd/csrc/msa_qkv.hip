@@ -13,8 +13,10 @@
 // key; values are stored as projected.
 //
 // Output columns: 45 heads of 128 -- 32 query heads, 4 key heads, 4 value
-// heads, 4 index queries (one per group), 1 index key.  One workgroup of 16
-// waves computes one head for 64 tokens (16 for a call of at most 64 rows):
+// heads, 4 index queries (one per group), 1 index key.  A call of at most 64
+// rows runs qkv_insert_kernel, one workgroup of 16 waves per (head, 16 rows);
+// a prompt chunk runs qkv_insert_tiled_kernel (LDS-staged, below).  In the
+// first:
 //  * GEMM on v_mfma_f32_16x16x32_bf16.  Each lane's operand is 8 consecutive
 //    k of one row: one 16-byte load.  x [n][hidden] is row-major; the weights
 //    come in 32-k blocks, w[head][k/32][row][k%32], so a wave's operand for 16
@@ -35,6 +37,73 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf8 load_bf8(const uint16_t* p) {
   return __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(p));
+}
+
+// The epilogue's view of one head: its kind (0 query, 1 key, 2 value,
+// 3 index query, 4 index key), index within the kind, and this lane's two
+// norm weights (dims lane and lane + 64).
+struct QkvHead {
+  int head, kind, sub;
+  float g_lo, g_hi;
+};
+
+__device__ __forceinline__ QkvHead qkv_head(const QkvArgs& A, int head, int lane) {
+  QkvHead h;
+  h.head = head;
+  h.kind = head < 32 ? 0 : head < 36 ? 1 : head < 40 ? 2 : head < 44 ? 3 : 4;
+  h.sub = h.kind == 0 ? head : h.kind == 1 ? head - 32 : h.kind == 2 ? head - 36 : h.kind == 3 ? head - 40 : 0;
+  const int gsel = h.kind == 0 ? 0 : h.kind == 1 ? 1 : h.kind == 3 ? 2 : 3;  // norm weight row
+  h.g_lo = h.g_hi = 0.f;
+  if (h.kind != 2) {
+    h.g_lo = A.norm_weight[gsel * kDim + lane];
+    h.g_hi = A.norm_weight[gsel * kDim + 64 + lane];
+  }
+  return h;
+}
+
+// One token of one head, on one wave: lo / hi are the projected values of
+// dims lane and lane + 64.  Norm, rotation, then the head's destination.
+__device__ __forceinline__ void qkv_epilogue_token(const QkvArgs& A, const QkvHead& hd, int tok, float lo, float hi,
+                                                   int lane) {
+  const int n = lane & 15, a = lane >> 4;
+  const int p = A.pos[tok];
+  if (p < 0 || p >= A.rope_rows) return;  // no rotation for this token: nothing of it is written
+  if (hd.kind != 2) {
+    // RMS norm: sum of squares over the head's 128 values (every lane gets it)
+    float ss = lo * lo + hi * hi;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float inv = 1.0f / sqrtf(ss / (float)kDim + A.eps);
+    const float ylo = lo * inv * hd.g_lo, yhi = hi * inv * hd.g_hi;
+    const float c = A.rope[(int64_t)p * kDim + lane], s = A.rope[(int64_t)p * kDim + 64 + lane];
+    lo = ylo * c - yhi * s;
+    hi = yhi * c + ylo * s;
+  }
+  if (A.pre) {
+    float* pr = A.pre + ((int64_t)tok * MSA_QKV_HEADS + hd.head) * kDim;
+    pr[lane] = lo;
+    pr[64 + lane] = hi;
+  }
+  if (hd.kind == 0 || hd.kind == 3) {
+    uint8_t* q = hd.kind == 0 ? A.q_out + ((int64_t)tok * 32 + hd.sub) * kDim
+                              : A.qidx_out + ((int64_t)tok * 4 + hd.sub) * kDim;
+    q[lane] = (uint8_t)e4m3_encode(lo / A.q_scale);
+    q[64 + lane] = (uint8_t)e4m3_encode(hi / A.q_scale);
+    return;
+  }
+  uint8_t* pages = hd.kind == 1 ? A.kpages : hd.kind == 2 ? A.vpages : A.ipages;
+  const int np = hd.kind == 1 ? A.knp : hd.kind == 2 ? A.vnp : A.inp;
+  const int heads = hd.kind == 4 ? 1 : kGroups;
+  const float ts = hd.kind == 1 ? A.kts : hd.kind == 2 ? A.vts : A.its;
+  const int64_t slot = A.slots[tok];
+  const bool valid = slot >= 0 && slot < (int64_t)np * kPage;
+  uint8_t* slab = pages + ((valid ? slot >> 7 : 0) * heads + hd.sub) * (int64_t)kNvSlab;
+  const int off = (int)(slot & (kPage - 1));
+  uint32_t code;
+  uint32_t sc = nvfp4_row_quantize(lo, ts, code);
+  nvfp4_row_store(slab, off, a, n, code, sc, hd.kind == 2, valid);
+  sc = nvfp4_row_quantize(hi, ts, code);
+  nvfp4_row_store(slab, off, 4 + a, n, code, sc, hd.kind == 2, valid);
 }
 
 // U k-steps of loads, then their products (all loads issue before the first product waits).
@@ -61,11 +130,12 @@ __device__ __forceinline__ void qkv_ksteps(const uint16_t* const (&wp)[2], const
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[u][mt], bw[u][nt], acc[mt][nt], 0, 0, 0);
 }
 
-// MT: 16-token tiles per workgroup -- 4 (64 tokens) for a prompt chunk, 1
-// for a decode step's few rows: a workgroup per (head, 16 rows) puts more CUs
-// on the weight stream (each CU sustains only part of it) and leaves each
-// wave one token of the epilogue; the extra weight reads of the other token
-// tiles hit the caches.
+// Calls of at most 64 rows (a decode step's new rows).  MT: 16-token tiles
+// per workgroup, launched with 1: a workgroup per (head, 16 rows) puts more
+// CUs on the weight stream (each CU sustains only part of it) than one per
+// (head, 64 rows), and leaves each wave one token of the epilogue; the other
+// token tiles' weight reads hit the caches.  Larger calls go to
+// qkv_insert_tiled_kernel.
 template <int MT>
 __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
   constexpr int kTok = 16 * MT;
@@ -113,57 +183,103 @@ __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
     __syncthreads();
   }
   // ---- epilogue, one token per wave at a time
-  // head kinds: 0 query, 1 key, 2 value, 3 index query, 4 index key
-  const int kind = head < 32 ? 0 : head < 36 ? 1 : head < 40 ? 2 : head < 44 ? 3 : 4;
-  const int sub = kind == 0 ? head : kind == 1 ? head - 32 : kind == 2 ? head - 36 : kind == 3 ? head - 40 : 0;
-  const int gsel = kind == 0 ? 0 : kind == 1 ? 1 : kind == 3 ? 2 : 3;  // norm weight row
-  float g_lo = 0.f, g_hi = 0.f;
-  if (kind != 2) {
-    g_lo = A.norm_weight[gsel * kDim + lane];
-    g_hi = A.norm_weight[gsel * kDim + 64 + lane];
-  }
+  const QkvHead hd = qkv_head(A, head, lane);
   for (int r = 0; r < MT; ++r) {
     const int tl = wave * MT + r;
-    const int tok = t0 + tl;
-    if (tok >= A.n) break;
-    const int p = A.pos[tok];
-    if (p < 0 || p >= A.rope_rows) continue;  // no rotation for this token: nothing of it is written
-    float lo = tile[tl][lane], hi = tile[tl][64 + lane];
-    if (kind != 2) {
-      // RMS norm: sum of squares over the head's 128 values (every lane gets it)
-      float ss = lo * lo + hi * hi;
+    if (t0 + tl >= A.n) break;
+    qkv_epilogue_token(A, hd, t0 + tl, tile[tl][lane], tile[tl][64 + lane], lane);
+  }
+}
+
+// Prompt chunks (more than 64 rows): one workgroup of 4 waves per (head, 128
+// tokens), a GEMM from LDS-staged operand blocks of 64 k, double-buffered.
+// Per block each thread moves 16 bytes of 4 x rows and 4 weight rows with
+// coalesced loads (a weight block pair is one contiguous 16 KB in the packed
+// layout); each wave then multiplies its 64 x 64 quarter from LDS, 16 MFMAs
+// per 32 k.  Operands are read from HBM or the caches once per workgroup
+// instead of once per wave.  The FP32 result tile reuses the staging memory.
+constexpr int kTT = 128;          // tokens per workgroup
+constexpr int kBK = 64;           // k per staged block
+constexpr int kLdsRow = kBK + 8;  // bf16 per staged row: 16 bytes of padding against bank conflicts
+
+__global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
+  __shared__ __align__(16) uint8_t lds[2 * 2 * kTT * kLdsRow * 2];  // 73,728 B
+  typedef uint16_t Stage[kTT][kLdsRow];
+  Stage* sA = reinterpret_cast<Stage*>(lds);  // [2 stages] hidden states
+  Stage* sB = reinterpret_cast<Stage*>(lds + 2 * sizeof(Stage));  // [2 stages] weights
+  float(*tile)[kDim + 4] = reinterpret_cast<float(*)[kDim + 4]>(lds);  // after the GEMM: 67,584 B
+  const int head = blockIdx.x, t0 = blockIdx.y * kTT;  // heads fastest: in-flight workgroups share token tiles
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, a = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;  // this wave's quarter: tokens 64 wm.., columns 64 wn..
+  const int lr = tid >> 3, lc = tid & 7;    // staging: rows lr + 32 i, 16-byte chunk lc
+  const uint16_t* xg[4];
+  const uint16_t* wg[4];
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-      const float inv = 1.0f / sqrtf(ss / (float)kDim + A.eps);
-      const float ylo = lo * inv * g_lo, yhi = hi * inv * g_hi;
-      const float c = A.rope[(int64_t)p * kDim + lane], s = A.rope[(int64_t)p * kDim + 64 + lane];
-      lo = ylo * c - yhi * s;
-      hi = yhi * c + ylo * s;
+  for (int i = 0; i < 4; ++i) {
+    const int row = lr + 32 * i;
+    xg[i] = A.x + (int64_t)min(t0 + row, A.n - 1) * A.hidden + 8 * lc;
+    wg[i] = A.w + (((int64_t)head * (A.hidden / 32) + (lc >> 2)) * kDim + row) * 32 + 8 * (lc & 3);
+  }
+  uint4 rx[4], rw[4];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rx[i] = *reinterpret_cast<const uint4*>(xg[i] + kb * kBK);
+      rw[i] = *reinterpret_cast<const uint4*>(wg[i] + (int64_t)kb * 2 * kDim * 32);
     }
-    if (A.pre) {
-      float* pr = A.pre + ((int64_t)tok * MSA_QKV_HEADS + head) * kDim;
-      pr[lane] = lo;
-      pr[64 + lane] = hi;
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(&sA[st][lr + 32 * i][8 * lc]) = rx[i];
+      *reinterpret_cast<uint4*>(&sB[st][lr + 32 * i][8 * lc]) = rw[i];
     }
-    if (kind == 0 || kind == 3) {
-      uint8_t* q = kind == 0 ? A.q_out + ((int64_t)tok * 32 + sub) * kDim : A.qidx_out + ((int64_t)tok * 4 + sub) * kDim;
-      q[lane] = (uint8_t)e4m3_encode(lo / A.q_scale);
-      q[64 + lane] = (uint8_t)e4m3_encode(hi / A.q_scale);
-      continue;
+  };
+  v4f acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int nkb = A.hidden / kBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nkb) gload(kb + 1);  // lands in registers while this block is multiplied
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf8 fa[4], fb[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        fa[mt] = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(&sA[cur][64 * wm + 16 * mt + n][32 * ks + 8 * a]));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        fb[nt] = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(&sB[cur][64 * wn + 16 * nt + n][32 * ks + 8 * a]));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
     }
-    uint8_t* pages = kind == 1 ? A.kpages : kind == 2 ? A.vpages : A.ipages;
-    const int np = kind == 1 ? A.knp : kind == 2 ? A.vnp : A.inp;
-    const int heads = kind == 4 ? 1 : kGroups;
-    const float ts = kind == 1 ? A.kts : kind == 2 ? A.vts : A.its;
-    const int64_t slot = A.slots[tok];
-    const bool valid = slot >= 0 && slot < (int64_t)np * kPage;
-    uint8_t* slab = pages + ((valid ? slot >> 7 : 0) * heads + sub) * (int64_t)kNvSlab;
-    const int off = (int)(slot & (kPage - 1));
-    uint32_t code;
-    uint32_t sc = nvfp4_row_quantize(lo, ts, code);
-    nvfp4_row_store(slab, off, a, n, code, sc, kind == 2, valid);
-    sc = nvfp4_row_quantize(hi, ts, code);
-    nvfp4_row_store(slab, off, 4 + a, n, code, sc, kind == 2, valid);
+    // the other stage was last read before the previous barrier
+    if (kb + 1 < nkb) lstore(cur ^ 1);
+    __syncthreads();
+  }
+  // every wave is past its last staging read: the result tile may overwrite the stages
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tile[64 * wm + 16 * mt + 4 * a + i][64 * wn + 16 * nt + n] = acc[mt][nt][i];
+  __syncthreads();
+  const QkvHead hd = qkv_head(A, head, lane);
+  for (int r = 0; r < kTT / 4; ++r) {
+    const int tl = wave * (kTT / 4) + r;
+    if (t0 + tl >= A.n) break;
+    qkv_epilogue_token(A, hd, t0 + tl, tile[tl][lane], tile[tl][64 + lane], lane);
   }
 }
 
@@ -177,7 +293,7 @@ extern "C" int msa_launch_qkv_insert(const QkvArgs* args, hipStream_t stream) {
     hipLaunchKernelGGL(qkv_insert_kernel<1>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 15) / 16)), dim3(1024), 0,
                        stream, *args);
   else
-    hipLaunchKernelGGL(qkv_insert_kernel<4>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 63) / 64)), dim3(1024), 0,
-                       stream, *args);
+    hipLaunchKernelGGL(qkv_insert_tiled_kernel, dim3(MSA_QKV_HEADS, (unsigned)((args->n + kTT - 1) / kTT)), dim3(256),
+                       0, stream, *args);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
