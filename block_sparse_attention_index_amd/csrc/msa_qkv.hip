@@ -130,22 +130,23 @@ __device__ __forceinline__ void qkv_ksteps(const uint16_t* const (&wp)[2], const
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[u][mt], bw[u][nt], acc[mt][nt], 0, 0, 0);
 }
 
-// Calls of at most 64 rows (a decode step's new rows).  MT: 16-token tiles
-// per workgroup, launched with 1: a workgroup per (head, 16 rows) puts more
-// CUs on the weight stream (each CU sustains only part of it) than one per
-// (head, 64 rows), and leaves each wave one token of the epilogue; the other
-// token tiles' weight reads hit the caches.  Larger calls go to
-// qkv_insert_tiled_kernel.
-template <int MT>
+// Calls of at most 64 rows (a decode step's new rows): a workgroup per
+// (head, ROWS rows), ROWS = 8 or 16 of the 16-row matrix tile (the padding
+// rows repeat a real row and are not stored).  Small workgroups put more CUs
+// on the weight stream, which each CU sustains only in part; the other
+// workgroups' reads of the same weights hit the caches.  A 32-row call: 64
+// rows per workgroup 44.1 us, 16 rows 29.5 us, 8 rows 25.7 us.  Larger calls
+// go to qkv_insert_tiled_kernel.
+template <int ROWS>
 __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
-  constexpr int kTok = 16 * MT;
-  __shared__ float tile[kTok][kDim + 4];
+  constexpr int MT = 1;  // one 16-row matrix tile
+  __shared__ float tile[16][kDim + 4];
   const int head = blockIdx.x;  // heads fastest: the workgroups in flight share a few token tiles
-  const int t0 = blockIdx.y * kTok;
+  const int t0 = blockIdx.y * ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, a = lane >> 4;
   const int cg = wave & 3, kq = wave >> 2;
-  const int mts = min(MT, (A.n - t0 + 15) / 16);  // token tiles of 16 holding real tokens (uniform)
+  const int mts = 1;
 
   // ---- GEMM: acc[mt][nt][i] = out[t0 + 16 mt + 4a + i][32 cg + 16 nt + n] over this wave's k quarter
   v4f acc[MT][2];
@@ -162,8 +163,8 @@ __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
     wp[nt] = A.w + ((int64_t)head * A.hidden + (kb - 8 * a)) * kDim + (32 * cg + 16 * nt + n) * 32 + 8 * a;
   const uint16_t* xp[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xp[mt] = A.x + (int64_t)min(t0 + 16 * mt + n, A.n - 1) * A.hidden + kb;
-  constexpr int U = MT == 1 ? 8 : 2;
+  for (int mt = 0; mt < MT; ++mt) xp[mt] = A.x + (int64_t)min(t0 + min(n, ROWS - 1), A.n - 1) * A.hidden + kb;
+  constexpr int U = 8;
   int k = 0;
   for (; k + 32 * U <= kl; k += 32 * U) qkv_ksteps<MT, U>(wp, xp, k, mts, acc);
   for (; k < kl; k += 64) qkv_ksteps<MT, 2>(wp, xp, k, mts, acc);
@@ -184,11 +185,7 @@ __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
   }
   // ---- epilogue, one token per wave at a time
   const QkvHead hd = qkv_head(A, head, lane);
-  for (int r = 0; r < MT; ++r) {
-    const int tl = wave * MT + r;
-    if (t0 + tl >= A.n) break;
-    qkv_epilogue_token(A, hd, t0 + tl, tile[tl][lane], tile[tl][64 + lane], lane);
-  }
+  if (wave < ROWS && t0 + wave < A.n) qkv_epilogue_token(A, hd, t0 + wave, tile[wave][lane], tile[wave][64 + lane], lane);
 }
 
 // Prompt chunks (more than 64 rows): one workgroup of 4 waves per (head, 128
@@ -289,8 +286,11 @@ using namespace msa;
 
 extern "C" int msa_launch_qkv_insert(const QkvArgs* args, hipStream_t stream) {
   if (args->n == 0) return 0;
-  if (args->n <= 64)
-    hipLaunchKernelGGL(qkv_insert_kernel<1>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 15) / 16)), dim3(1024), 0,
+  if (args->n <= 32)
+    hipLaunchKernelGGL(qkv_insert_kernel<8>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 7) / 8)), dim3(1024), 0,
+                       stream, *args);
+  else if (args->n <= 64)
+    hipLaunchKernelGGL(qkv_insert_kernel<16>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 15) / 16)), dim3(1024), 0,
                        stream, *args);
   else
     hipLaunchKernelGGL(qkv_insert_tiled_kernel, dim3(MSA_QKV_HEADS, (unsigned)((args->n + kTT - 1) / kTT)), dim3(256),
