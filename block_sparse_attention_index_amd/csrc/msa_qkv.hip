@@ -218,33 +218,34 @@ __global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
     xg[i] = A.x + (int64_t)min(t0 + row, A.n - 1) * A.hidden + 8 * lc;
     wg[i] = A.w + (((int64_t)head * (A.hidden / 32) + (lc >> 2)) * kDim + row) * 32 + 8 * (lc & 3);
   }
-  uint4 rx[4], rw[4];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rx[i] = *reinterpret_cast<const uint4*>(xg[i] + kb * kBK);
-      rw[i] = *reinterpret_cast<const uint4*>(wg[i] + (int64_t)kb * 2 * kDim * 32);
-    }
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&sA[st][lr + 32 * i][8 * lc]) = rx[i];
-      *reinterpret_cast<uint4*>(&sB[st][lr + 32 * i][8 * lc]) = rw[i];
-    }
-  };
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 rx[4], rw[4];
   v4f acc[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nkb = A.hidden / kBK;
-  gload(0);
-  lstore(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rx[i] = *reinterpret_cast<const u32x4*>(xg[i]);
+    rw[i] = *reinterpret_cast<const u32x4*>(wg[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<u32x4*>(&sA[0][lr + 32 * i][8 * lc]) = rx[i];
+    *reinterpret_cast<u32x4*>(&sB[0][lr + 32 * i][8 * lc]) = rw[i];
+  }
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);  // lands in registers while this block is multiplied
+    if (kb + 1 < nkb) {  // the next block lands in registers while this one is multiplied
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rx[i] = *reinterpret_cast<const u32x4*>(xg[i] + (kb + 1) * kBK);
+        rw[i] = *reinterpret_cast<const u32x4*>(wg[i] + (int64_t)(kb + 1) * 2 * kDim * 32);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf8 fa[4], fb[4];
@@ -261,7 +262,13 @@ __global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
     }
     // the other stage was last read before the previous barrier
-    if (kb + 1 < nkb) lstore(cur ^ 1);
+    if (kb + 1 < nkb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<u32x4*>(&sA[cur ^ 1][lr + 32 * i][8 * lc]) = rx[i];
+        *reinterpret_cast<u32x4*>(&sB[cur ^ 1][lr + 32 * i][8 * lc]) = rw[i];
+      }
+    }
     __syncthreads();
   }
   // every wave is past its last staging read: the result tile may overwrite the stages
