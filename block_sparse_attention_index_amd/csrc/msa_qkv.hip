@@ -188,38 +188,51 @@ __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
   if (wave < ROWS && t0 + wave < A.n) qkv_epilogue_token(A, hd, t0 + wave, tile[wave][lane], tile[wave][64 + lane], lane);
 }
 
-// Prompt chunks (more than 64 rows): one workgroup of 4 waves per (head, 128
-// tokens), a GEMM from LDS-staged operand blocks of 64 k, double-buffered.
-// Per block each thread moves 16 bytes of 4 x rows and 4 weight rows with
-// coalesced loads (a weight block pair is one contiguous 16 KB in the packed
-// layout); each wave then multiplies its 64 x 64 quarter from LDS, 16 MFMAs
-// per 32 k.  Operands are read from HBM or the caches once per workgroup
-// instead of once per wave.  The FP32 result tile reuses the staging memory.
-constexpr int kTT = 128;          // tokens per workgroup
+// Prompt chunks (more than 64 rows): one workgroup per (head, TT tokens), TT
+// = 128 (4 waves) or 256 (8 waves), a GEMM from LDS-staged operand blocks of
+// 64 k, double-buffered.  Per block each thread moves 16-byte chunks of the
+// hidden-state and weight rows with coalesced loads (a weight block pair is
+// one contiguous 16 KB in the packed layout); each wave then multiplies a 64
+// x 64 part from LDS, 16 MFMAs per 32 k.  Operands are read from HBM or the
+// caches once per workgroup instead of once per wave.  The FP32 result tile
+// reuses the staging memory.  Launched with 128: 256 tokens (each staged
+// weight block serving twice the rows, one workgroup per CU) measured slower
+// for an 8,192-row chunk (599 against 557 us).
 constexpr int kBK = 64;           // k per staged block
 constexpr int kLdsRow = kBK + 8;  // bf16 per staged row: 16 bytes of padding against bank conflicts
 
-__global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
-  __shared__ __align__(16) uint8_t lds[2 * 2 * kTT * kLdsRow * 2];  // 73,728 B
-  typedef uint16_t Stage[kTT][kLdsRow];
-  Stage* sA = reinterpret_cast<Stage*>(lds);  // [2 stages] hidden states
-  Stage* sB = reinterpret_cast<Stage*>(lds + 2 * sizeof(Stage));  // [2 stages] weights
-  float(*tile)[kDim + 4] = reinterpret_cast<float(*)[kDim + 4]>(lds);  // after the GEMM: 67,584 B
-  const int head = blockIdx.x, t0 = blockIdx.y * kTT;  // heads fastest: in-flight workgroups share token tiles
+template <int TT>
+__global__ __launch_bounds__(TT * 2) void qkv_insert_tiled_kernel(QkvArgs A) {
+  constexpr int NT = TT * 2;                  // threads: TT / 32 waves
+  constexpr int kStageA = TT * kLdsRow * 2;   // bytes of one hidden-state stage
+  constexpr int kStageB = kDim * kLdsRow * 2; // bytes of one weight stage
+  constexpr int kStages = 2 * (kStageA + kStageB);
+  constexpr int kTile = TT * (kDim + 4) * 4;  // the FP32 result tile
+  constexpr int AX = TT * 8 / NT;             // 16-byte hidden-state chunks per thread per block: 4
+  constexpr int BX = kDim * 8 / NT;           // weight chunks per thread per block: 4 or 2
+  __shared__ __align__(16) uint8_t lds[kStages > kTile ? kStages : kTile];
+  typedef uint16_t RowA[TT][kLdsRow];
+  typedef uint16_t RowB[kDim][kLdsRow];
+  RowA* sA = reinterpret_cast<RowA*>(lds);                // [2 stages] hidden states
+  RowB* sB = reinterpret_cast<RowB*>(lds + 2 * kStageA);  // [2 stages] weights
+  float(*tile)[kDim + 4] = reinterpret_cast<float(*)[kDim + 4]>(lds);
+  const int head = blockIdx.x, t0 = blockIdx.y * TT;  // heads fastest: in-flight workgroups share token tiles
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, a = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;  // this wave's quarter: tokens 64 wm.., columns 64 wn..
-  const int lr = tid >> 3, lc = tid & 7;    // staging: rows lr + 32 i, 16-byte chunk lc
-  const uint16_t* xg[4];
-  const uint16_t* wg[4];
+  constexpr int WM = TT / 64;                  // waves along the tokens
+  const int wm = wave % WM, wn = wave / WM;    // this wave's part: tokens 64 wm.., columns 64 wn..
+  const int lr = tid >> 3, lc = tid & 7;       // staging: rows lr + (NT / 8) i, 16-byte chunk lc
+  static_assert(AX == 4, "four hidden-state chunks per thread");
+  const uint16_t* xg[AX];
+  const uint16_t* wg[BX];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = lr + 32 * i;
-    xg[i] = A.x + (int64_t)min(t0 + row, A.n - 1) * A.hidden + 8 * lc;
-    wg[i] = A.w + (((int64_t)head * (A.hidden / 32) + (lc >> 2)) * kDim + row) * 32 + 8 * (lc & 3);
-  }
+  for (int i = 0; i < AX; ++i)
+    xg[i] = A.x + (int64_t)min(t0 + lr + (NT / 8) * i, A.n - 1) * A.hidden + 8 * lc;
+#pragma unroll
+  for (int i = 0; i < BX; ++i)
+    wg[i] = A.w + (((int64_t)head * (A.hidden / 32) + (lc >> 2)) * kDim + lr + (NT / 8) * i) * 32 + 8 * (lc & 3);
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 rx[4], rw[4];
+  u32x4 rx[AX], rw[BX];
   v4f acc[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -227,34 +240,32 @@ __global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nkb = A.hidden / kBK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rx[i] = *reinterpret_cast<const u32x4*>(xg[i]);
-    rw[i] = *reinterpret_cast<const u32x4*>(wg[i]);
-  }
+  for (int i = 0; i < AX; ++i) rx[i] = *reinterpret_cast<const u32x4*>(xg[i]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4*>(&sA[0][lr + 32 * i][8 * lc]) = rx[i];
-    *reinterpret_cast<u32x4*>(&sB[0][lr + 32 * i][8 * lc]) = rw[i];
-  }
+  for (int i = 0; i < BX; ++i) rw[i] = *reinterpret_cast<const u32x4*>(wg[i]);
+#pragma unroll
+  for (int i = 0; i < AX; ++i) *reinterpret_cast<u32x4*>(&sA[0][lr + (NT / 8) * i][8 * lc]) = rx[i];
+#pragma unroll
+  for (int i = 0; i < BX; ++i) *reinterpret_cast<u32x4*>(&sB[0][lr + (NT / 8) * i][8 * lc]) = rw[i];
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
     if (kb + 1 < nkb) {  // the next block lands in registers while this one is multiplied
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rx[i] = *reinterpret_cast<const u32x4*>(xg[i] + (kb + 1) * kBK);
+      for (int i = 0; i < AX; ++i) rx[i] = *reinterpret_cast<const u32x4*>(xg[i] + (kb + 1) * kBK);
+#pragma unroll
+      for (int i = 0; i < BX; ++i)
         rw[i] = *reinterpret_cast<const u32x4*>(wg[i] + (int64_t)(kb + 1) * 2 * kDim * 32);
-      }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf8 fa[4], fb[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        fa[mt] = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(&sA[cur][64 * wm + 16 * mt + n][32 * ks + 8 * a]));
+        fa[mt] = __builtin_bit_cast(bf8, *reinterpret_cast<const u32x4*>(&sA[cur][64 * wm + 16 * mt + n][32 * ks + 8 * a]));
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        fb[nt] = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(&sB[cur][64 * wn + 16 * nt + n][32 * ks + 8 * a]));
+        fb[nt] = __builtin_bit_cast(bf8, *reinterpret_cast<const u32x4*>(&sB[cur][64 * wn + 16 * nt + n][32 * ks + 8 * a]));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -264,10 +275,9 @@ __global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
     // the other stage was last read before the previous barrier
     if (kb + 1 < nkb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4*>(&sA[cur ^ 1][lr + 32 * i][8 * lc]) = rx[i];
-        *reinterpret_cast<u32x4*>(&sB[cur ^ 1][lr + 32 * i][8 * lc]) = rw[i];
-      }
+      for (int i = 0; i < AX; ++i) *reinterpret_cast<u32x4*>(&sA[cur ^ 1][lr + (NT / 8) * i][8 * lc]) = rx[i];
+#pragma unroll
+      for (int i = 0; i < BX; ++i) *reinterpret_cast<u32x4*>(&sB[cur ^ 1][lr + (NT / 8) * i][8 * lc]) = rw[i];
     }
     __syncthreads();
   }
@@ -280,8 +290,8 @@ __global__ __launch_bounds__(256) void qkv_insert_tiled_kernel(QkvArgs A) {
       for (int i = 0; i < 4; ++i) tile[64 * wm + 16 * mt + 4 * a + i][64 * wn + 16 * nt + n] = acc[mt][nt][i];
   __syncthreads();
   const QkvHead hd = qkv_head(A, head, lane);
-  for (int r = 0; r < kTT / 4; ++r) {
-    const int tl = wave * (kTT / 4) + r;
+  for (int r = 0; r < 32; ++r) {  // TT / 32 waves x 32 tokens
+    const int tl = wave * 32 + r;
     if (t0 + tl >= A.n) break;
     qkv_epilogue_token(A, hd, t0 + tl, tile[tl][lane], tile[tl][64 + lane], lane);
   }
@@ -300,7 +310,7 @@ extern "C" int msa_launch_qkv_insert(const QkvArgs* args, hipStream_t stream) {
     hipLaunchKernelGGL(qkv_insert_kernel<16>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 15) / 16)), dim3(1024), 0,
                        stream, *args);
   else
-    hipLaunchKernelGGL(qkv_insert_tiled_kernel, dim3(MSA_QKV_HEADS, (unsigned)((args->n + kTT - 1) / kTT)), dim3(256),
-                       0, stream, *args);
+    hipLaunchKernelGGL(qkv_insert_tiled_kernel<128>, dim3(MSA_QKV_HEADS, (unsigned)((args->n + 127) / 128)),
+                       dim3(256), 0, stream, *args);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
