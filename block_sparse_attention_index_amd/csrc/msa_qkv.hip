@@ -14,9 +14,9 @@
 //
 // Output columns: 45 heads of 128 -- 32 query heads, 4 key heads, 4 value
 // heads, 4 index queries (one per group), 1 index key.  A call of at most 64
-// rows runs qkv_insert_kernel, one workgroup of 16 waves per (head, 16 rows);
-// a prompt chunk runs qkv_insert_tiled_kernel (LDS-staged, below).  In the
-// first:
+// rows runs qkv_insert_kernel, one workgroup of 16 waves per (head, 8 or 16
+// rows); a prompt chunk runs qkv_insert_tiled_kernel (LDS-staged, below).  In
+// the first:
 //  * GEMM on v_mfma_f32_16x16x32_bf16.  Each lane's operand is 8 consecutive
 //    k of one row: one 16-byte load.  x [n][hidden] is row-major; the weights
 //    come in 32-k blocks, w[head][k/32][row][k%32], so a wave's operand for 16
@@ -25,9 +25,9 @@
 //    apart, and the stream ran at about 1 TB/s).  Wave w takes 32 columns
 //    (w % 4) over a quarter of the hidden dimension (w / 4); the quarters are
 //    summed through one LDS tile in four rounds.
-//  * Epilogue: each wave takes 1/16 of the tokens; lane l holds dims l and
-//    l + 64, which is both a rotary pair and, per 16-lane row, two NVFP4
-//    groups (the insert's row quantiser and store).
+//  * Epilogue (both kernels): a wave takes one token of the head at a time;
+//    lane l holds dims l and l + 64, which is both a rotary pair and, per
+//    16-lane row, two NVFP4 groups (the insert's row quantiser and store).
 #include "msa_device.h"
 #include "msa_kernels.h"
 
