@@ -174,3 +174,48 @@ def test_qkv_prefill_chunk_sampled(M):
     got = run_gpu(M, q)
     rows = np.random.default_rng(1).choice(2048, 12, replace=False)
     check_against_oracle(q, got, tokens=rows)
+
+
+@pytest.mark.parametrize("n,hidden", [(32, 1024), (300, 512)])
+def test_qkv_graph_replay_matches_eager(M, n, hidden):
+    """Captured in a HIP graph and replayed three times (eager work and synchronisations in
+    between, caches cleared by a fill kernel before each replay): every replay writes the
+    bytes of the eager call."""
+    q = W.make_qkv_inputs(40 + n, n, hidden, max_pos=4000, bad_positions=1, bad_slots=1)
+    q.num_pages = max(q.num_pages, 4)
+    print(f"[case] qkv graph n={n} hidden={hidden}", flush=True)
+    x = _dev(q.x.view(np.int16))
+    w = _dev(W.pack_qkv_weights(q.w).view(np.int16))
+    g, rope, pos, slots = _dev(q.norm_weight), _dev(q.rope), _dev(q.positions), _dev(q.slots)
+    kc = M.Cache.empty(M.MSA_NVFP4, M.MSA_TOKEN_MAJOR, 4, q.num_pages, q.tensor_scale)
+    vc = M.Cache.empty(M.MSA_NVFP4, M.MSA_DIM_MAJOR, 4, q.num_pages, q.tensor_scale)
+    ic = M.Cache.empty(M.MSA_NVFP4, M.MSA_TOKEN_MAJOR, 1, q.num_pages, q.tensor_scale)
+    q_out = torch.zeros((n, 32, 128), dtype=torch.uint8, device="cuda")
+    qi_out = torch.zeros((n, 4, 128), dtype=torch.uint8, device="cuda")
+    outs = (q_out, qi_out, kc.pages, vc.pages, ic.pages)
+
+    def call(stream=None):
+        M.msa_qkv_project_insert(x, w, g, q.eps, rope, pos, slots, q.q_scale, q_out, qi_out, kc, vc, ic,
+                                 stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for t in outs:
+            t.zero_()
+        call(stream)  # warm-up on the capture stream
+        stream.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            call(stream)
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = (x.float() * 2).sum().item()  # eager work between replays
