@@ -199,7 +199,8 @@ __global__ __launch_bounds__(1024) void qkv_insert_kernel(QkvArgs A) {
 // weight block serving twice the rows, one workgroup per CU) measured slower
 // for an 8,192-row chunk (599 against 557 us).
 constexpr int kBK = 64;           // k per staged block
-constexpr int kLdsRow = kBK + 8;  // bf16 per staged row: 16 bytes of padding against bank conflicts
+constexpr int kLdsRow = kBK + 16;  // bf16 per staged row: 32 bytes of padding against bank conflicts
+                                   // (16 bytes: 1.6% slower; 48: two workgroups no longer fit a CU's LDS)
 
 template <int TT>
 __global__ __launch_bounds__(TT * 2) void qkv_insert_tiled_kernel(QkvArgs A) {
