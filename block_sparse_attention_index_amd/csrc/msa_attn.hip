@@ -415,7 +415,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
   __shared__ float s_inv[NQ];         // v_scale / denominator per query row
   __shared__ ScaleSlot s_slot[FP8 ? 1 : WAVES];  // NVFP4: scales of each wave's current block
   __shared__ SelectScratch s_sel[SELECT ? RPW : 1];  // selection scratch of waves 0..nr-1
-  __shared__ float s_o[WAVES][NQ / 2][kDim];  // each wave's rescaled output rows (half the columns at a time)
+  // each wave's rescaled output rows (half the rows at a time); rows padded by 4 floats so that
+  // the 4-row stride of a wave's stores spreads over the banks instead of hitting the same 16
+  __shared__ __align__(16) float s_o[WAVES][NQ / 2][kDim + 4];
 
   const int RG = (R + RPW - 1) / RPW;
   const int g = blockIdx.x / RG, rg = blockIdx.x % RG;
