@@ -55,7 +55,7 @@ def _load() -> C.CDLL:
         "msa_quantize_e4m3": (C.c_int, [vp, i64, f32, vp, vp]),
         "msa_index_score": (C.c_int, [P(msa_batch), vp, i32, f32, P(msa_cache), vp, vp, vp]),
         "msa_block_maxpool_topk": (C.c_int, [P(msa_batch), vp, i32, i32, vp, vp, vp]),
-        "msa_decode_workspace_bytes": (sz, [P(msa_batch), i32]),
+        "msa_workspace_bytes": (sz, [P(msa_batch), i32]),
         "msa_sparse_decode": (C.c_int, [P(msa_batch), vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp, vp, i32,
                                         vp, vp, sz, vp]),
         "msa_select_decode": (C.c_int, [P(msa_batch), vp, i32, vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp,
@@ -209,8 +209,8 @@ def msa_block_maxpool_topk(batch: Batch, scores, scores_are_token_level: int, to
                                       _ptr(sel_blocks), _ptr(sel_count), _stream(stream)), "msa_block_maxpool_topk")
 
 
-def msa_decode_workspace_bytes(batch: Batch, topk: int) -> int:
-    return int(lib.msa_decode_workspace_bytes(batch.ref(), int(topk)))
+def msa_workspace_bytes(batch: Batch, topk: int) -> int:
+    return int(lib.msa_workspace_bytes(batch.ref(), int(topk)))
 
 
 def msa_sparse_decode(batch: Batch, q, q_dtype: int, q_scale: float, sm_scale: float, k_cache: Cache,

@@ -139,7 +139,7 @@ int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t 
              : MSA_ERR_HIP;
 }
 
-size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk) {
+size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk) {
   if (check_batch(batch, MSA_MAX_PREFILL_ROWS) != MSA_OK || topk < 1 || topk > MSA_MAX_TOPK) return 0;
   return msa_decode_partials_bytes(batch, topk);
 }
@@ -158,7 +158,7 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
   if ((st = query_dtype_ok(q_dtype, k_cache)) != MSA_OK) return st;
   if (!finite_pos(sm_scale) || (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale))) return MSA_ERR_INVALID_ARG;
-  if (workspace_bytes < msa_decode_workspace_bytes(batch, topk)) return MSA_ERR_WORKSPACE;
+  if (workspace_bytes < msa_workspace_bytes(batch, topk)) return MSA_ERR_WORKSPACE;
   return msa_launch_sparse_decode(batch, q, q_dtype, q_scale, sm_scale, k_cache, v_cache, sel_blocks, sel_count,
                                   topk, out, workspace, stream) == 0
              ? MSA_OK

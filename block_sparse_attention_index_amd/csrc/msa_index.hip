@@ -29,41 +29,24 @@ namespace msa {
 
 // One page of the index cache as one wave holds it: lane l keeps, for each
 // 16-token chunk c, the 16 code bytes of token 16c + l%16, dims
-// 32*(l/16)..+31 (the fp4 operand), and the 8 scale bytes of that token.
-// With WIDE scale loads the 1 KB of scales arrives as one 16-byte load per
-// lane (tokens 2l, 2l+1) and is redistributed through a 1 KB LDS slot of the
-// wave (stage_scales), instead of eight 8-byte loads per lane.
+// 32*(l/16)..+31 (the fp4 operand), and the 8 scale bytes of that token.  The
+// 1 KB of scales arrives as one 16-byte load per lane (tokens 2l, 2l+1) and
+// is redistributed through a 1 KB LDS slot of the wave (stage_scales),
+// instead of eight 8-byte loads per lane.  Every load carries the streaming
+// (non-temporal) hint: the index is read once per step.
 struct PageRegs {
   uint4 cw[8];
   uint2 sw[8];
   uint4 sraw;
 };
 
-// NT: non-temporal loads (the index is read once per step; streaming hint).
-template <bool NT, bool WIDE = false>
-__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ slab, int col, int grp,
-                                          int lane = 0) {
-  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ slab, int col, int grp, int lane) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const u4* cp = reinterpret_cast<const u4*>(slab + (16 * c + col) * 64 + 16 * grp);
-    const u4 cv = NT ? __builtin_nontemporal_load(cp) : *cp;
-    pr.cw[c] = make_uint4(cv.x, cv.y, cv.z, cv.w);
-    if (!WIDE) {
-      const u2* sp = reinterpret_cast<const u2*>(slab + kScaleOff + (16 * c + col) * 8);
-      const u2 sv = NT ? __builtin_nontemporal_load(sp) : *sp;
-      pr.sw[c] = make_uint2(sv.x, sv.y);
-    }
-  }
-  if (WIDE) {
-    const u4* sp = reinterpret_cast<const u4*>(slab + kScaleOff + 16 * lane);
-    const u4 sv = NT ? __builtin_nontemporal_load(sp) : *sp;
-    pr.sraw = make_uint4(sv.x, sv.y, sv.z, sv.w);
-  }
+  for (int c = 0; c < 8; ++c) pr.cw[c] = nt_load4(slab + (16 * c + col) * 64 + 16 * grp);
+  pr.sraw = nt_load4(slab + kScaleOff + 16 * lane);
 }
 
-// WIDE: every lane's 8 scale bytes per chunk from the wave's LDS slot.
+// Every lane's 8 scale bytes per chunk from the wave's LDS slot.
 __device__ __forceinline__ void stage_scales(PageRegs& pr, uint4* slot, int lane, int col) {
   slot[lane] = pr.sraw;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -90,14 +73,14 @@ __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
   return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
 }
 
-// The chunk of workgroup id (pages p0 + 4*PPW*chunk ..) and its request b,
+// The chunk of workgroup id (pages p0 + 4*chunk ..) and its request b,
 // with b's clamped length L and newest chunk.  Workgroups 0..B-1 take each
 // request's newest chunk.  Unpacked, workgroup B + b*(C-1) + i takes chunk i
 // of request b, skipping the newest (C chunks per table row; the chunks past
 // a context are empty).  Packed (COMPACT, B <= 64), workgroups B.. take only
 // the chunks below each newest one, request after request, from a prefix sum
 // of the B lengths held one per lane; false for the leftovers at the end.
-template <bool COMPACT, int PPW>
+template <bool COMPACT>
 __device__ __forceinline__ bool chunk_of(int id, int B, const int32_t* __restrict__ lens, int max_pages, int p0,
                                          int lane, int& b, int& L, int& latest, int& chunk) {
   if (COMPACT && id >= B) {
@@ -105,7 +88,7 @@ __device__ __forceinline__ bool chunk_of(int id, int B, const int32_t* __restric
     if (lane < B) {
       Ll = clamp_len(lens[lane], max_pages);
       const int np = (Ll + kPage - 1) / kPage;
-      nl = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
+      nl = np > p0 ? (np - 1 - p0) / 4 : 0;
     }
     const int incl = wave_incl_sum(nl, lane);
     const int k = id - B;
@@ -117,12 +100,12 @@ __device__ __forceinline__ bool chunk_of(int id, int B, const int32_t* __restric
     latest = __builtin_amdgcn_readlane(nl, b);
     return chunk >= 0 && chunk < latest;
   }
-  const int C = (max_pages - p0 + 4 * PPW - 1) / (4 * PPW);
+  const int C = (max_pages - p0 + 3) / 4;
   b = id < B ? id : (id - B) / max(C - 1, 1);
   const int i_rest = id < B ? 0 : (id - B) % max(C - 1, 1);
   L = clamp_len(lens[b], max_pages);  // id < B: a scalar load, first in the newest chunk's chain
   const int np = (L + kPage - 1) / kPage;
-  latest = np > p0 ? (np - 1 - p0) / (4 * PPW) : 0;
+  latest = np > p0 ? (np - 1 - p0) / 4 : 0;
   chunk = id < B ? latest : (i_rest < latest ? i_rest : i_rest + 1);
   return true;
 }
@@ -281,11 +264,10 @@ struct NewRows {
   float ts_k, ts_v, ts_i;
 };
 
-// Pages [j0, j0 + PPW) of request b per wave; with PREFETCH the next page's
-// loads are issued before the current page is scored (register double buffer).
-// The scan covers pages p0 .. max_pages-1 of every request (p0 > 0: the
-// leading pages are shared by all requests and scored once, by
-// prefix_index_kernel); chunk i is pages p0 + 4*PPW*i ...
+// Page p0 + 4*chunk + wave of request b per wave (one page per wave, four per
+// workgroup).  The scan covers pages p0 .. max_pages-1 of every request (p0 >
+// 0: the leading pages are shared by all requests and scored once, by
+// prefix_index_kernel).
 // One-dimensional grid of B x C workgroups (C = page chunks per request row of
 // the table past p0), mapped to chunks by chunk_of.  Workgroups 0..B-1 take
 // the chunk holding each request's newest tokens, so the chunks that insert
@@ -297,25 +279,22 @@ struct NewRows {
 // the new tokens that fall in its chunk into the caches (one 16-lane row per
 // 16-element group, as the insert kernel does) and makes them visible to its
 // own waves before any page is read.
-template <int R, bool kTok, int PPW, bool PREFETCH, bool NT = false, int WPE = 1, bool INSERT = false,
-          bool WIDE = false, bool F16 = false, bool COMPACT = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void index_nvfp4_kernel(const int32_t* __restrict__ table,
-                                                          const int32_t* __restrict__ lens, int32_t max_pages,
-                                                          const uint8_t* __restrict__ q_idx, float out_scale,
-                                                          const uint8_t* __restrict__ pages, int32_t num_pages,
-                                                          float* __restrict__ block_scores,
-                                                          float* __restrict__ token_scores, int32_t B,
-                                                          int32_t p0, NewRows NR) {
+// Occupancy target: 4 waves per SIMD (4-6 measured equal, 8 thrash).
+template <int R, bool kTok, bool INSERT = false, bool F16 = false, bool COMPACT = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_nvfp4_kernel(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages,
+    const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
+    float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t B, int32_t p0, NewRows NR) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int id = (int)blockIdx.x;
   int b, L, latest, chunk;
-  if (!chunk_of<COMPACT, PPW>(id, B, lens, max_pages, p0, lane, b, L, latest, chunk)) return;
+  if (!chunk_of<COMPACT>(id, B, lens, max_pages, p0, lane, b, L, latest, chunk)) return;
   const int npb = (L + kPage - 1) / kPage;
   if (INSERT) {
     // new tokens [max(L - R, 0), L) that lie in this chunk's token range
-    const int lo = (p0 + chunk * 4 * PPW) * kPage;
-    const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * PPW * kPage);
+    const int lo = (p0 + chunk * 4) * kPage;
+    const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * kPage);
     if (t0 < t1) {
       const int i = threadIdx.x & 15;
       const int nrow = (t1 - t0) * 72;  // 16-dim groups: 32 keys, 32 values, 8 index keys per token
@@ -363,24 +342,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   }
   auto fill_past = [&] {
-    if (COMPACT && id < B) fill_past_chunks<R>(block_scores, b, min(p0 + (latest + 1) * 4 * PPW, max_pages), max_pages);
+    if (COMPACT && id < B) fill_past_chunks<R>(block_scores, b, min(p0 + (latest + 1) * 4, max_pages), max_pages);
   };
-  const int j0 = p0 + (chunk * 4 + wave) * PPW;
-  if (j0 >= max_pages) {
+  const int j = p0 + chunk * 4 + wave;
+  if (j >= max_pages) {
     fill_past();
     return;
   }
-  const int j1 = min(j0 + PPW, max_pages);
   const int grp = lane >> 4;  // this lane's query group (output) and fp4 lane group
   const int col = lane & 15;  // token within a 16-token chunk
   const int64_t T = (int64_t)max_pages * kPage;
 
-  // physical pages of this wave, one per lane, then broadcast
-  int my_phys = -1;
-  if (lane < PPW && j0 + lane < npb) {
-    my_phys = table[(int64_t)b * max_pages + j0 + lane];
-    if (my_phys >= num_pages) my_phys = -1;
-  }
+  // this wave's physical page (-1: past the context or outside the pool)
+  int phys = j < npb ? table[(int64_t)b * max_pages + j] : -1;
+  if (phys >= num_pages) phys = -1;
 
   // A operands: queries of row r masked to one scale group per MFMA row
   // (FP16 form: 16 index queries per tile instead).
@@ -423,35 +398,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     finish(j, m);
   };
 
-  static_assert(!(WIDE && PREFETCH), "wide scale loads are staged per page: no prefetch");
-  __shared__ uint4 s_scales[WIDE ? 4 : 1][64];
-  PageRegs buf[PREFETCH ? 2 : 1];
-  int phys_cur = __shfl(my_phys, 0);
-  if (PREFETCH && phys_cur >= 0) load_page<NT>(buf[0], pages + (int64_t)phys_cur * kNvSlab, col, grp);
-#pragma unroll
-  for (int k = 0; k < PPW; ++k) {
-    const int j = j0 + k;
-    if (j >= j1) break;
-    PageRegs& cur = buf[PREFETCH ? (k & 1) : 0];
-    const int phys_next = (k + 1 < PPW) ? __shfl(my_phys, k + 1) : -1;
-    if (!PREFETCH && phys_cur >= 0) {
-      load_page<NT, WIDE>(cur, pages + (int64_t)phys_cur * kNvSlab, col, grp, lane);
-      if (WIDE) stage_scales(cur, &s_scales[WIDE ? wave : 0][0], lane, col);
-    }
-    if (PREFETCH && phys_next >= 0 && j + 1 < j1)
-      load_page<NT>(buf[(k + 1) & 1], pages + (int64_t)phys_next * kNvSlab, col, grp);
-    if (phys_cur >= 0) {
-      if constexpr (F16) {
-        score_page_f16<R, kTok>(cur, Qh, L, j, b, lane, max_pages, out_scale, T, block_scores, token_scores);
-      } else {
-        float m[R];
-        score_page<R, kTok>(cur, A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
-        finish(j, m);
-      }
+  __shared__ uint4 s_scales[4][64];
+  if (phys >= 0) {
+    PageRegs pr;
+    load_page(pr, pages + (int64_t)phys * kNvSlab, col, grp, lane);
+    stage_scales(pr, &s_scales[wave][0], lane, col);
+    if constexpr (F16) {
+      score_page_f16<R, kTok>(pr, Qh, L, j, b, lane, max_pages, out_scale, T, block_scores, token_scores);
     } else {
-      empty_page(j);
+      float m[R];
+      score_page<R, kTok>(pr, A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
+      finish(j, m);
     }
-    phys_cur = phys_next;
+  } else {
+    empty_page(j);
   }
   fill_past();
 }
@@ -479,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int wave = threadIdx.x >> 6;
   const int id = (int)blockIdx.x;
   int b, L, latest, chunk;
-  if (!chunk_of<COMPACT, 1>(id, B, lens, max_pages, 0, lane, b, L, latest, chunk)) return;
+  if (!chunk_of<COMPACT>(id, B, lens, max_pages, 0, lane, b, L, latest, chunk)) return;
   const int npb = (L + kPage - 1) / kPage;
   if (INSERT) {
     // new tokens [max(L - R, 0), L) in this chunk: one thread per element
@@ -663,42 +623,28 @@ __global__ __launch_bounds__(128) void index_f32_kernel(const int32_t* __restric
     block_scores[((int64_t)b * R * kGroups + rg) * max_pages + j] = fmaxf(red[0][rg], red[1][rg]);
 }
 
-template <int R, int PPW, bool PREFETCH, bool NT, int WPE, bool INSERT, bool WIDE, bool F16 = false>
-static void launch_nvfp4_cfg(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
-                             float* ts, const NewRows& nr, hipStream_t s) {
-  const int p0 = ic->dtype == MSA_NVFP4 ? bt->shared_prefix_pages : 0;
-  const int chunks = (bt->max_pages_per_req - p0 + 4 * PPW - 1) / (4 * PPW);
-  if (chunks <= 0) return;  // every page is shared: the prefix kernel scored them all
-  const dim3 grid((unsigned)(chunks * bt->num_reqs));
-  if (ts)
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16>), grid, dim3(256), 0, s,
-                       bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
-  else if (bt->num_reqs <= 64)
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16, true>), grid, dim3(256),
-                       0, s, bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
-  else
-    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, PPW, PREFETCH, NT, WPE, INSERT, WIDE, F16>), grid, dim3(256), 0, s,
-                       bt->block_table, bt->ctx_lens, bt->max_pages_per_req, q, out_scale,
-                       (const uint8_t*)ic->pages, ic->num_pages, bs, ts, bt->num_reqs, p0, nr);
-}
-
-// One page per wave, non-temporal (streaming) loads, wide scale loads, and an
-// occupancy target of WPE waves per SIMD: measured best on the 128K-context
-// shapes (the streaming hint alone is worth ~12%, one 16-byte scale load per
-// lane instead of eight 8-byte ones ~4.5%; many short waves balance the
-// ragged contexts better than a deeper per-wave pipeline, and 4-6 waves per
-// SIMD are equal while 8 thrash).
 // Three rows or more: the FP16 form (the masked FP4 products grow with R and
 // bound the scan from R = 3 on).
 template <int R, bool INSERT>
 static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                          float* ts, const NewRows& nr, hipStream_t s) {
-  if constexpr (R <= 2)
-    launch_nvfp4_cfg<R, 1, false, true, 4, INSERT, true>(bt, q, out_scale, ic, bs, ts, nr, s);
+  constexpr bool F16 = R >= 3;
+  const int p0 = ic->dtype == MSA_NVFP4 ? bt->shared_prefix_pages : 0;
+  const int chunks = (bt->max_pages_per_req - p0 + 3) / 4;
+  if (chunks <= 0) return;  // every page is shared: the prefix kernel scored them all
+  const dim3 grid((unsigned)(chunks * bt->num_reqs));
+  if (ts)
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, true, INSERT, F16>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs,
+                       ts, bt->num_reqs, p0, nr);
+  else if (bt->num_reqs <= 64)
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, INSERT, F16, true>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs,
+                       ts, bt->num_reqs, p0, nr);
   else
-    launch_nvfp4_cfg<R, 1, false, true, 4, INSERT, true, true>(bt, q, out_scale, ic, bs, ts, nr, s);
+    hipLaunchKernelGGL((index_nvfp4_kernel<R, false, INSERT, F16>), grid, dim3(256), 0, s, bt->block_table,
+                       bt->ctx_lens, bt->max_pages_per_req, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages, bs,
+                       ts, bt->num_reqs, p0, nr);
 }
 
 template <bool INSERT>

@@ -1,5 +1,5 @@
 // msa_kernels.h -- launchers of the gfx950 MSA kernels, called by the C ABI
-// layer (msa_api.cpp) after it has validated every host-side argument.
+// layer (msa_api.hip) after it has validated every host-side argument.
 // Each returns 0, or -1 when the launch failed.
 #pragma once
 

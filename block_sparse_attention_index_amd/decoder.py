@@ -12,7 +12,7 @@ import torch
 
 from . import (MSA_DIM_MAJOR, MSA_F32, MSA_FP8_E4M3, MSA_HALF_ROWS, MSA_MAX_ROWS, MSA_NVFP4, MSA_TOKEN_MAJOR,
                Batch, Cache,
-               msa_block_maxpool_topk, msa_decode_workspace_bytes, msa_index_score, msa_insert_index_score,
+               msa_block_maxpool_topk, msa_workspace_bytes, msa_index_score, msa_insert_index_score,
                msa_kv_insert, msa_select_decode, msa_sparse_decode)
 
 GROUPS = 4
@@ -39,7 +39,7 @@ class MsaDecoder:
         self.sel = torch.empty((B, R, GROUPS, topk), dtype=torch.int32, device=device)
         self.cnt = torch.empty((B, R, GROUPS), dtype=torch.int32, device=device)
         self.out = torch.empty((B, R, HEADS, 128), dtype=torch.float32, device=device)
-        nbytes = msa_decode_workspace_bytes(batch, topk)
+        nbytes = msa_workspace_bytes(batch, topk)
         self.workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=device)
 
     def insert(self, k, v, idx_k, slots, stream=None):

@@ -250,7 +250,7 @@ int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t 
                            int32_t topk, int32_t* sel_blocks, int32_t* sel_count, hipStream_t stream);
 
 /* Workspace bytes msa_sparse_decode needs for this batch and topk (host call). */
-size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk);
+size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk);
 
 /*
  * Step 4: exact GQA softmax attention over the selected blocks (vLLM post,
@@ -260,7 +260,7 @@ size_t msa_decode_workspace_bytes(const msa_batch* batch, int32_t topk);
  *   out[b][r][h] = sum_t softmax_t(sm_scale * q_h . K_g[t]) V_g[t].
  * q: [B][R][4*8][128], FP8 E4M3 bytes (times q_scale) with NVFP4 caches or
  * FP32 with F32 caches.  out: [B][R][32][128] FP32; rows with no selected
- * block get zeros.  workspace: device, >= msa_decode_workspace_bytes() (used
+ * block get zeros.  workspace: device, >= msa_workspace_bytes() (used
  * by the F32 route for per-block partial results; no initial contents
  * needed).  Two calls that share a workspace must not run concurrently.
  * With NVFP4 or FP8 caches R may be up to MSA_MAX_PREFILL_ROWS (each row of a

@@ -26,10 +26,22 @@ def lib():
     return C.CDLL(LIB)
 
 
-def test_header_declares_the_four_calls():
+# The boundary's calls as the problem statement names them: the four steps (insert, index
+# score, max-pool + top-k, sparse decode) and the helpers that go with them (workspace size,
+# status text, the test-only dequantiser).
+BOUNDARY = ("msa_kv_insert_nvfp4", "msa_index_score", "msa_block_maxpool_topk", "msa_sparse_decode",
+            "msa_workspace_bytes", "msa_status_str", "msa_debug_dequant")
+
+
+def test_header_declares_the_boundary_calls():
     names = _declared()
-    for n in ("msa_kv_insert_nvfp4", "msa_index_score", "msa_block_maxpool_topk", "msa_sparse_decode"):
-        assert n in names
+    missing = [n for n in BOUNDARY if n not in names]
+    assert not missing, missing
+
+
+def test_library_exports_the_boundary_calls(lib):
+    missing = [n for n in BOUNDARY if not hasattr(lib, n)]
+    assert not missing, missing
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -87,8 +99,8 @@ def test_host_validation_without_gpu(lib):
     # workspace too small; value cache must be dim-major when NVFP4
     k = Cache(2, 0, 4, 16, 0.01, fake)
     v = Cache(2, 1, 4, 16, 0.01, fake)
-    lib.msa_decode_workspace_bytes.restype = C.c_size_t
-    need = lib.msa_decode_workspace_bytes(C.byref(good), 16)
+    lib.msa_workspace_bytes.restype = C.c_size_t
+    need = lib.msa_workspace_bytes(C.byref(good), 16)
     assert need > 0
     assert lib.msa_sparse_decode(C.byref(good), fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k), C.byref(v),
                                  fake, fake, 16, fake, fake, C.c_size_t(need - 1), None) == -3
@@ -122,11 +134,11 @@ def test_host_validation_without_gpu(lib):
 
 
 def test_workspace_size_formula(lib):
-    lib.msa_decode_workspace_bytes.restype = C.c_size_t
+    lib.msa_workspace_bytes.restype = C.c_size_t
     fake = C.c_void_p(0x1000)
     b = Batch(32, 1, 1536, 0, fake, fake)
     # 4 splits of 4 blocks for top-16; FP32 route needs 16 splits of 1 block: the larger is reserved
-    assert lib.msa_decode_workspace_bytes(C.byref(b), 16) == 32 * 4 * 16 * 8 * 130 * 4
+    assert lib.msa_workspace_bytes(C.byref(b), 16) == 32 * 4 * 16 * 8 * 130 * 4
 
 
 def test_layout_rules_without_gpu(lib):

@@ -133,6 +133,28 @@ CASES = {
     # more than 64 requests: the scan's grid is not packed to the contexts (the per-lane map covers 64)
     "many_reqs": lambda: W.make_workload(3, seed=21, B=80, len_div=256),
     "fp8_many_reqs": lambda: W.make_workload(3, seed=22, B=80, len_div=256, cache="fp8"),
+    # 5, 6 and 7 rows: the index scan's second FP16 query tile is partial (40, 48, 56 of 64 index
+    # queries), and attention's two-tile row groups end with a partial group
+    # (r6 and fp8_r6: 11 x 6 x 4 = 264 workgroup rows, so attention takes row groups of 4 + 2 rows;
+    # r5, r7: one workgroup per row)
+    "r5": lambda: W.make_workload(4, seed=23, B=2, len_div=64, R=5),
+    "r6": lambda: W.make_workload(4, seed=24, B=11, len_div=64, R=6),
+    "r7": lambda: W.make_workload(4, seed=25, lengths=[3, 900, 6000], R=7),
+    "union_r7": lambda: W.make_workload(4, seed=36, B=10, len_div=64, R=7),
+    "fp8_r5": lambda: W.make_workload(4, seed=26, B=2, len_div=64, R=5, cache="fp8"),
+    "fp8_r6": lambda: W.make_workload(4, seed=27, B=11, len_div=64, R=6, cache="fp8"),
+    "fp8_r7": lambda: W.make_workload(4, seed=28, lengths=[3, 900, 6000], R=7, cache="fp8"),
+    # 3 rows on the row-group union path: 24 x 3 x 4 = 288 workgroup rows exceed the 256 CUs
+    "union_r3": lambda: W.make_workload(4, seed=29, B=24, len_div=32, R=3),
+    # other selection sizes through the index scan, the fused selection and attention
+    "topk8": lambda: W.make_workload(3, seed=30, B=4, len_div=24, topk=8),
+    "topk32": lambda: W.make_workload(3, seed=31, B=4, len_div=12, topk=32),
+    "topk32_r4": lambda: W.make_workload(4, seed=32, B=3, len_div=24, R=4, topk=32),
+    "fp8_topk8": lambda: W.make_workload(3, seed=33, B=3, len_div=24, topk=8, cache="fp8"),
+    # a block table wider than 3,072 entries (short contexts): the selection reads its scores from
+    # memory on demand and attention reads the table row from memory instead of LDS
+    "wide_table": lambda: W.make_workload(3, seed=34, B=3, len_div=32, table_width=3100),
+    "wide_table_r4": lambda: W.make_workload(4, seed=35, B=2, len_div=32, R=4, table_width=3100),
 }
 
 
@@ -282,7 +304,8 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
-                                  "fp8_prefill", "fp8_prefill_r512", "many_reqs", "fp8_many_reqs"])
+                                  "fp8_prefill", "fp8_prefill_r512", "many_reqs", "fp8_many_reqs", "r5", "r6", "r7",
+                                  "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "wide_table", "wide_table_r4"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -315,6 +338,53 @@ def test_index_scores(M, oracle, case):
     dec.block_scores.fill_(3.0)
     dec.index(q_idx, wl.q_scale, None)
     assert np.array_equal(dec.block_scores.cpu().numpy().astype(np.float64), got_blk)
+
+
+@pytest.mark.parametrize("case", ["prefix_wide", "prefill_ragged", "cfg4_small", "fp8_cfg3_small"])
+def test_nan_index_query(M, oracle, case):
+    """An index query holding a NaN (the E4M3 NaN byte 0x7F in one dim) scores NaN on every token,
+    and the max-pool skips NaN on both sides, so its blocks score -inf; the other queries are
+    untouched.  Through the shared-prefix indexer (matrix cores, FP16), the prefill indexer, the
+    FP16 multi-row scan and the FP8 scan; the selection of the NaN rows is then the tie rule's:
+    the latest block and the lowest others."""
+    wl = CASES[case]()
+    _print_case(f"nan index query {case}", wl)
+    dec, q_idx, _ = gpu_setup(M, wl)
+    bi = oracle.quantize_queries(W.queries(wl)[0], wl.q_scale)
+    nan_rows = [(0, 0, 1), (wl.B - 1, wl.R - 1, 3)] + ([(1, wl.R // 2, 0)] if wl.B > 1 else [])
+    for (b, r, g) in nan_rows:
+        bi[b, r, g, 5] = 0x7F
+    q_idx.copy_(_dev(bi))
+    T = wl.max_pages * 128
+    tok = torch.empty((wl.B, wl.R, 4, T), dtype=torch.float32, device="cuda")
+    dec.index(q_idx, wl.q_scale, tok)
+    dec.select()
+    torch.cuda.synchronize()
+    got_tok = tok.cpu().numpy().astype(np.float64)
+    got_blk = dec.block_scores.cpu().numpy().astype(np.float64)
+    ci, _, _ = oracle_caches(oracle, wl)
+    bt = oracle_batch(oracle, wl)
+    qi = oracle.decode_queries(bi, oracle.FP8_E4M3, wl.q_scale)
+    ref_tok, ref_abs = oracle.index_scores(bt, qi, ci, with_abs=True)
+    ref_blk = oracle.block_maxpool(bt, ref_tok)
+    nan = np.isnan(ref_tok)
+    assert nan.any()
+    assert np.array_equal(np.isnan(got_tok), nan)
+    inv = np.isneginf(ref_tok)
+    assert np.array_equal(np.isneginf(got_tok), inv)
+    ok = ~nan & ~inv
+    assert (np.abs(got_tok[ok] - ref_tok[ok]) <= SCORE_TOL * ref_abs[ok] + 1e-30).all()
+    binv = np.isneginf(ref_blk)
+    for (b, r, g) in nan_rows:
+        assert binv[b, r, g].all()
+    assert np.array_equal(np.isneginf(got_blk), binv)
+    fin = ~binv
+    pooled = np.where(np.isnan(got_tok), -np.inf, got_tok).reshape(got_tok.shape[:3] + (wl.max_pages, 128)).max(-1)
+    assert np.array_equal(got_blk[fin], pooled[fin])
+    rs, rc = oracle.select(bt, ref_blk, wl.topk)
+    g_sel, g_cnt = dec.sel.cpu().numpy(), dec.cnt.cpu().numpy()
+    for (b, r, g) in nan_rows:
+        assert g_cnt[b, r, g] == rc[b, r, g] and np.array_equal(g_sel[b, r, g], rs[b, r, g])
 
 
 # ---------------------------------------------------------------- step 3
@@ -378,7 +448,8 @@ def _out_err(got, ref):
 
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small",
                                   "ragged", "ragged_r4", "r3", "r8", "fp8_cfg3_small", "fp8_ragged_r4", "fp8_r8",
-                                  "prefill_ragged", "fp8_prefill"])
+                                  "prefill_ragged", "fp8_prefill", "r5", "r7", "fp8_r6", "union_r3", "topk8",
+                                  "topk32", "topk32_r4", "fp8_topk8", "wide_table"])
 def test_sparse_decode_on_oracle_selection(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -471,7 +542,9 @@ def _sampled_caches(oracle, wl, rows):
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
-                                  "union_r4", "union_r2", "fp8_prefill", "fp8_prefill_r512"])
+                                  "union_r4", "union_r2", "fp8_prefill", "fp8_prefill_r512", "r5", "r6", "r7",
+                                  "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "union_r7", "topk8", "topk32",
+                                  "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
@@ -481,7 +554,8 @@ def test_full_step(M, oracle, case, fused):
 
 
 @pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged", "ragged_r4", "r8",
-                                  "prefix_wide", "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r8"])
+                                  "prefix_wide", "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "r5",
+                                  "r6", "r7", "fp8_r5", "fp8_r7", "union_r3", "topk32"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step_with_new_rows(M, oracle, case, fused):
     """The step inserts each request's R new rows itself (fused: insert + index in one
@@ -491,7 +565,8 @@ def test_full_step_with_new_rows(M, oracle, case, fused):
     _check_full_step(M, oracle, wl, fused=fused, new_rows=True)
 
 
-@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8", "many_reqs"])
+@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8", "many_reqs", "r5",
+                                  "r6", "r7", "fp8_r7", "union_r3"])
 def test_insert_index_equals_separate_calls(M, oracle, case):
     """msa_insert_index_score: the caches bitwise as msa_kv_insert_nvfp4 writes them (and as
     the oracle writes them), and bitwise the block scores of msa_index_score after that insert."""
@@ -511,7 +586,9 @@ def test_insert_index_equals_separate_calls(M, oracle, case):
     assert torch.equal(dec_a.block_scores.view(torch.int32), dec_b.block_scores.view(torch.int32))
 
 
-@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8", "union_r4", "union_r2"])
+@pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8", "union_r4", "union_r2", "r5", "r6",
+                                  "r7", "fp8_r6", "union_r3", "union_r7", "topk8", "topk32", "topk32_r4",
+                                  "fp8_topk8", "wide_table", "wide_table_r4"])
 def test_select_decode_equals_separate_calls(M, oracle, case):
     """msa_select_decode: same selection as msa_block_maxpool_topk and bitwise the same
     output as msa_sparse_decode on that selection."""

@@ -293,3 +293,89 @@ def test_fp8_layouts_hold_the_same_values(oracle):
             for d in (0, 17, 127):
                 for c in (tm, dm, hr):
                     assert c.value(int(s // 128), h, int(s % 128), d) == vals[codes[i, h, d]] * ts
+
+
+# ---------------------------------------------------------------- NVFP4 page placement
+def _nvfp4_expected_pool(codes, scales, slots, heads, num_pages, dim_major):
+    """Bytes of an NVFP4 page pool holding the given per-element E2M1 codes [n][heads][128] and
+    per-group E4M3 scale codes [n][heads][8] at `slots`, placed by the slab layouts the C ABI
+    defines (9,216 B per (page, head): 8,192 B of codes, then 1,024 B of scales).
+    Token-major: codes [tok][64 B], byte i = dim 2i (low nibble) | dim 2i+1 (high); scales [tok][8].
+    Dim-major: codes [dim][64 B], byte i = token 2i (low) | token 2i+1 (high); scales [8][tok]."""
+    pool = np.zeros((num_pages, heads, 9216), np.uint8)
+    for i, s in enumerate(slots):
+        p, t = int(s) // 128, int(s) % 128
+        for h in range(heads):
+            slab = pool[p, h]
+            for d in range(128):
+                c = int(codes[i, h, d])
+                if dim_major:
+                    byte, shift = d * 64 + t // 2, 4 * (t % 2)
+                else:
+                    byte, shift = t * 64 + d // 2, 4 * (d % 2)
+                slab[byte] |= np.uint8(c << shift)
+            for j in range(8):
+                slab[8192 + (j * 128 + t if dim_major else t * 8 + j)] = scales[i, h, j]
+    return pool.reshape(-1)
+
+
+@pytest.mark.parametrize("heads,layout", [(4, "token_major"), (1, "token_major"), (4, "dim_major")])
+def test_nvfp4_cache_bytes_sit_where_the_layout_puts_them(oracle, heads, layout):
+    """The oracle's NVFP4 cache writer against the layout definition, with no quantiser or
+    decoder in the comparison.  Rows are built from drawn E2M1 codes and E4M3 scale codes as
+    e2m1 * e4m3 * ts with a power-of-two ts and one magnitude-6 element per 16-dim group, so
+    every FP32 step of the amax recipe is exact: the scale is the drawn one and each code
+    comes back.  The rows go to shuffled slots of a 3-page pool (token pairs sharing a
+    dim-major byte included); every byte of the pool must equal the layout's placement of the
+    drawn codes and zero elsewhere.  Keys (4 heads) and index keys (1 head) are token-major,
+    values dim-major."""
+    rng = np.random.default_rng(31 + heads + (layout == "dim_major"))
+    e4m3 = _torch_e4m3_values()
+    ts = 2.0 ** -8
+    n, num_pages = 150, 3
+    codes = rng.choice(np.array([c for c in range(16) if c != 8], np.uint8), size=(n, heads, 128))
+    sixes = rng.integers(0, 16, size=(n, heads, 8))
+    g = codes.reshape(n, heads, 8, 16)
+    np.put_along_axis(g, sixes[..., None], (7 | (8 * rng.integers(0, 2, size=(n, heads, 8, 1)))).astype(np.uint8),
+                      axis=-1)
+    codes = g.reshape(n, heads, 128)
+    scales = rng.integers(8, 0x7E, size=(n, heads, 8)).astype(np.uint8)  # normal E4M3 scales
+    x = oracle.e2m1_value(codes) * np.repeat(e4m3[scales], 16, axis=-1) * ts
+    x = x.astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), oracle.e2m1_value(codes) * np.repeat(e4m3[scales], 16, -1) * ts)
+    slots = rng.choice(num_pages * 128, size=n, replace=False)
+    dm = layout == "dim_major"
+    cache = oracle.OracleCache(oracle.NVFP4, oracle.DIM_MAJOR if dm else oracle.TOKEN_MAJOR, heads, num_pages, ts)
+    cache.write(slots, x if heads > 1 else x[:, 0])
+    want = _nvfp4_expected_pool(codes, scales, slots, heads, num_pages, dm)
+    assert np.array_equal(cache.bytes, want)
+
+
+@pytest.mark.parametrize("layout", ["token_major", "dim_major"])
+def test_nvfp4_cache_values_stay_within_a_grid_step_of_their_source(oracle, layout):
+    """N(0,1) rows written at shuffled slots, read back by the tests' own decoder of the
+    documented layout (helpers.decode_pages_f64): every (slot, head, dim) lies within one E2M1
+    grid step of its source value, and every slot not written reads as zero.  The step bound
+    is independent of the oracle: a group's E4M3 scale s is amax/6/ts rounded to 3 mantissa
+    bits (relative error at most 2^-4), and the error is at most half a grid step of at most
+    2 * s * ts, or the saturation distance past 6 * s * ts, both below s * ts <= (amax/6) *
+    (1 + 2^-4).  A row or group written to the wrong place would be off by O(1)."""
+    from helpers import decode_pages_f64
+
+    rng = np.random.default_rng(41 + (layout == "dim_major"))
+    ts = float(np.float32(8 / (6 * 448)))
+    n, num_pages, heads = 200, 3, 4
+    x = rng.standard_normal((n, heads, 128)).astype(np.float32)
+    slots = rng.choice(num_pages * 128, size=n, replace=False)
+    dm = layout == "dim_major"
+    cache = oracle.OracleCache(oracle.NVFP4, oracle.DIM_MAJOR if dm else oracle.TOKEN_MAJOR, heads, num_pages, ts)
+    cache.write(slots, x)
+    vals = decode_pages_f64(cache.bytes, True, dm, heads, num_pages, ts)  # [page][head][tok][dim]
+    got = vals[slots // 128, :, slots % 128, :]  # [n][heads][128]
+    amax = np.abs(x.astype(np.float64)).reshape(n, heads, 8, 16).max(-1)
+    bound = np.repeat(amax / 6 * (1 + 2.0 ** -4), 16, axis=-1)
+    err = np.abs(got - x)
+    assert np.all(err <= bound * (1 + 1e-9))
+    assert err.max() > 0.1 * bound.max()  # the values did go through the quantiser
+    unused = np.setdiff1d(np.arange(num_pages * 128), slots)
+    assert not vals[unused // 128, :, unused % 128, :].any()

@@ -92,10 +92,13 @@ class Workload:
 
 
 def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int = 1,
-                  lengths: list[int] | None = None, R: int | None = None, cache: str | None = None) -> Workload:
+                  lengths: list[int] | None = None, R: int | None = None, cache: str | None = None,
+                  topk: int = TOPK, table_width: int | None = None) -> Workload:
     """Build the shapes of a configuration.  ``B``/``len_div`` shrink it for
     parity tests; ``lengths`` overrides the drawn lengths (edge cases);
-    ``cache`` = "fp8" stores the same shapes in FP8 caches instead of NVFP4."""
+    ``cache`` = "fp8" stores the same shapes in FP8 caches instead of NVFP4;
+    ``topk`` sets the selected blocks per row; ``table_width`` pads the block
+    table with unused columns (page 0) up to that many entries per request."""
     cfg = CONFIGS[config]
     rng = np.random.default_rng([seed, 0])
     B = cfg["B"] if B is None else B
@@ -123,6 +126,9 @@ def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int
         perm = np.arange(num_pages, dtype=np.int64)
     else:
         perm = rng.permutation(num_pages)
+    if table_width is not None:
+        assert table_width >= max_pages
+        max_pages = table_width
     table = np.zeros((B, max_pages), dtype=np.int32)
     nxt = prefix_pages
     for b in range(B):
@@ -135,7 +141,8 @@ def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int
     ts = {"nvfp4": NVFP4_TENSOR_SCALE, "fp8": FP8_TENSOR_SCALE, "f32": 1.0}[kind]
     name = cfg["name"] if kind == cfg["cache"] else f'{cfg["name"]}_{kind}'
     return Workload(name=name, seed=seed, B=B, R=R, cache=kind, lengths=lens.astype(np.int32),
-                    block_table=table, num_pages=int(num_pages), prefix_tokens=int(prefix), tensor_scale=ts)
+                    block_table=table, num_pages=int(num_pages), prefix_tokens=int(prefix), topk=topk,
+                    tensor_scale=ts)
 
 
 def request_rows(wl: Workload, b: int):
