@@ -66,6 +66,7 @@ def _load() -> C.CDLL:
                                              P(msa_cache), P(msa_cache), vp, vp]),
         "msa_status_str": (C.c_char_p, [C.c_int]),
         "msa_debug_dequant": (C.c_int, [P(msa_cache), vp, i32, i32, vp, vp]),
+        "msa_debug_stream_read": (C.c_int, [vp, i64, i32, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -235,3 +236,9 @@ def msa_status_str(status: int) -> str:
 def msa_debug_dequant(cache: Cache, pages, mode: int, out, stream=None) -> None:
     _check(lib.msa_debug_dequant(cache.ref(), _ptr(pages), pages.shape[0], int(mode), _ptr(out), _stream(stream)),
            "msa_debug_dequant")
+
+
+def msa_debug_stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None) -> None:
+    """Read all of src (a contiguous device tensor) with the index scan's streaming loads: a measurement aid."""
+    _check(lib.msa_debug_stream_read(_ptr(src), src.numel() * src.element_size(), int(workgroups), _ptr(sink),
+                                     _stream(stream)), "msa_debug_stream_read")

@@ -16,12 +16,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["msa_api.hip", "msa_insert.hip", "msa_index.hip", "msa_prefix.hip", "msa_topk.hip", "msa_attn.hip",
-           "msa_qkv.hip"]
-# Per-file flags.  msa_prefix.hip: max-pooling of matrix-core results is
-# compiled without NaN canonicalisation (every fmaxf there would otherwise
-# first quieten its operand with an extra v_max x, x); the hardware maximum
-# still returns the non-NaN operand, which is what fmaxf returns.
-EXTRA_FLAGS = {"msa_prefix.hip": ["-fno-honor-nans"]}
+           "msa_qkv.hip", "msa_stream.hip"]
+# Per-file flags (none at present: every file keeps IEEE NaN semantics, so the
+# indexers' max-pools skip NaN scores as the definition does).
+EXTRA_FLAGS = {}
 
 
 def build(verbose: bool = False, jobs: int = 5) -> str:

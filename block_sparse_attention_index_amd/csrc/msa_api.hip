@@ -206,6 +206,13 @@ int msa_insert_index_score(const msa_batch* batch, const float* k_new, const flo
              : MSA_ERR_HIP;
 }
 
+int msa_debug_stream_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink || bytes < 0 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return MSA_ERR_INVALID_ARG;
+  if (workgroups < 1 || workgroups > 65535) return MSA_ERR_INVALID_ARG;
+  if (bytes == 0) return MSA_OK;
+  return msa_launch_stream_read(src, bytes, workgroups, sink, stream) == 0 ? MSA_OK : MSA_ERR_HIP;
+}
+
 const char* msa_status_str(int status) {
   switch (status) {
     case MSA_OK: return "ok";

@@ -284,6 +284,17 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
                       const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,
                       hipStream_t stream);
 
+/*
+ * Measurement aid, not a step of the path: read `bytes` bytes of device
+ * memory at src (16-byte aligned, bytes a multiple of 16) with the streaming
+ * 16-byte loads the index scan uses, spread over `workgroups` workgroups of
+ * 256 threads (1..65535) that each read one contiguous share.  Nothing is
+ * written except, with negligible probability, one word of sink (device,
+ * 4 bytes).  Its rate is the practical HBM read ceiling the index scan is
+ * reported against.
+ */
+int msa_debug_stream_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, hipStream_t stream);
+
 /* Static text for a status code (host call). */
 const char* msa_status_str(int status);
 

@@ -27,6 +27,7 @@ STUB(msa_launch_insert_index_score, const msa_batch*, const float*, const float*
 STUB(msa_launch_topk, const msa_batch*, const float*, int32_t, int32_t, int32_t*, int32_t*, hipStream_t)
 STUB(msa_launch_select_decode, const msa_batch*, const float*, int32_t, const void*, float, float, const msa_cache*,
      const msa_cache*, int32_t*, int32_t*, float*, hipStream_t)
+STUB(msa_launch_stream_read, const void*, int64_t, int32_t, uint32_t*, hipStream_t)
 STUB(msa_launch_sparse_decode, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, void*, hipStream_t)
 extern "C" size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk) {
@@ -43,7 +44,7 @@ static void expect(int got, int want, int want_launches, const char* what) {
 }
 
 int main() {
-  char buf[64];
+  alignas(16) char buf[64];
   void* p = buf;  // never dereferenced by the validation
   const int32_t* ip = reinterpret_cast<const int32_t*>(buf);
   msa_cache kc{MSA_NVFP4, MSA_TOKEN_MAJOR, 4, 16, 0.01f, p}, vc{MSA_NVFP4, MSA_DIM_MAJOR, 4, 16, 0.01f, p};
@@ -150,6 +151,11 @@ int main() {
   expect(msa_quantize_e4m3(f, 10, 0.0f, u8, nullptr), MSA_ERR_INVALID_ARG, 0, "e4m3 scale");
   expect(msa_debug_dequant(&kc, ip, 2, 0, f, nullptr), MSA_OK, 1, "dequant ok");
   expect(msa_debug_dequant(&kc, ip, 2, 2, f, nullptr), MSA_ERR_INVALID_ARG, 0, "dequant mode");
+  uint32_t* sink = reinterpret_cast<uint32_t*>(buf);
+  expect(msa_debug_stream_read(buf, 64, 4, sink, nullptr), MSA_OK, 1, "stream ok");
+  expect(msa_debug_stream_read(buf, 60, 4, sink, nullptr), MSA_ERR_INVALID_ARG, 0, "stream size");
+  expect(msa_debug_stream_read(buf + 4, 64, 4, sink, nullptr), MSA_ERR_INVALID_ARG, 0, "stream alignment");
+  expect(msa_debug_stream_read(buf, 64, 0, sink, nullptr), MSA_ERR_INVALID_ARG, 0, "stream grid");
   for (int s = -6; s <= 2; ++s) launches += msa_status_str(s)[0] == '\0';
   expect(MSA_OK, MSA_OK, 0, "status text");
 
