@@ -19,6 +19,7 @@ MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP
 MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
 MSA_TOKEN_MAJOR, MSA_DIM_MAJOR, MSA_HALF_ROWS = 0, 1, 2
 MSA_MAX_ROWS, MSA_MAX_PREFILL_ROWS = 8, 8192
+MSA_NOALLOC_SCRATCH_BYTES = 4 << 20
 PAGE_TOKENS = 128
 HEAD_DIM = 128
 HEADS_PER_GROUP = 8
@@ -58,6 +59,8 @@ def _load() -> C.CDLL:
         "msa_workspace_bytes": (sz, [P(msa_batch), i32]),
         "msa_sparse_decode": (C.c_int, [P(msa_batch), vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp, vp, i32,
                                         vp, vp, sz, vp]),
+        "msa_sparse_decode_noalloc": (C.c_int, [P(msa_batch), vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp, vp,
+                                                i32, vp, vp]),
         "msa_select_decode": (C.c_int, [P(msa_batch), vp, i32, vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp,
                                         vp, vp, vp]),
         "msa_insert_index_score": (C.c_int, [P(msa_batch), vp, vp, vp, vp, i32, f32, P(msa_cache), P(msa_cache),
@@ -242,3 +245,11 @@ def msa_debug_stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor
     """Read all of src (a contiguous device tensor) with the index scan's streaming loads: a measurement aid."""
     _check(lib.msa_debug_stream_read(_ptr(src), src.numel() * src.element_size(), int(workgroups), _ptr(sink),
                                      _stream(stream)), "msa_debug_stream_read")
+
+
+def msa_sparse_decode_noalloc(batch: Batch, q, q_dtype: int, q_scale: float, sm_scale: float, k_cache: Cache,
+                              v_cache: Cache, sel_blocks, sel_count, topk: int, out, stream=None) -> None:
+    """msa_sparse_decode with the library's fixed per-GPU scratch array instead of a workspace."""
+    _check(lib.msa_sparse_decode_noalloc(batch.ref(), _ptr(q), q_dtype, float(q_scale), float(sm_scale),
+                                         k_cache.ref(), v_cache.ref(), _ptr(sel_blocks), _ptr(sel_count), int(topk),
+                                         _ptr(out), _stream(stream)), "msa_sparse_decode_noalloc")

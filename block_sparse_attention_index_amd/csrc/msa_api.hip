@@ -165,6 +165,28 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
              : MSA_ERR_HIP;
 }
 
+int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
+                              const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
+                              const int32_t* sel_count, int32_t topk, float* out, hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, VALUES)) != MSA_OK) return st;
+  if (k_cache->dtype != v_cache->dtype || k_cache->num_pages != v_cache->num_pages) return MSA_ERR_INVALID_ARG;
+  if (batch->rows_per_req > MSA_MAX_ROWS && k_cache->dtype == MSA_F32) return MSA_ERR_UNSUPPORTED;
+  if (!q || !sel_blocks || !sel_count || !out) return MSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
+  if ((st = query_dtype_ok(q_dtype, k_cache)) != MSA_OK) return st;
+  if (!finite_pos(sm_scale) || (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale))) return MSA_ERR_INVALID_ARG;
+  // only the F32 route keeps partial results in scratch memory
+  if (k_cache->dtype == MSA_F32 && msa_workspace_bytes(batch, topk) > (size_t)MSA_NOALLOC_SCRATCH_BYTES)
+    return MSA_ERR_WORKSPACE;
+  return msa_launch_sparse_decode_noalloc(batch, q, q_dtype, q_scale, sm_scale, k_cache, v_cache, sel_blocks,
+                                          sel_count, topk, out, stream) == 0
+             ? MSA_OK
+             : MSA_ERR_HIP;
+}
+
 int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t topk, const void* q,
                       int32_t q_dtype, float q_scale, float sm_scale, const msa_cache* k_cache,
                       const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,

@@ -40,6 +40,7 @@
 //    selected block is read once per step), cacheable in prefill (the other
 //    rows of the chunk read the same blocks).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "msa_device.h"
@@ -835,6 +836,32 @@ extern "C" int msa_launch_sparse_decode(const msa_batch* bt, const void* q, int3
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part_o, part_ml, B, R, S,
                      out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// msa_sparse_decode_noalloc keeps the F32 route's per-block partial results in
+// this file-scope array instead of a caller workspace.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// is only a stand-in name; the array's device address on each device comes
+// from hipGetSymbolAddress, taken once per device (on the first call with that
+// device current) and used for every kernel argument.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+extern "C" int msa_launch_sparse_decode_noalloc(const msa_batch* bt, const void* q, int32_t q_dtype, float q_scale,
+                                                float sm_scale, const msa_cache* kc, const msa_cache* vc,
+                                                const int32_t* sel, const int32_t* cnt, int32_t topk, float* out,
+                                                hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return -1;
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  }
+  return msa_launch_sparse_decode(bt, q, q_dtype, q_scale, sm_scale, kc, vc, sel, cnt, topk, out, ptr, s);
 }
 
 extern "C" int msa_launch_select_decode(const msa_batch* bt, const float* block_scores, int32_t topk,

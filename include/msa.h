@@ -71,6 +71,7 @@ typedef enum { MSA_TOKEN_MAJOR = 0, MSA_DIM_MAJOR = 1, MSA_HALF_ROWS = 2 } msa_l
 #define MSA_F32_SLAB_BYTES 65536
 #define MSA_FP8_SLAB_BYTES 16384
 #define MSA_QKV_HEADS 45
+#define MSA_NOALLOC_SCRATCH_BYTES (4 << 20)
 
 /*
  * One paged cache tensor of one layer.  Page p, head h is the slab at
@@ -270,6 +271,27 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
                       const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
                       const int32_t* sel_count, int32_t topk, float* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * attention as msa_sparse_decode, same arguments without the workspace, same
+ * results.  Scratch memory comes from a fixed array inside the library, one
+ * per GPU, of MSA_NOALLOC_SCRATCH_BYTES (4 MiB), held from the first call on
+ * a GPU until the process ends; the call itself allocates nothing.  Only
+ * F32 caches use scratch memory (NVFP4 and FP8 caches need none, for any
+ * batch): an F32 batch whose msa_workspace_bytes() exceeds that size returns
+ * MSA_ERR_WORKSPACE (4 MiB holds 15 one-row requests at topk 16, the partial
+ * results of every selected block).  Every call on a GPU shares that GPU's
+ * array, and nothing in it needs initial contents (each call writes every
+ * partial it reads).  Two calls that may
+ * overlap on one GPU (different streams, or different host threads) race and
+ * must not be issued.  Errors as msa_sparse_decode; a failed device query
+ * returns MSA_ERR_HIP.
+ */
+int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
+                              const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
+                              const int32_t* sel_count, int32_t topk, float* out, hipStream_t stream);
 
 /*
  * Steps 3+4 in one launch (NVFP4 caches, FP8 queries): the selection of

@@ -27,6 +27,8 @@ STUB(msa_launch_insert_index_score, const msa_batch*, const float*, const float*
 STUB(msa_launch_topk, const msa_batch*, const float*, int32_t, int32_t, int32_t*, int32_t*, hipStream_t)
 STUB(msa_launch_select_decode, const msa_batch*, const float*, int32_t, const void*, float, float, const msa_cache*,
      const msa_cache*, int32_t*, int32_t*, float*, hipStream_t)
+STUB(msa_launch_sparse_decode_noalloc, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
+     const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, hipStream_t)
 STUB(msa_launch_stream_read, const void*, int64_t, int32_t, uint32_t*, hipStream_t)
 STUB(msa_launch_sparse_decode, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, void*, hipStream_t)
@@ -123,7 +125,20 @@ int main() {
          "select_decode ok");
   expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, nullptr, f, nullptr),
          MSA_ERR_INVALID_ARG, 0, "select_decode no counts");
+  expect(msa_sparse_decode_noalloc(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, nullptr), MSA_OK, 1,
+         "noalloc ok");
+  b2 = bt;
+  b2.num_reqs = 4000;  // NVFP4: no scratch memory, any batch
+  expect(msa_sparse_decode_noalloc(&b2, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, nullptr), MSA_OK, 1,
+         "noalloc nvfp4 large batch");
   msa_cache k32{MSA_F32, MSA_TOKEN_MAJOR, 4, 16, 1.0f, p};
+  msa_cache v32{MSA_F32, MSA_TOKEN_MAJOR, 4, 16, 1.0f, p};
+  expect(msa_sparse_decode_noalloc(&b2, p, MSA_F32, 1.0f, 0.088f, &k32, &v32, i32, i32, 16, f, nullptr),
+         MSA_ERR_WORKSPACE, 0, "noalloc f32 beyond the scratch array");
+  expect(msa_sparse_decode_noalloc(&bt, p, MSA_F32, 1.0f, 0.088f, &k32, &v32, i32, i32, 16, f, nullptr), MSA_OK, 1,
+         "noalloc f32 ok");
+  expect(msa_sparse_decode_noalloc(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, nullptr, 16, f, nullptr),
+         MSA_ERR_INVALID_ARG, 0, "noalloc no counts");
   expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &k32, &k32, i32, i32, f, nullptr),
          MSA_ERR_UNSUPPORTED, 0, "select_decode f32");
 
