@@ -62,7 +62,7 @@ def _load() -> C.CDLL:
         "msa_sparse_decode_noalloc": (C.c_int, [P(msa_batch), vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp, vp,
                                                 i32, vp, vp]),
         "msa_select_decode": (C.c_int, [P(msa_batch), vp, i32, vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp,
-                                        vp, vp, vp]),
+                                        vp, vp, vp, sz, vp]),
         "msa_insert_index_score": (C.c_int, [P(msa_batch), vp, vp, vp, vp, i32, f32, P(msa_cache), P(msa_cache),
                                              P(msa_cache), vp, vp, vp]),
         "msa_qkv_project_insert": (C.c_int, [vp, vp, i32, i32, vp, f32, vp, i32, vp, vp, f32, vp, vp, P(msa_cache),
@@ -226,10 +226,11 @@ def msa_sparse_decode(batch: Batch, q, q_dtype: int, q_scale: float, sm_scale: f
 
 
 def msa_select_decode(batch: Batch, block_scores, topk: int, q, q_dtype: int, q_scale: float, sm_scale: float,
-                      k_cache: Cache, v_cache: Cache, sel_blocks, sel_count, out, stream=None) -> None:
+                      k_cache: Cache, v_cache: Cache, sel_blocks, sel_count, out, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.msa_select_decode(batch.ref(), _ptr(block_scores), int(topk), _ptr(q), q_dtype, float(q_scale),
                                  float(sm_scale), k_cache.ref(), v_cache.ref(), _ptr(sel_blocks), _ptr(sel_count),
-                                 _ptr(out), _stream(stream)), "msa_select_decode")
+                                 _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)), "msa_select_decode")
 
 
 def msa_status_str(status: int) -> str:

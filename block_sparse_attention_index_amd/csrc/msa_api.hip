@@ -141,7 +141,9 @@ int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t 
 
 size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk) {
   if (check_batch(batch, MSA_MAX_PREFILL_ROWS) != MSA_OK || topk < 1 || topk > MSA_MAX_TOPK) return 0;
-  return msa_decode_partials_bytes(batch, topk);
+  // F32 caches: per-block partial results; NVFP4 / FP8: the partials of rows split over several workgroups
+  const size_t f32 = msa_decode_partials_bytes(batch, topk), split = msa_split_partials_bytes(batch);
+  return f32 > split ? f32 : split;
 }
 
 int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
@@ -178,9 +180,9 @@ int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_d
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
   if ((st = query_dtype_ok(q_dtype, k_cache)) != MSA_OK) return st;
   if (!finite_pos(sm_scale) || (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale))) return MSA_ERR_INVALID_ARG;
-  // only the F32 route keeps partial results in scratch memory
-  if (k_cache->dtype == MSA_F32 && msa_workspace_bytes(batch, topk) > (size_t)MSA_NOALLOC_SCRATCH_BYTES)
-    return MSA_ERR_WORKSPACE;
+  const size_t need = k_cache->dtype == MSA_F32 ? msa_decode_partials_bytes(batch, topk)
+                                               : msa_split_partials_bytes(batch);
+  if (need > (size_t)MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_WORKSPACE;
   return msa_launch_sparse_decode_noalloc(batch, q, q_dtype, q_scale, sm_scale, k_cache, v_cache, sel_blocks,
                                           sel_count, topk, out, stream) == 0
              ? MSA_OK
@@ -189,8 +191,8 @@ int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_d
 
 int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t topk, const void* q,
                       int32_t q_dtype, float q_scale, float sm_scale, const msa_cache* k_cache,
-                      const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,
-                      hipStream_t stream) {
+                      const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   int st;
   if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
   if ((st = check_cache(k_cache, KEYS)) != MSA_OK) return st;
@@ -201,8 +203,9 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
   if (q_dtype != MSA_FP8_E4M3) return MSA_ERR_UNSUPPORTED;
   if (!finite_pos(sm_scale) || !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
+  if (workspace && workspace_bytes < msa_workspace_bytes(batch, topk)) return MSA_ERR_WORKSPACE;
   return msa_launch_select_decode(batch, block_scores, topk, q, q_scale, sm_scale, k_cache, v_cache, sel_blocks,
-                                  sel_count, out, stream) == 0
+                                  sel_count, out, workspace, stream) == 0
              ? MSA_OK
              : MSA_ERR_HIP;
 }

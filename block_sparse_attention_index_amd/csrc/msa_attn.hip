@@ -382,6 +382,42 @@ __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h
 }
 
 constexpr int kTabLds = 2048;  // block-table rows up to this width are staged in LDS
+constexpr int kSplitPart = 2 * kHpg + kHpg * kDim;  // floats of one split's partial: M[8], l[8], O[8][128]
+constexpr int kMaxSplit = 4;
+
+// Merge of the SPLIT partials of each (request, row, group): with M = max_s
+// M_s and w_s = exp2(M_s - M), out = v_scale * sum_s w_s O_s / sum_s w_s l_s,
+// summed in split order (bitwise reproducible).  One workgroup per (request,
+// row, group); thread t handles head t / 32, dims 4 (t % 32) .. + 3.
+template <int SPLIT>
+__global__ __launch_bounds__(256) void split_combine_kernel(const float* __restrict__ part, float v_scale,
+                                                            float* __restrict__ out) {
+  const int64_t row = blockIdx.x;
+  const int hh = threadIdx.x >> 5, d = 4 * (threadIdx.x & 31);
+  const float* p = part + row * SPLIT * kSplitPart;
+  float ms[SPLIT], ls[SPLIT];
+  float4 os[SPLIT];
+#pragma unroll
+  for (int s = 0; s < SPLIT; ++s) {
+    ms[s] = p[s * kSplitPart + hh];
+    ls[s] = p[s * kSplitPart + kHpg + hh];
+    os[s] = *reinterpret_cast<const float4*>(p + s * kSplitPart + 2 * kHpg + hh * kDim + d);
+  }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < SPLIT; ++s) M = fmaxf(M, ms[s]);
+  float den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < SPLIT; ++s) {
+    const float w = ms[s] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
+    den += ls[s] * w;
+    acc.x += os[s].x * w, acc.y += os[s].y * w, acc.z += os[s].z * w, acc.w += os[s].w * w;
+  }
+  const float inv = den > 0.f ? v_scale / den : 0.f;
+  *reinterpret_cast<float4*>(out + (row * kHpg + hh) * kDim + d) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
 
 // Steps 3 (when SELECT) and 4 for one (request, group, row group); grid (groups x row groups, requests).
 // WAVES per workgroup: 8 with one query tile; 4 with two, so that each wave can
@@ -394,14 +430,21 @@ constexpr int kTabLds = 2048;  // block-table rows up to this width are staged i
 // rows select independently (no union to share).
 // RPW: rows per workgroup, 4 (the union of a row group) or 1 (each row on
 // its own, more workgroups: used while the batch leaves CUs idle).
-template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8, int RPW, bool PREFILL = false>
+// SPLIT > 1 (one row per workgroup, while SPLIT workgroups per row still fit
+// the CUs): workgroup s of a row takes union blocks s, s + SPLIT, ... and
+// writes its softmax partial -- running max M, denominator l and unnormalised
+// output O of each query row -- to part ([row][SPLIT][16 + 8 x 128] floats: M
+// of the 8 heads, l of the 8 heads, O); split_combine_kernel merges them.
+template <int QT, bool SELECT, int KMAX, int WAVES, bool FP8, int RPW, bool PREFILL = false, int SPLIT = 1>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREFILL ? 3 : 1))) void attend_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t R, int32_t max_pages,
     const uint8_t* __restrict__ q, float qk2, float v_scale, const uint8_t* __restrict__ kpages,
     const uint8_t* __restrict__ vpages, int32_t num_pages, const float* __restrict__ block_scores,
-    int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t topk, float* __restrict__ out) {
+    int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t topk, float* __restrict__ out,
+    float* __restrict__ part) {
   static_assert(!PREFILL || (QT == 1 && WAVES == 4 && RPW == 1), "the prefill form: one tile, 4 waves, one row");
   static_assert(RPW == 1 || RPW == 4, "rows per workgroup: 1 or 4");
+  static_assert(SPLIT == 1 || (RPW == 1 && QT == 1 && !PREFILL), "split rows: one row per workgroup");
   constexpr int NT = WAVES * 64;
   constexpr int NQ = QT * 16;  // query columns of the workgroup (rows nq.. are padding)
   __shared__ int s_tab[PREFILL ? 1 : kTabLds];
@@ -421,7 +464,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
   __shared__ __align__(16) float s_o[WAVES][NQ / 2][kDim + 4];
 
   const int RG = (R + RPW - 1) / RPW;
-  const int g = blockIdx.x / RG, rg = blockIdx.x % RG;
+  const int split = SPLIT > 1 ? (int)(blockIdx.x % SPLIT) : 0;
+  const int g = (blockIdx.x / SPLIT) / RG, rg = (blockIdx.x / SPLIT) % RG;
   const int b = blockIdx.y;
   const int r0 = rg * RPW, nr = min(RPW, R - r0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -457,16 +501,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
       const float* srow_scores = block_scores + row_id * max_pages;
       int32_t* o = sel + row_id * topk;
       int* srow = s_rowsel + wave * topk;
+      // the selection's outputs are written once per row, by split 0
       const int c = select_fast<KMAX>(sc, [&](int j) { return srow_scores[j]; }, nb, topk, lane, &s_sel[SELECT ? wave : 0],
                                       [&](int rank, int id) {
                                         srow[rank] = id;
-                                        o[rank] = id;
+                                        if (split == 0) o[rank] = id;
                                       });
       if (lane >= c && lane < topk) {
         srow[lane] = -1;
-        o[lane] = -1;
+        if (split == 0) o[lane] = -1;
       }
-      if (lane == 0) cnt[row_id] = c;
+      if (lane == 0 && split == 0) cnt[row_id] = c;
     }
     __syncthreads();
     nu = union_of_rows(s_rowsel, nr, topk, s_first, s_union, &s_nu);
@@ -481,6 +526,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
   }
   __syncthreads();
 
+  // this workgroup's share of the union: blocks split, split + SPLIT, ...
+  const int nus = SPLIT > 1 ? (nu > split ? (nu - split + SPLIT - 1) / SPLIT : 0) : nu;
+  auto U = [&](int i) { return SPLIT > 1 ? split + SPLIT * i : i; };
+
   AttnState<QT> st;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -491,7 +540,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
   }
   // visibility of block j to this lane's query columns
   auto block_lim = [&](int j, int (&lim)[QT]) {
-    bool part = false;
+    bool any_partial = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const int rl = (qt * 16 + n) / kHpg;  // row within the row group
@@ -499,9 +548,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
       if (rl < nr)
         v = (nr == 1 || row_has_block(s_rowsel, rl, topk, j)) ? min(kPage - 1, L - R + r0 + rl - j * kPage) : -1;
       lim[qt] = v;
-      part |= v < kPage - 1;
+      any_partial |= v < kPage - 1;
     }
-    return __any(part) != 0;
+    return __any(any_partial) != 0;
   };
   constexpr int kSlab = FP8 ? kFp8Slab : kNvSlab;
   auto kslab = [&](int ph) { return kpages + ((int64_t)max(ph, 0) * kGroups + g) * kSlab; };
@@ -516,14 +565,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
       std::conditional_t<FP8, VRegs8, VRegs> V;
       load_k<false>(kslab(ph), lane, K);
       int lim[QT];
-      const bool part = block_lim(s_union[u], lim);
+      const bool partial = block_lim(s_union[u], lim);
       // NVFP4 values load during the softmax; FP8 values (twice the
       // registers) once the scores are consumed
       auto ld_v = [&] { load_v<false>(vslab(ph), lane, V); };
       if constexpr (FP8)
-        attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, NoOp{}, ld_v);
+        attend_block<QT, true>(K, V, Q, lim, partial, first, qk2, lane, &s_slot[0], st, NoOp{}, ld_v);
       else
-        attend_block<QT, true>(K, V, Q, lim, part, first, qk2, lane, &s_slot[wave], st, ld_v);
+        attend_block<QT, true>(K, V, Q, lim, partial, first, qk2, lane, &s_slot[wave], st, ld_v);
       first = false;
     }
   } else if constexpr (FP8) {
@@ -533,33 +582,48 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
     // this block's P V is done
     KRegs8 K;
     VRegs8 V;
-    if (wave < nu) {
-      load_k(kslab(s_phys[wave]), lane, K);
-      load_v(vslab(s_phys[wave]), lane, V);
+    if (wave < nus) {
+      load_k(kslab(s_phys[U(wave)]), lane, K);
+      load_v(vslab(s_phys[U(wave)]), lane, V);
     }
-    for (int u = wave; u < nu; u += WAVES) {
+    for (int i = wave; i < nus; i += WAVES) {
+      const int u = U(i);
       const int ph = s_phys[u];
-      const int un = u + WAVES;
+      const int in = i + WAVES;
       auto next_k = [&]() {
-        if (un < nu) load_k(kslab(s_phys[un]), lane, K);
+        if (in < nus) load_k(kslab(s_phys[U(in)]), lane, K);
       };
       if (ph >= 0) {
         int lim[QT];
-        const bool part = block_lim(s_union[u], lim);
-        attend_block<QT>(K, V, Q, lim, part, first, qk2, lane, &s_slot[0], st, next_k);
+        const bool partial = block_lim(s_union[u], lim);
+        attend_block<QT>(K, V, Q, lim, partial, first, qk2, lane, &s_slot[0], st, next_k);
         first = false;
       } else {
         next_k();
       }
-      if (un < nu) load_v(vslab(s_phys[un]), lane, V);
+      if (in < nus) load_v(vslab(s_phys[U(in)]), lane, V);
+    }
+  } else if (nus <= WAVES) {
+    // at most one block per wave (a split row): its keys and values load
+    // together, and no wave issues loads for a second block it does not have
+    if (wave < nus && s_phys[U(wave)] >= 0) {
+      const int u = U(wave);
+      KRegs K;
+      VRegs V;
+      load_k(kslab(s_phys[u]), lane, K);
+      load_v(vslab(s_phys[u]), lane, V);
+      int lim[QT];
+      const bool partial = block_lim(s_union[u], lim);
+      attend_block<QT>(K, V, Q, lim, partial, first, qk2, lane, &s_slot[wave], st, [] {});
+      first = false;
     }
   } else
   // blocks wave, wave + WAVES, ... of the union, two at a time: the second
   // block's keys load with the first block's, its values once the first
   // block's keys are consumed (register budget of two waves per SIMD)
-  for (int u0 = wave; u0 < nu; u0 += 2 * WAVES) {
-    const int u1 = u0 + WAVES;
-    const bool has1 = u1 < nu;
+  for (int i0 = wave; i0 < nus; i0 += 2 * WAVES) {
+    const bool has1 = i0 + WAVES < nus;
+    const int u0 = U(i0), u1 = U(i0 + WAVES);
     const int ph0 = s_phys[u0], ph1 = has1 ? s_phys[u1] : -1;
     KRegs K0, K1;
     VRegs V0, V1;
@@ -569,16 +633,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
     auto load_v1 = [&]() { load_v(vslab(ph1), lane, V1); };
     if (ph0 >= 0) {
       int lim[QT];
-      const bool part = block_lim(s_union[u0], lim);
-      attend_block<QT>(K0, V0, Q, lim, part, first, qk2, lane, &s_slot[wave], st, load_v1);
+      const bool partial = block_lim(s_union[u0], lim);
+      attend_block<QT>(K0, V0, Q, lim, partial, first, qk2, lane, &s_slot[wave], st, load_v1);
       first = false;
     } else {
       load_v1();
     }
     if (ph1 >= 0) {
       int lim[QT];
-      const bool part = block_lim(s_union[u1], lim);
-      attend_block<QT>(K1, V1, Q, lim, part, first, qk2, lane, &s_slot[wave], st, [] {});
+      const bool partial = block_lim(s_union[u1], lim);
+      attend_block<QT>(K1, V1, Q, lim, partial, first, qk2, lane, &s_slot[wave], st, [] {});
       first = false;
     }
   }
@@ -608,7 +672,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
       s_fac[w][tid] = f;
       den += s_l[w][tid] * f;
     }
-    s_inv[tid] = den > 0.f ? v_scale / den : 0.f;
+    s_inv[tid] = SPLIT > 1 ? 1.f : (den > 0.f ? v_scale / den : 0.f);
+    if (SPLIT > 1) {  // this split's max and denominator of query row tid (row r0, head tid)
+      float* pr = part + ((((int64_t)b * R + r0) * kGroups + g) * SPLIT + split) * kSplitPart;
+      pr[tid] = M;
+      pr[kHpg + tid] = den;
+    }
   }
   __syncthreads();
   // the output rows go through LDS in two halves of NQ/2 rows (LDS budget)
@@ -639,8 +708,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PREF
       }
       const float inv = s_inv[qi];
       const int r = r0 + qi / kHpg, hh = qi % kHpg;
-      *reinterpret_cast<float4*>(&out[((((int64_t)b * R + r) * kGroups + g) * kHpg + hh) * kDim + 4 * d4]) =
-          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      float* dst = SPLIT > 1 ? part + ((((int64_t)b * R + r) * kGroups + g) * SPLIT + split) * kSplitPart + 2 * kHpg +
+                                   hh * kDim
+                             : out + ((((int64_t)b * R + r) * kGroups + g) * kHpg + hh) * kDim;
+      *reinterpret_cast<float4*>(dst + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (half == 0 && nq > NQ / 2) __syncthreads();  // s_o is rewritten for the second half
   }
@@ -760,11 +831,33 @@ static int cu_count() {
   return n;
 }
 
-// NVFP4 and FP8 route: one launch, selection fused in when block_scores != NULL.
+// Workgroups per (request, row, group) of the NVFP4 / FP8 decode route: the
+// attention is bound by the vector ALUs' dequantisation of the selected
+// blocks, so a batch that leaves CUs idle with one workgroup per row spreads
+// each row's blocks over 2 or 4 workgroups (the largest that still fits the
+// CUs), whose partial results split_combine_kernel merges.
+static int attend_splits(const msa_batch* bt) {
+  const int R = bt->rows_per_req;
+  if (R > MSA_MAX_ROWS) return 1;  // prefill chunks: thousands of rows already
+  const int64_t rows = (int64_t)bt->num_reqs * R * kGroups;
+  const int cus = cu_count();
+  for (int S = kMaxSplit; S > 1; S /= 2)
+    if (rows * S <= cus) return S;
+  return 1;
+}
+
+extern "C" size_t msa_split_partials_bytes(const msa_batch* bt) {
+  const int S = attend_splits(bt);
+  if (S == 1) return 0;
+  return (size_t)bt->num_reqs * bt->rows_per_req * kGroups * S * kSplitPart * sizeof(float);
+}
+
+// NVFP4 and FP8 route: one launch, selection fused in when block_scores != NULL,
+// plus the merge of split rows when part != NULL and the batch splits.
 template <bool SELECT, bool FP8>
 static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, float sm_scale,
-                               const msa_cache* kc, const msa_cache* vc, const float* block_scores, int32_t* sel,
-                               int32_t* cnt, int32_t topk, float* out, hipStream_t s) {
+                         const msa_cache* kc, const msa_cache* vc, const float* block_scores, int32_t* sel,
+                         int32_t* cnt, int32_t topk, float* out, float* part, hipStream_t s) {
   const int R = bt->rows_per_req, P = bt->max_pages_per_req;
   // scores enter the kernel's softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
@@ -774,7 +867,7 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
 #define MSA_PREFILL(K)                                                                                          \
   hipLaunchKernelGGL((attend_kernel<1, SELECT, K, 4, FP8, 1, true>), pgrid, dim3(256), 0, s, bt->block_table,     \
                      bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,                     \
-                     (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out)
+                     (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out, nullptr)
     switch (km) {  // 48 candidates per lane do not fit the prefill form's registers: read them on demand
       case 8: MSA_PREFILL(8); break;
       case 24: MSA_PREFILL(24); break;
@@ -790,28 +883,42 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
   // rows walking the union of their sets (rows that select alike share the
   // reads and the dequantisation).
   const bool per_row = R == 1 || (int64_t)bt->num_reqs * R * kGroups <= cu_count();
-#define MSA_ATTEND(QT, K, RPW)                                                                                  \
-  hipLaunchKernelGGL((attend_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4), FP8, RPW>),                              \
-                     dim3(kGroups * ((R + RPW - 1) / RPW), bt->num_reqs), dim3((QT == 1 ? 8 : 4) * 64), 0, s,       \
-                     bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,    \
-                     (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out)
-#define MSA_ATTEND_K(QT, RPW)           \
-  switch (km) {                         \
-    case 8: MSA_ATTEND(QT, 8, RPW); break;   \
-    case 24: MSA_ATTEND(QT, 24, RPW); break; \
-    case 48: MSA_ATTEND(QT, 48, RPW); break; \
-    default: MSA_ATTEND(QT, 0, RPW); break;  \
+  const int S = part ? attend_splits(bt) : 1;
+#define MSA_ATTEND(QT, K, RPW, SPLIT)                                                                           \
+  hipLaunchKernelGGL((attend_kernel<QT, SELECT, K, (QT == 1 ? 8 : 4), FP8, RPW, false, SPLIT>),                  \
+                     dim3(kGroups * ((R + RPW - 1) / RPW) * SPLIT, bt->num_reqs), dim3((QT == 1 ? 8 : 4) * 64), 0, \
+                     s, bt->block_table, bt->ctx_lens, R, P, q, qk2, vc->tensor_scale, (const uint8_t*)kc->pages,  \
+                     (const uint8_t*)vc->pages, kc->num_pages, block_scores, sel, cnt, topk, out, part)
+#define MSA_ATTEND_K(QT, RPW, SPLIT)           \
+  switch (km) {                                \
+    case 8: MSA_ATTEND(QT, 8, RPW, SPLIT); break;   \
+    case 24: MSA_ATTEND(QT, 24, RPW, SPLIT); break; \
+    case 48: MSA_ATTEND(QT, 48, RPW, SPLIT); break; \
+    default: MSA_ATTEND(QT, 0, RPW, SPLIT); break;  \
   }
-  if (per_row) {
-    MSA_ATTEND_K(1, 1)
+  if (per_row && S == 4) {
+    MSA_ATTEND_K(1, 1, 4)
+  } else if (per_row && S == 2) {
+    MSA_ATTEND_K(1, 1, 2)
+  } else if (per_row) {
+    MSA_ATTEND_K(1, 1, 1)
   } else if (R <= 2) {
-    MSA_ATTEND_K(1, 4)
+    MSA_ATTEND_K(1, 4, 1)
   } else {
-    MSA_ATTEND_K(2, 4)
+    MSA_ATTEND_K(2, 4, 1)
   }
 #undef MSA_ATTEND_K
 #undef MSA_ATTEND
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (S > 1) {
+    const dim3 cgrid((unsigned)((int64_t)bt->num_reqs * R * kGroups));
+    if (S == 4)
+      hipLaunchKernelGGL(split_combine_kernel<4>, cgrid, dim3(256), 0, s, part, vc->tensor_scale, out);
+    else
+      hipLaunchKernelGGL(split_combine_kernel<2>, cgrid, dim3(256), 0, s, part, vc->tensor_scale, out);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
 }
 
 extern "C" int msa_launch_sparse_decode(const msa_batch* bt, const void* q, int32_t q_dtype, float q_scale,
@@ -821,10 +928,10 @@ extern "C" int msa_launch_sparse_decode(const msa_batch* bt, const void* q, int3
   const int B = bt->num_reqs, R = bt->rows_per_req, P = bt->max_pages_per_req;
   if (kc->dtype == MSA_NVFP4)
     return launch_attend<false, false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
-                                       (int32_t*)cnt, topk, out, s);
+                                       (int32_t*)cnt, topk, out, (float*)workspace, s);
   if (kc->dtype == MSA_FP8_E4M3)
     return launch_attend<false, true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
-                                      (int32_t*)cnt, topk, out, s);
+                                      (int32_t*)cnt, topk, out, (float*)workspace, s);
   const int S = (int)f32_splits(bt, topk);
   float* part_o = (float*)workspace;
   float* part_ml = part_o + (size_t)B * kGroups * S * R * kHpg * kDim;
@@ -867,10 +974,10 @@ extern "C" int msa_launch_sparse_decode_noalloc(const msa_batch* bt, const void*
 extern "C" int msa_launch_select_decode(const msa_batch* bt, const float* block_scores, int32_t topk,
                                         const void* q, float q_scale, float sm_scale, const msa_cache* kc,
                                         const msa_cache* vc, int32_t* sel, int32_t* cnt, float* out,
-                                        hipStream_t s) {
+                                        void* workspace, hipStream_t s) {
   if (kc->dtype == MSA_FP8_E4M3)
     return launch_attend<true, true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
-                                     out, s);
+                                     out, (float*)workspace, s);
   return launch_attend<true, false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
-                                    out, s);
+                                    out, (float*)workspace, s);
 }

@@ -47,9 +47,10 @@ int msa_launch_prefill_index(const msa_batch* b, const void* q_idx, float q_scal
 int msa_launch_topk(const msa_batch* b, const float* scores, int32_t token_level, int32_t topk, int32_t* sel,
                     int32_t* cnt, hipStream_t stream);
 size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk);
+size_t msa_split_partials_bytes(const msa_batch* b);
 int msa_launch_select_decode(const msa_batch* b, const float* block_scores, int32_t topk, const void* q,
                              float q_scale, float sm_scale, const msa_cache* kc, const msa_cache* vc, int32_t* sel,
-                             int32_t* cnt, float* out, hipStream_t stream);
+                             int32_t* cnt, float* out, void* workspace, hipStream_t stream);
 int msa_launch_sparse_decode_noalloc(const msa_batch* b, const void* q, int32_t q_dtype, float q_scale,
                                      float sm_scale, const msa_cache* kc, const msa_cache* vc, const int32_t* sel,
                                      const int32_t* cnt, int32_t topk, float* out, hipStream_t stream);

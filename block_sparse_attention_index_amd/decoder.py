@@ -64,7 +64,7 @@ class MsaDecoder:
     def select_attend(self, q, q_scale, sm_scale, stream=None):
         """Steps 3+4 in one launch (NVFP4 caches)."""
         msa_select_decode(self.batch, self.block_scores, self.topk, q, self.q_dtype, q_scale, sm_scale, self.k,
-                          self.v, self.sel, self.cnt, self.out, stream)
+                          self.v, self.sel, self.cnt, self.out, self.workspace, stream)
 
     def step(self, q_idx, q, q_scale, sm_scale, new_tokens=None, stream=None, fused=True):
         """new_tokens: optional (k [n][4][128], v [n][4][128], idx [n][128], slots [n]) FP32 rows to insert first.

@@ -250,7 +250,15 @@ int msa_insert_index_score(const msa_batch* batch, const float* k_new, const flo
 int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t scores_are_token_level,
                            int32_t topk, int32_t* sel_blocks, int32_t* sel_count, hipStream_t stream);
 
-/* Workspace bytes msa_sparse_decode needs for this batch and topk (host call). */
+/*
+ * Workspace bytes msa_sparse_decode (and msa_select_decode, when given one)
+ * needs for this batch and topk, on the current device (host call; 0 for an
+ * invalid batch).  F32 caches keep per-block partial results there; NVFP4 and
+ * FP8 caches keep the partials of rows whose selected blocks are spread over
+ * 2 or 4 workgroups, which a batch gets when one workgroup per (request,
+ * row, group) would leave that many times the CUs idle (at most one float
+ * partial of 8 x 130 values per workgroup the device's CUs can hold).
+ */
 size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk);
 
 /*
@@ -261,9 +269,11 @@ size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk);
  *   out[b][r][h] = sum_t softmax_t(sm_scale * q_h . K_g[t]) V_g[t].
  * q: [B][R][4*8][128], FP8 E4M3 bytes (times q_scale) with NVFP4 caches or
  * FP32 with F32 caches.  out: [B][R][32][128] FP32; rows with no selected
- * block get zeros.  workspace: device, >= msa_workspace_bytes() (used
- * by the F32 route for per-block partial results; no initial contents
- * needed).  Two calls that share a workspace must not run concurrently.
+ * block get zeros.  workspace: device, >= msa_workspace_bytes() (per-block
+ * partial results of the F32 route, and of NVFP4 / FP8 rows split over
+ * several workgroups, merged by a second launch in a fixed order; no initial
+ * contents needed).  Two calls that share a workspace must not run
+ * concurrently.
  * With NVFP4 or FP8 caches R may be up to MSA_MAX_PREFILL_ROWS (each row of a
  * prefill chunk attends to its own selection).
  */
@@ -278,16 +288,16 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
  * attention as msa_sparse_decode, same arguments without the workspace, same
  * results.  Scratch memory comes from a fixed array inside the library, one
  * per GPU, of MSA_NOALLOC_SCRATCH_BYTES (4 MiB), held from the first call on
- * a GPU until the process ends; the call itself allocates nothing.  Only
- * F32 caches use scratch memory (NVFP4 and FP8 caches need none, for any
- * batch): an F32 batch whose msa_workspace_bytes() exceeds that size returns
- * MSA_ERR_WORKSPACE (4 MiB holds 15 one-row requests at topk 16, the partial
- * results of every selected block).  Every call on a GPU shares that GPU's
- * array, and nothing in it needs initial contents (each call writes every
- * partial it reads).  Two calls that may
- * overlap on one GPU (different streams, or different host threads) race and
- * must not be issued.  Errors as msa_sparse_decode; a failed device query
- * returns MSA_ERR_HIP.
+ * a GPU until the process ends; the call itself allocates nothing.  F32
+ * caches keep the partial results of every selected block there: an F32
+ * batch needing more than that size returns MSA_ERR_WORKSPACE (4 MiB holds 15
+ * one-row requests at topk 16).  NVFP4 and FP8 caches keep only the partials
+ * of split rows (at most 8 x 130 floats per workgroup the CUs can hold, about
+ * 1 MiB on 256 CUs), so every batch fits.  Every call on a GPU shares that
+ * GPU's array, and nothing in it needs initial contents (each call writes
+ * every partial it reads).  Two calls that may overlap on one GPU (different
+ * streams, or different host threads) race and must not be issued.  Errors as
+ * msa_sparse_decode; a failed device query returns MSA_ERR_HIP.
  */
 int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
                               const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
@@ -299,12 +309,17 @@ int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_d
  * msa_sparse_decode, per (request, group) in one workgroup, so the selected
  * sets never make a round trip through memory between the two steps.
  * sel_blocks / sel_count are written as msa_block_maxpool_topk writes them;
- * out as msa_sparse_decode writes it.  No workspace.
+ * out as msa_sparse_decode writes it.  workspace (device, may be NULL; else
+ * at least msa_workspace_bytes() bytes, MSA_ERR_WORKSPACE otherwise): with
+ * it, a batch that would leave CUs idle spreads each row's selected blocks
+ * over several workgroups and merges their partial results in a second
+ * launch, and out then equals msa_sparse_decode's bit for bit; without it,
+ * one workgroup per row.
  */
 int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t topk, const void* q,
                       int32_t q_dtype, float q_scale, float sm_scale, const msa_cache* k_cache,
-                      const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out,
-                      hipStream_t stream);
+                      const msa_cache* v_cache, int32_t* sel_blocks, int32_t* sel_count, float* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Measurement aid, not a step of the path: read `bytes` bytes of device

@@ -6,6 +6,7 @@
 // the documented status and launch nothing.
 #include "../../block_sparse_attention_index_amd/csrc/msa_api.hip"
 
+#include <algorithm>
 #include <cstdio>
 #include <limits>
 
@@ -26,7 +27,7 @@ STUB(msa_launch_insert_index_score, const msa_batch*, const float*, const float*
      const msa_cache*, const msa_cache*, const msa_cache*, float*, float*, hipStream_t)
 STUB(msa_launch_topk, const msa_batch*, const float*, int32_t, int32_t, int32_t*, int32_t*, hipStream_t)
 STUB(msa_launch_select_decode, const msa_batch*, const float*, int32_t, const void*, float, float, const msa_cache*,
-     const msa_cache*, int32_t*, int32_t*, float*, hipStream_t)
+     const msa_cache*, int32_t*, int32_t*, float*, void*, hipStream_t)
 STUB(msa_launch_sparse_decode_noalloc, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, hipStream_t)
 STUB(msa_launch_stream_read, const void*, int64_t, int32_t, uint32_t*, hipStream_t)
@@ -34,6 +35,11 @@ STUB(msa_launch_sparse_decode, const msa_batch*, const void*, int32_t, float, fl
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, void*, hipStream_t)
 extern "C" size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk) {
   return (size_t)b->num_reqs * 4 * (size_t)b->rows_per_req * 8 * (size_t)topk * 130 * 4;
+}
+extern "C" size_t msa_split_partials_bytes(const msa_batch* b) {  // the split rule for 256 CUs
+  const size_t rows = (size_t)b->num_reqs * b->rows_per_req * 4;
+  const size_t S = rows * 4 <= 256 ? 4 : (rows * 2 <= 256 ? 2 : 1);
+  return S > 1 ? rows * S * 1040 * 4 : 0;
 }
 
 static int failures = 0;
@@ -111,7 +117,8 @@ int main() {
 
   // attention
   const size_t ws = msa_workspace_bytes(&bt, 16);
-  expect(ws == msa_decode_partials_bytes(&bt, 16) ? MSA_OK : -99, MSA_OK, 0, "workspace size");
+  expect(ws == std::max(msa_decode_partials_bytes(&bt, 16), msa_split_partials_bytes(&bt)) ? MSA_OK : -99, MSA_OK, 0,
+         "workspace size");
   expect(msa_workspace_bytes(nullptr, 16) == 0 ? MSA_OK : -99, MSA_OK, 0, "workspace size of no batch");
   expect(msa_sparse_decode(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, p, ws, nullptr), MSA_OK, 1,
          "decode ok");
@@ -121,9 +128,13 @@ int main() {
          MSA_ERR_INVALID_ARG, 0, "decode sm_scale");
   expect(msa_sparse_decode(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &vc, &kc, i32, i32, 16, f, p, ws, nullptr),
          MSA_ERR_UNSUPPORTED, 0, "decode swapped layouts");
-  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, f, nullptr), MSA_OK, 1,
-         "select_decode ok");
-  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, nullptr, f, nullptr),
+  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, f, nullptr, 0, nullptr),
+         MSA_OK, 1, "select_decode without workspace");
+  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, f, p, ws, nullptr), MSA_OK,
+         1, "select_decode with workspace");
+  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, f, p, ws - 1, nullptr),
+         MSA_ERR_WORKSPACE, 0, "select_decode small workspace");
+  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, nullptr, f, nullptr, 0, nullptr),
          MSA_ERR_INVALID_ARG, 0, "select_decode no counts");
   expect(msa_sparse_decode_noalloc(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, nullptr), MSA_OK, 1,
          "noalloc ok");
@@ -139,7 +150,7 @@ int main() {
          "noalloc f32 ok");
   expect(msa_sparse_decode_noalloc(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, nullptr, 16, f, nullptr),
          MSA_ERR_INVALID_ARG, 0, "noalloc no counts");
-  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &k32, &k32, i32, i32, f, nullptr),
+  expect(msa_select_decode(&bt, f, 16, p, MSA_FP8_E4M3, 1.0f, 0.088f, &k32, &k32, i32, i32, f, nullptr, 0, nullptr),
          MSA_ERR_UNSUPPORTED, 0, "select_decode f32");
 
   // fused insert + index

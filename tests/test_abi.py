@@ -113,11 +113,11 @@ def test_host_validation_without_gpu(lib):
     assert lib.msa_quantize_e4m3(fake, C.c_int64(4), C.c_float(0.0), fake, None) == -1
     # fused selection + attention: NVFP4 only, topk range, null outputs
     assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(f32k),
-                                 C.byref(f32k), fake, fake, fake, None) == -2
+                                 C.byref(f32k), fake, fake, fake, None, C.c_size_t(0), None) == -2
     assert lib.msa_select_decode(C.byref(good), fake, 65, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k),
-                                 C.byref(v), fake, fake, fake, None) == -1
+                                 C.byref(v), fake, fake, fake, None, C.c_size_t(0), None) == -1
     assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k),
-                                 C.byref(v), fake, fake, None, None) == -1
+                                 C.byref(v), fake, fake, None, None, C.c_size_t(0), None) == -1
     # fused insert + index: NVFP4 caches, FP8 queries, every row pointer present, value cache dim-major
     f32i = Cache(0, 0, 1, 16, 1.0, fake)
     ins = lib.msa_insert_index_score
@@ -159,7 +159,7 @@ def test_layout_rules_without_gpu(lib):
                                  C.byref(v8), fake, fake, 16, fake, fake, C.c_size_t(1 << 30), None) == -2
     # keys and values of one format; the fused insert + index needs all three caches in one format
     assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k8),
-                                 C.byref(v_nv), fake, fake, fake, None) == -2
+                                 C.byref(v_nv), fake, fake, fake, None, C.c_size_t(0), None) == -2
     assert lib.msa_insert_index_score(C.byref(good), fake, fake, fake, fake, 1, C.c_float(1.0), C.byref(k8),
                                       C.byref(v8), C.byref(i_nv), fake, None, None) == -2
     assert lib.msa_kv_insert_nvfp4(fake, None, None, fake, 4, C.byref(k8), None, None, None) == -2
