@@ -310,10 +310,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--config", type=int, default=CONFIG_ID, choices=[2, 3, 4, 5, 6],
+    ap.add_argument("--config", type=int, default=CONFIG_ID, choices=[2, 3, 4, 5, 6, 7],
                     help="workload: 3 = 32 requests at 64K-192K tokens (the default, the metric's own); "
                          "2 = 8 x 32K; 4 = 16 requests x 4 speculative rows; 5 = 64 requests sharing a "
-                         "256K-token prefix; 6 = prefill, 4 prompts of 64K tokens whose last 2,048 form the chunk")
+                         "256K-token prefix; 6 = prefill, 4 prompts of 64K tokens whose last 2,048 form the chunk; "
+                         "7 = 32 x 8K with top-64 (every block selected: the forced-dense traffic check)")
     ap.add_argument("--kv", choices=["nvfp4", "fp8"], default="nvfp4",
                     help="cache format of keys, values and index keys (default NVFP4, the metric's own)")
     ap.add_argument("--replicas", type=int, default=2)
@@ -373,19 +374,30 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    # an event after every replay (every step without graphs) gives the spread of step times
+    marks = []
     with torch.cuda.stream(stream):
         t_start.record(stream)
         if use_graph:
             for _ in range(args.steps // per_graph):
                 graph.replay()
+                marks.append(torch.cuda.Event(enable_timing=True))
+                marks[-1].record(stream)
         else:
             for i in range(args.steps):
                 run_step(i, stream)
+                marks.append(torch.cuda.Event(enable_timing=True))
+                marks[-1].record(stream)
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+    per = per_graph if use_graph else 1
+    spans = [t_start.elapsed_time(marks[0])] + [a_.elapsed_time(b_) for a_, b_ in zip(marks[:-1], marks[1:])]
+    step_us = np.array(spans) * 1e3 / per
+    step_spread = {"p10": float(np.percentile(step_us, 10)), "median": float(np.median(step_us)),
+                   "p90": float(np.percentile(step_us, 90)), "samples": len(spans), "steps_per_sample": per}
     log(f"timed {args.steps} steps ({per_graph} per graph): {ms_step * 1e3:.1f} us/step (events), "
         f"wall {wall / args.steps * 1e6:.1f} us/step")
 
@@ -430,6 +442,36 @@ def main():
         us[name] = a_.elapsed_time(b_) * 1e3 / (replays * reps)
     log("per-kernel us (graph of back-to-back launches): " + ", ".join(f"{k} {v:.1f}" for k, v in us.items()))
 
+    # ---- the practical HBM read ceiling in this process: a plain streaming read of as many
+    # bytes as the index scan reads, with the scan's load form, alternating two buffers
+    # (together larger than the 256 MB Infinity Cache), timed like the kernels above
+    stream_ref = None
+    if not prefill:
+        nbytes_idx = algorithmic_bytes(wl, decs[0].sel.cpu().numpy(), decs[0].cnt.cpu().numpy())["index"]
+        n16 = nbytes_idx // 16 * 16
+        bufs = [torch.empty(n16, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        for b_ in bufs:
+            b_.fill_(1)
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        wgs = 65535  # the best grid of a sweep on this part (7.05 TB/s over 310 MB; 6.6 TB/s at 1,024)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(reps):
+                    M.msa_debug_stream_read(bufs[i % 2], wgs, sink, stream)
+            g.replay()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(replays):
+                g.replay()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        st_us = a_.elapsed_time(b_) * 1e3 / (replays * reps)
+        stream_ref = {"kernel": "stream_read_kernel (16-byte non-temporal loads, 65,535 workgroups)",
+                      "bytes_per_launch": int(n16), "avg_launch_us": st_us, "achieved_GBps": n16 / st_us / 1e3}
+        del bufs
+        log(f"streaming read of {n16 / 1e6:.1f} MB: {st_us:.1f} us = {n16 / st_us / 1e3:.0f} GB/s")
+
     sel = decs[0].sel.cpu().numpy()
     cnt = decs[0].cnt.cpu().numpy()
     nbytes = algorithmic_bytes(wl, sel, cnt)
@@ -441,6 +483,8 @@ def main():
     prefill_flops = 2 * 128 * 128 * pages_scored * wl.R * 4
     prefix_flops = 2 * 128 * 128 * P * wl.B * wl.R * 4  # dims x tokens x index queries
     step_gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
+    if stream_ref is not None:
+        stream_ref["index_scan_frac"] = (nbytes["index"] / (us["index"] * 1e-6) / 1e9) / stream_ref["achieved_GBps"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -475,7 +519,8 @@ def main():
                       "achieved": prefill_flops / (us["index"] * 1e-6) / 1e12, "peak": PEAK_F16_MFMA_TFLOPS,
                       "unit": "TFLOP/s", "frac": prefill_flops / (us["index"] * 1e-6) / 1e12 / PEAK_F16_MFMA_TFLOPS,
                       "traffic": None, "index_GBps": idx_gbps} if prefill else
-                     {"bound": "hbm", "kernel": f"index_{wl.cache}_kernel with the insert fused in (steps 0-2)",
+                     {"bound": "hbm", "scope": "dominant kernel, per launch (the whole step: step_hbm)",
+                      "kernel": f"index_{wl.cache}_kernel with the insert fused in (steps 0-2)",
                       "achieved": idx_gbps,
                       "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS,
                       "traffic": recorded_traffic() if headline else None,
@@ -490,8 +535,11 @@ def main():
             "bound": "mfma", "flops_per_launch": prefix_flops, "avg_launch_us": us["prefix"],
             "achieved": prefix_flops / (us["prefix"] * 1e-6) / 1e12, "peak": PEAK_F16_MFMA_TFLOPS,
             "unit": "TFLOP/s", "frac": prefix_flops / (us["prefix"] * 1e-6) / 1e12 / PEAK_F16_MFMA_TFLOPS},
-        "step_hbm": {"algorithmic_bytes": nbytes["total"], "achieved_GBps": step_gbps,
+        "step_hbm": {"scope": "whole step (insert, index, selection, attention) per layer-step",
+                     "algorithmic_bytes": nbytes["total"], "achieved_GBps": step_gbps,
                      "frac_of_peak": step_gbps / PEAK_HBM_GBPS, "kv_tokens_read": nbytes["kv_tokens"]},
+        "step_us": step_spread,
+        "stream_read": stream_ref,
         "kernel_us": us,
         "cpu_baseline": cpu,
     }

@@ -46,6 +46,10 @@ CONFIGS = {
             cache="nvfp4", table="shuffled"),
     # prefill: the last 2,048 tokens of 64K-token prompts scored, selected and attended as one chunk
     6: dict(name="prefill_b4_2k_chunk_64k", B=4, R=2048, lens=("fixed", 65536), cache="nvfp4", table="shuffled"),
+    # a measurement aid, not a workload of the pages: every block selected (64 blocks, top-64), so the
+    # attention reads the whole K/V and its traffic can be set against the index scan's (8:1 by bytes)
+    7: dict(name="forced_dense_b32_8k_top64", B=32, R=1, lens=("fixed", 8192), cache="nvfp4", table="shuffled",
+            topk=64),
 }
 
 
@@ -136,6 +140,7 @@ def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int
         n = own_pages[b]
         table[b, prefix_pages:prefix_pages + n] = perm[nxt:nxt + n]
         nxt += n
+    topk = cfg.get("topk", topk)
     kind = cfg["cache"] if cache is None else cache
     assert kind in ("f32", "nvfp4", "fp8")
     ts = {"nvfp4": NVFP4_TENSOR_SCALE, "fp8": FP8_TENSOR_SCALE, "f32": 1.0}[kind]
