@@ -319,8 +319,7 @@ __device__ __forceinline__ void attend_block(const KR& kr, const VR& vr, const h
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) mx = fmaxf(mx, Sacc[qt][m][qq]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max4(mx);
     const float m_new = fmaxf(st.m[qt], mx);
     // exponent base: a column with nothing visible yet keeps m = -inf and uses 0,
     // so exp2(-inf - base) = 0 throughout

@@ -116,13 +116,36 @@ __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, row_mask, 0xf, false);
 }
 
-// Max within each 16-lane row, in every lane of the row: pairs and quads by
-// quad permutes, then half-row and row mirrors.
+// Running maximum of a max-pool: m (which starts at -inf and so is never NaN)
+// against a score x, skipping a NaN x.  The median of (m, x, +inf) is
+// max(m, x) for a number x, and the hardware median of operands that include
+// a NaN is the minimum of the others, m; the compiler folds chains of these
+// into v_max3_f32, whose IEEE-mode result skips quiet NaN operands the same
+// way.  (fmaxf means the same, but its lowering first quiets every operand
+// that is not known to be canonical -- one extra instruction per matrix-core
+// result.)
+__device__ __forceinline__ float pool_max(float m, float x) { return __builtin_amdgcn_fmed3f(m, x, __builtin_inff()); }
+
+// fmaxf over lanes l, l^16, l^32 and l^48 (the four 16-lane rows) in every
+// lane: gfx950's row swaps, which run on the vector ALU, instead of permutes
+// through the LDS unit.  Swapping the upper half of one copy with the lower
+// half of another leaves each lane's partner l^32 in one of the two results
+// and the lane's own value in the other (likewise odd and even rows for
+// l^16), so the max of the pair is the max over both lanes.
+__device__ __forceinline__ float rows_max4(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Max within each 16-lane row, in every lane of the row (no lane NaN): pairs
+// and quads by quad permutes, then half-row and row mirrors.
 __device__ __forceinline__ float wave_max16(float v) {
-  v = fmaxf(v, __uint_as_float(dpp_mov<0xB1, 0xf>(__float_as_uint(v))));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, __uint_as_float(dpp_mov<0x4E, 0xf>(__float_as_uint(v))));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, __uint_as_float(dpp_mov<0x141, 0xf>(__float_as_uint(v))));  // row_half_mirror
-  v = fmaxf(v, __uint_as_float(dpp_mov<0x140, 0xf>(__float_as_uint(v))));  // row_mirror
+  v = pool_max(v, __uint_as_float(dpp_mov<0xB1, 0xf>(__float_as_uint(v))));   // quad_perm [1,0,3,2]
+  v = pool_max(v, __uint_as_float(dpp_mov<0x4E, 0xf>(__float_as_uint(v))));   // quad_perm [2,3,0,1]
+  v = pool_max(v, __uint_as_float(dpp_mov<0x141, 0xf>(__float_as_uint(v))));  // row_half_mirror
+  v = pool_max(v, __uint_as_float(dpp_mov<0x140, 0xf>(__float_as_uint(v))));  // row_mirror
   return v;
 }
 

@@ -35,6 +35,7 @@
 
 #include "msa_device.h"
 #include "msa_kernels.h"
+#include "msa_scan.h"
 
 namespace msa {
 
@@ -86,17 +87,18 @@ __device__ __forceinline__ void load_prefix_part(const uint8_t* __restrict__ sla
   }
 }
 
-__device__ __forceinline__ void store_prefix_part(const PrefixPart& p, int wave, int lane, h8* __restrict__ img) {
+// Piece `piece` (0..3) of the part into the LDS image: M-tile wave + 4*(piece/2),
+// k-steps 2*(piece%2) and 2*(piece%2) + 1 (one E4M3 scale group).
+__device__ __forceinline__ void store_prefix_piece(const PrefixPart& p, int wave, int lane, h8* __restrict__ img,
+                                                   int piece) {
+  const int h = piece >> 1, m = wave + 4 * h;
+  const uint32_t sw = p.ks[h];
+  const _Float16 s = e4m3x2_to_h2<false>(sw)[piece & 1];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int m = wave + 4 * h;
-    const h2 sc = e4m3x2_to_h2<false>(p.ks[h]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t w = ks == 0 ? p.kc[h].x : ks == 1 ? p.kc[h].y : ks == 2 ? p.kc[h].z : p.kc[h].w;
-      const _Float16 s = ks < 2 ? sc[0] : sc[1];
-      img[(m * 4 + ks) * 64 + lane] = e2m1x8_to_h8(w) * h8{s, s, s, s, s, s, s, s};
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int ks = 2 * (piece & 1) + i;
+    const uint32_t w = ks == 0 ? p.kc[h].x : ks == 1 ? p.kc[h].y : ks == 2 ? p.kc[h].z : p.kc[h].w;
+    img[(m * 4 + ks) * 64 + lane] = e2m1x8_to_h8(w) * h8{s, s, s, s, s, s, s, s};
   }
 }
 
@@ -119,19 +121,24 @@ __device__ __forceinline__ void load_prefix_part(const uint8_t* __restrict__ sla
   }
 }
 
-__device__ __forceinline__ void store_prefix_part(const PrefixPart8& p, int wave, int lane, h8* __restrict__ img) {
+__device__ __forceinline__ void store_prefix_piece(const PrefixPart8& p, int wave, int lane, h8* __restrict__ img,
+                                                   int piece) {
+  const int h = piece >> 1, m = wave + 4 * h;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int m = wave + 4 * h;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4& q = p.kc[h][ks >> 1];
-      const uint32_t lo = (ks & 1) ? q.z : q.x, hi = (ks & 1) ? q.w : q.y;
-      const h2 x0 = e4m3x2_to_h2<false>(lo), x1 = e4m3x2_to_h2<true>(lo);
-      const h2 x2 = e4m3x2_to_h2<false>(hi), x3 = e4m3x2_to_h2<true>(hi);
-      img[(m * 4 + ks) * 64 + lane] = h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int ks = 2 * (piece & 1) + i;
+    const uint4& q = p.kc[h][ks >> 1];
+    const uint32_t lo = (ks & 1) ? q.z : q.x, hi = (ks & 1) ? q.w : q.y;
+    const h2 x0 = e4m3x2_to_h2<false>(lo), x1 = e4m3x2_to_h2<true>(lo);
+    const h2 x2 = e4m3x2_to_h2<false>(hi), x3 = e4m3x2_to_h2<true>(hi);
+    img[(m * 4 + ks) * 64 + lane] = h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
   }
+}
+
+template <typename Part>
+__device__ __forceinline__ void store_prefix_part(const Part& p, int wave, int lane, h8* __restrict__ img) {
+#pragma unroll
+  for (int piece = 0; piece < 4; ++piece) store_prefix_piece(p, wave, lane, img, piece);
 }
 
 // Scores of one page (its LDS image) for this wave's columns; mx = per-lane
@@ -140,13 +147,15 @@ __device__ __forceinline__ void store_prefix_part(const PrefixPart8& p, int wave
 // once the instruction has completed, so reading each pair's accumulators
 // right after its last MFMA would drain the matrix pipe eight times a page:
 // instead the accumulators are double-buffered and pair p is max-pooled after
-// the MFMAs of pair p+1 have been issued.  MASK: some column does not see the
-// whole page (token t counts for column c only when t <= pos[c]).
-template <int NTILE, bool MASK, bool kTok>
+// the MFMAs of pair p+1 have been issued.  side(p) runs right after the
+// MFMAs of pair p are issued: vector work of the caller's (the next page's
+// dequantisation) that then overlaps them.  MASK: some column does not see
+// the whole page (token t counts for column c only when t <= pos[c]).
+template <int NTILE, bool MASK, bool kTok, typename Side>
 __device__ __forceinline__ void score_prefix_page(const h8* __restrict__ img, const h8 (&Q)[NTILE][4],
                                                   const int (&pos)[NTILE], int j, int lane, int col0, int ncols,
                                                   float out_scale, int64_t T, float* __restrict__ token_scores,
-                                                  float (&mx)[NTILE]) {
+                                                  float (&mx)[NTILE], Side&& side) {
   const int n = lane & 15, a = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NTILE; ++nt) mx[nt] = -__builtin_inff();
@@ -177,10 +186,10 @@ __device__ __forceinline__ void score_prefix_page(const h8* __restrict__ img, co
       for (int nt = 0; nt < NTILE; ++nt) {
         const v4f& x = ac[mm][nt];
         if (!MASK) {
-          mx[nt] = fmaxf(fmaxf(mx[nt], fmaxf(x[0], x[1])), fmaxf(x[2], x[3]));
+          mx[nt] = pool_max(pool_max(pool_max(pool_max(mx[nt], x[0]), x[1]), x[2]), x[3]);
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx[nt] = fmaxf(mx[nt], t0 + i <= pos[nt] ? x[i] : -__builtin_inff());
+          for (int i = 0; i < 4; ++i) mx[nt] = pool_max(mx[nt], t0 + i <= pos[nt] ? x[i] : -__builtin_inff());
         }
         if (kTok) {
           const int c = col0 + 16 * nt + n;
@@ -197,9 +206,11 @@ __device__ __forceinline__ void score_prefix_page(const h8* __restrict__ img, co
     }
   };
   multiply(0, acc[0]);
+  side(0);
 #pragma unroll
   for (int p = 1; p < 4; ++p) {
     multiply(2 * p, acc[p & 1]);
+    side(p);
     pool(2 * (p - 1), acc[(p - 1) & 1]);
   }
   pool(6, acc[1]);
@@ -211,19 +222,24 @@ __device__ __forceinline__ void score_prefix_page(const h8* __restrict__ img, co
 // below n_valid have a table entry; the rest score -inf), for query columns
 // col_lo + 64*NTILE*yt .. (below col_hi).  Column c = (b*R + r)*4 + g is
 // index query (b, r, g); its last visible token is pos = L_b - R + r.
-template <int NTILE, int PPW, bool kTok, bool FP8 = false>
+// between() runs once, workgroup-uniformly, while the first two pages are in
+// flight (or at once when the workgroup has no page).
+template <int NTILE, int PPW, bool kTok, bool FP8 = false, typename Between>
 __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ trow, const int32_t* __restrict__ lens,
                                                  int32_t max_pages, int32_t R, int32_t n_pages, int32_t n_valid,
                                                  int32_t col_lo, int32_t col_hi, int pg, int yt,
                                                  const uint8_t* __restrict__ q_idx, float out_scale,
                                                  const uint8_t* __restrict__ pages, int32_t num_pages,
                                                  float* __restrict__ block_scores, float* __restrict__ token_scores,
-                                                 h8 (&s_img)[2][kPfxImgH8]) {
+                                                 h8 (&s_img)[2][kPfxImgH8], Between&& between) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, a = lane >> 4;
   const int j0 = pg * PPW;
-  if (j0 >= n_pages) return;  // the whole workgroup
+  if (j0 >= n_pages) {  // the whole workgroup
+    between();
+    return;
+  }
   const int jn = min(PPW, n_pages - j0);
   const int ncols = col_hi;
   const int col0 = col_lo + yt * 64 * NTILE + wave * 16 * NTILE;
@@ -254,6 +270,7 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
   auto slab_of = [&](int k) { return pages + (int64_t)max(phys[k], 0) * kSlab; };
 #pragma unroll
   for (int k = 0; k < 2 && k < PPW; ++k) load_prefix_part(slab_of(k), wave, n, a, part[k]);
+  between();
 
   h8 Q[NTILE][4];
   load_prefix_queries<NTILE>(q_idx, col0, ncols, n, a, Q);
@@ -289,14 +306,23 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
     const int j = j0 + k;
     if (k + 2 < PPW)  // slot k%2 held page k, already in LDS
       load_prefix_part(slab_of(k + 2), wave, n, a, part[k & 1]);
+    // page k+1 -> the other image (last read before the previous barrier), a
+    // piece at a time between this page's matrix products
+    auto next_piece = [&](int piece) {
+      if (k + 1 < PPW) store_prefix_piece(part[(k + 1) & 1], wave, lane, s_img[(k + 1) & 1], piece);
+    };
+    bool pieces_done = false;
     if (has_cols) {
       float mx[NTILE];
       if (phys[k] >= 0) {
         const h8* img = s_img[k & 1];
         if (pmin >= j * kPage + kPage - 1)  // every column sees the whole page
-          score_prefix_page<NTILE, false, kTok>(img, Q, pos, j, lane, col0, ncols, out_scale, T, token_scores, mx);
+          score_prefix_page<NTILE, false, kTok>(img, Q, pos, j, lane, col0, ncols, out_scale, T, token_scores, mx,
+                                                next_piece);
         else
-          score_prefix_page<NTILE, true, kTok>(img, Q, pos, j, lane, col0, ncols, out_scale, T, token_scores, mx);
+          score_prefix_page<NTILE, true, kTok>(img, Q, pos, j, lane, col0, ncols, out_scale, T, token_scores, mx,
+                                               next_piece);
+        pieces_done = true;
       } else {
         // a page id outside the pool: no visible token
 #pragma unroll
@@ -317,15 +343,14 @@ __device__ __forceinline__ void dense_index_body(const int32_t* __restrict__ tro
       // block max: across the four lane groups holding the same column
 #pragma unroll
       for (int nt = 0; nt < NTILE; ++nt) {
-        float v = mx[nt];
-        v = fmaxf(v, __shfl_xor(v, 16));
-        v = fmaxf(v, __shfl_xor(v, 32));
+        const float v = rows_max4(mx[nt]);
         const int c = col0 + 16 * nt + n;
         if (a == 0 && c < ncols) block_scores[(int64_t)c * max_pages + j] = v * out_scale;
       }
     }
-    // page k+1 -> the other image (last read before the previous barrier)
-    if (k + 1 < PPW) store_prefix_part(part[(k + 1) & 1], wave, lane, s_img[(k + 1) & 1]);
+    if (!pieces_done)
+#pragma unroll
+      for (int piece = 0; piece < 4; ++piece) next_piece(piece);
     __syncthreads();
   }
 }
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int id = (int)blockIdx.x;
   dense_index_body<NTILE, PPW, kTok>(table, lens, max_pages, R, prefix_pages, prefix_pages, 0, B * R * kGroups,
                                      (id / (8 * ny)) * 8 + (id & 7), (id >> 3) % ny, q_idx, out_scale, pages,
-                                     num_pages, block_scores, token_scores, s_img);
+                                     num_pages, block_scores, token_scores, s_img, [] {});
 }
 
 // Prefill (many query rows per request): request b = blockIdx.y, all its
@@ -362,7 +387,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   dense_index_body<NTILE, PPW, kTok, FP8>(table + (int64_t)b * max_pages, lens, max_pages, R, max_pages,
                                      (L + kPage - 1) / kPage, b * ncols, (b + 1) * ncols,
                                      (id / (8 * ny)) * 8 + (id & 7), (id >> 3) % ny, q_idx, out_scale, pages,
-                                     num_pages, block_scores, token_scores, s_img);
+                                     num_pages, block_scores, token_scores, s_img, [] {});
+}
+
+// Decode with a shared prefix, the per-request scan fused in (one row per
+// request): each workgroup of the prefix product (NTILE = PPW = 4) also runs
+// scan chunk ids blockIdx.x, blockIdx.x + gridDim.x, ... (nvfp4_scan_chunk,
+// with its insert and -inf fill), between issuing its first two prefix pages
+// and consuming them.  The scan's dependent load round trips then run while
+// those pages are in flight, and the two passes share one launch instead of
+// running one after the other.
+template <bool INSERT, bool COMPACT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefix_scan_kernel(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t B,
+    int32_t prefix_pages, const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages,
+    int32_t num_pages, float* __restrict__ block_scores, int32_t ny, int32_t n_chunk_ids, NewRows NR) {
+  __shared__ h8 s_img[2][kPfxImgH8];
+  const int id = (int)blockIdx.x;
+  auto scan = [&] {
+    for (int c = id; c < n_chunk_ids; c += (int)gridDim.x)
+      nvfp4_scan_chunk<1, false, INSERT, false, COMPACT>(c, table, lens, max_pages, q_idx, out_scale, pages,
+                                                         num_pages, block_scores, nullptr, B, prefix_pages, NR);
+  };
+  dense_index_body<4, 4, false>(table, lens, max_pages, 1, prefix_pages, prefix_pages, 0, B * kGroups,
+                                (id / (8 * ny)) * 8 + (id & 7), (id >> 3) % ny, q_idx, out_scale, pages, num_pages,
+                                block_scores, nullptr, s_img, scan);
 }
 
 template <int NTILE, int PPW>
@@ -403,6 +452,37 @@ static int launch_prefill_cfg(const msa_batch* bt, const uint8_t* q, float out_s
     if (fp8) MSA_PREFILL_INDEX(false, true); else MSA_PREFILL_INDEX(false, false);
   }
 #undef MSA_PREFILL_INDEX
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The fused form when it applies: NVFP4, one row per request, block scores
+// only, and at most two scan chunk ids per workgroup (a suffix past the
+// prefix that is short next to it).  Returns 1 when it does not apply (the
+// caller launches the two passes), else 0, or -1 when the launch failed.
+int launch_prefix_scan(const msa_batch* bt, const uint8_t* q, float q_scale, const msa_cache* ic, float* bs,
+                       float* ts, const NewRows& nr, bool insert, hipStream_t s) {
+  const int p0 = bt->shared_prefix_pages;
+  if (p0 <= 0 || ts || bt->rows_per_req != 1 || ic->dtype != MSA_NVFP4) return 1;
+  const int chunks = (bt->max_pages_per_req - p0 + 3) / 4;
+  if (chunks <= 0) return 1;
+  const int B = bt->num_reqs;
+  const int ncols = B * kGroups;
+  const int ny = (ncols + 255) / 256;
+  const int npg8 = ((p0 + 3) / 4 + 7) / 8 * 8;
+  const int64_t grid = (int64_t)npg8 * ny, n_ids = (int64_t)chunks * B;
+  if (n_ids > 2 * grid) return 1;
+  const float out_scale = ic->tensor_scale * q_scale;
+#define MSA_PREFIX_SCAN(INS, CMP)                                                                                \
+  hipLaunchKernelGGL((prefix_scan_kernel<INS, CMP>), dim3((unsigned)grid), dim3(256), 0, s, bt->block_table,      \
+                     bt->ctx_lens, bt->max_pages_per_req, B, p0, q, out_scale, (const uint8_t*)ic->pages,          \
+                     ic->num_pages, bs, ny, (int32_t)n_ids, nr)
+  const bool compact = B <= 64;
+  if (insert) {
+    if (compact) MSA_PREFIX_SCAN(true, true); else MSA_PREFIX_SCAN(true, false);
+  } else {
+    if (compact) MSA_PREFIX_SCAN(false, true); else MSA_PREFIX_SCAN(false, false);
+  }
+#undef MSA_PREFIX_SCAN
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -109,6 +109,13 @@ CASES = {
     # shared prefix of 32 pages (4,096 tokens); 70 requests x 4 groups = 280 index queries span
     # several query tiles of the prefix kernel, the last one partial
     "prefix_wide": lambda: W.make_workload(5, seed=9, B=70, len_div=64),
+    # shared-prefix decode with the scan fused into the prefix launch (one row per request):
+    # 70 requests (unpacked scan ids, two query tiles) and 32 requests (packed ids), both with
+    # workgroups that run two scan chunk ids; contexts shorter than the prefix on the fused path
+    "prefix_fused_wide": lambda: W.make_workload(5, seed=37, B=70, len_div=16),
+    "prefix_fused_b32": lambda: W.make_workload(5, seed=38, B=32, len_div=32),
+    "prefix_short_r1": lambda: W.make_workload(5, seed=39, len_div=64, R=1,
+                                               lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 4500)]),
     # contexts shorter than, equal to and just past the shared prefix, two rows each
     "prefix_short": lambda: W.make_workload(5, seed=10, len_div=64, R=2,
                                             lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 9000)]),
@@ -305,7 +312,8 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
                                   "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
                                   "fp8_prefill", "fp8_prefill_r512", "many_reqs", "fp8_many_reqs", "r5", "r6", "r7",
-                                  "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "wide_table", "wide_table_r4"])
+                                  "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "wide_table", "wide_table_r4",
+                                  "prefix_fused_wide", "prefix_fused_b32", "prefix_short_r1"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -555,7 +563,7 @@ def test_full_step(M, oracle, case, fused):
 
 @pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged", "ragged_r4", "r8",
                                   "prefix_wide", "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "r5",
-                                  "r6", "r7", "fp8_r5", "fp8_r7", "union_r3", "topk32"])
+                                  "r6", "r7", "fp8_r5", "fp8_r7", "union_r3", "topk32", "prefix_fused_b32"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step_with_new_rows(M, oracle, case, fused):
     """The step inserts each request's R new rows itself (fused: insert + index in one
@@ -566,7 +574,8 @@ def test_full_step_with_new_rows(M, oracle, case, fused):
 
 
 @pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8", "many_reqs", "r5",
-                                  "r6", "r7", "fp8_r7", "union_r3"])
+                                  "r6", "r7", "fp8_r7", "union_r3", "cfg5_small", "prefix_fused_wide",
+                                  "prefix_fused_b32", "prefix_short_r1"])
 def test_insert_index_equals_separate_calls(M, oracle, case):
     """msa_insert_index_score: the caches bitwise as msa_kv_insert_nvfp4 writes them (and as
     the oracle writes them), and bitwise the block scores of msa_index_score after that insert."""
