@@ -84,13 +84,14 @@ __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
 // a context are empty).  Packed (COMPACT, B <= 64), workgroups B.. take only
 // the chunks below each newest one, request after request, from a prefix sum
 // of the B lengths held one per lane; false for the leftovers at the end.
-template <bool COMPACT>
+// PRE: lane_len holds lens[lane] (lanes below B), loaded by the caller.
+template <bool COMPACT, bool PRE = false>
 __device__ __forceinline__ bool chunk_of(int id, int B, const int32_t* __restrict__ lens, int max_pages, int p0,
-                                         int lane, int& b, int& L, int& latest, int& chunk) {
+                                         int lane, int& b, int& L, int& latest, int& chunk, int lane_len = 0) {
   if (COMPACT && id >= B) {
     int Ll = 0, nl = 0;
     if (lane < B) {
-      Ll = clamp_len(lens[lane], max_pages);
+      Ll = clamp_len(PRE ? lane_len : lens[lane], max_pages);
       const int np = (Ll + kPage - 1) / kPage;
       nl = np > p0 ? (np - 1 - p0) / 4 : 0;
     }
@@ -283,16 +284,17 @@ struct NewRows {
 // row per 16-element group, as the insert kernel does) and makes them visible
 // to its own waves before any page is read.  Control flow is uniform over the
 // workgroup up to the insert's barrier; a return ends the chunk, not the
-// caller.
-template <int R, bool kTok, bool INSERT = false, bool F16 = false, bool COMPACT = false>
+// caller.  PRE, lane_len: see chunk_of.
+template <int R, bool kTok, bool INSERT = false, bool F16 = false, bool COMPACT = false, bool PRE = false>
 __device__ __forceinline__ void nvfp4_scan_chunk(
     int id, const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages,
     const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
-    float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t B, int32_t p0, const NewRows& NR) {
+    float* __restrict__ block_scores, float* __restrict__ token_scores, int32_t B, int32_t p0, const NewRows& NR,
+    int lane_len = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int b, L, latest, chunk;
-  if (!chunk_of<COMPACT>(id, B, lens, max_pages, p0, lane, b, L, latest, chunk)) return;
+  if (!chunk_of<COMPACT, PRE>(id, B, lens, max_pages, p0, lane, b, L, latest, chunk, lane_len)) return;
   const int npb = (L + kPage - 1) / kPage;
   if (INSERT) {
     // new tokens [max(L - R, 0), L) that lie in this chunk's token range
