@@ -223,6 +223,7 @@ def bench_qkv(args):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_nvfp4_long_ctx_b32_64k_192k_hbm_traffic.md")
 INDEX_KERNEL_SOURCES = ["include/msa.h", "block_sparse_attention_index_amd/csrc/msa_device.h",
+                        "block_sparse_attention_index_amd/csrc/msa_scan.h",
                         "block_sparse_attention_index_amd/csrc/msa_index.hip"]
 
 

@@ -53,24 +53,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * kPage);
     constexpr int kPerTok = 9 * kDim;
     if (t0 < t1) {  // uniform over the workgroup
-      for (int e = threadIdx.x; e < (t1 - t0) * kPerTok; e += 256) {
-        const int tok = t0 + e / kPerTok;
+      // element e: token t0 + e / kPerTok, then its keys, values, index key.
+      // A batch of elements per thread: every source load issues before the
+      // first store (which could alias them), so a batch is one memory round
+      // -- sized for all of a chunk's elements up to four new rows.  The new
+      // tokens lie on at most two pages, whose table entries load with them.
+      const int ne = (t1 - t0) * kPerTok;
+      constexpr int kBatch = (kPerTok * R + 255) / 256 < 18 ? (kPerTok * R + 255) / 256 : 18;
+      const int pa = t0 / kPage;
+      const int ph_a = table[(int64_t)b * max_pages + pa], ph_b = table[(int64_t)b * max_pages + (t1 - 1) / kPage];
+      auto locate = [&](int e, int& tok, int& c, int& head, int& d) {
+        tok = t0 + e / kPerTok;
         int u = e % kPerTok;
-        const int c = u < 4 * kDim ? 0 : (u < 8 * kDim ? 1 : 2);
+        c = u < 4 * kDim ? 0 : (u < 8 * kDim ? 1 : 2);
         u -= c * 4 * kDim;
-        const int heads = c == 2 ? 1 : kGroups;
-        const int head = u / kDim, d = u % kDim;
-        const int r = tok - (L - R);
-        const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
-        const float x = src[(((int64_t)b * R + r) * heads + head) * kDim + d];
-        const int ph = table[(int64_t)b * max_pages + tok / kPage];
-        const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
-        uint8_t* slab = (c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages)) +
-                        ((int64_t)(valid ? ph : 0) * heads + head) * kFp8Slab;
-        const int off = tok & (kPage - 1);
-        const float ts = c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i);
-        const int layout = c == 0 ? MSA_TOKEN_MAJOR : (c == 1 ? MSA_DIM_MAJOR : MSA_HALF_ROWS);
-        if (valid) slab[fp8_offset(layout, off, d)] = (uint8_t)e4m3_encode(x / ts);
+        head = u / kDim;
+        d = u % kDim;
+      };
+      for (int e0 = threadIdx.x; e0 < ne; e0 += 256 * kBatch) {
+        float x[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          int tok, c, head, d;
+          locate(min(e0 + 256 * k, ne - 1), tok, c, head, d);
+          const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
+          x[k] = src[(((int64_t)b * R + tok - (L - R)) * (c == 2 ? 1 : kGroups) + head) * kDim + d];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int e = e0 + 256 * k;
+          if (e >= ne) break;
+          int tok, c, head, d;
+          locate(e, tok, c, head, d);
+          const int heads = c == 2 ? 1 : kGroups;
+          const int ph = tok / kPage == pa ? ph_a : ph_b;
+          const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
+          uint8_t* slab = (c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages)) +
+                          ((int64_t)(valid ? ph : 0) * heads + head) * kFp8Slab;
+          const float ts = c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i);
+          const int layout = c == 0 ? MSA_TOKEN_MAJOR : (c == 1 ? MSA_DIM_MAJOR : MSA_HALF_ROWS);
+          if (valid) slab[fp8_offset(layout, tok & (kPage - 1), d)] = (uint8_t)e4m3_encode(x[k] / ts);
+        }
       }
       // the index keys just written are read back by this workgroup's waves
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

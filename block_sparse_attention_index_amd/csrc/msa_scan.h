@@ -313,18 +313,21 @@ __device__ __forceinline__ void nvfp4_scan_chunk(
         grp = u & 7;
       };
       // a batch of rows per 16-lane row of threads: every source load issues
-      // before the first store (which could alias them) -- one memory round
-      constexpr int kBatch = 5;
+      // before the first store (which could alias them), so a batch is one
+      // memory round -- sized for all of a chunk's rows (one round) up to
+      // four new rows, two rounds beyond.  The new tokens lie on at most two
+      // pages (R <= 128), whose table entries load with the sources.
+      constexpr int kBatch = (72 * R + 15) / 16 < 18 ? (72 * R + 15) / 16 : 18;
+      const int pa = t0 / kPage;
+      const int ph_a = table[(int64_t)b * max_pages + pa], ph_b = table[(int64_t)b * max_pages + (t1 - 1) / kPage];
       for (int rb = threadIdx.x >> 4; rb < nrow; rb += 16 * kBatch) {
         float x[kBatch];
-        int ph[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
           int tok, c, head, grp;
           locate(min(rb + 16 * k, nrow - 1), tok, c, head, grp);
           const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
           x[k] = src[(((int64_t)b * R + tok - (L - R)) * (c == 2 ? 1 : kGroups) + head) * kDim + grp * 16 + i];
-          ph[k] = table[(int64_t)b * max_pages + tok / kPage];
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -332,11 +335,12 @@ __device__ __forceinline__ void nvfp4_scan_chunk(
           int tok, c, head, grp;
           locate(rb + 16 * k, tok, c, head, grp);
           const int heads = c == 2 ? 1 : kGroups;
-          const bool valid = ph[k] >= 0 && ph[k] < (c == 2 ? num_pages : NR.kv_num_pages);
+          const int ph = tok / kPage == pa ? ph_a : ph_b;
+          const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
           uint8_t* base = c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages);
           uint32_t code;
           const uint32_t sc = nvfp4_row_quantize(x[k], c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i), code);
-          nvfp4_row_store(base + ((int64_t)(valid ? ph[k] : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i,
+          nvfp4_row_store(base + ((int64_t)(valid ? ph : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i,
                           code, sc, c == 1, valid);
         }
       }
