@@ -392,10 +392,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 // Decode with a shared prefix, the per-request scan fused in (one row per
 // request): each workgroup of the prefix product (NTILE = PPW = 4) also runs
-// one or two scan chunk ids (nvfp4_scan_chunk, with its insert and -inf
-// fill), between issuing its first two prefix pages and consuming them.  The scan's dependent load round trips then run while
-// those pages are in flight, and the two passes share one launch instead of
-// running one after the other.
+// up to two scan chunk ids (nvfp4_scan_chunk, with its insert and -inf
+// fill), between issuing its first two prefix pages and consuming them.  The
+// scan's dependent load round trips then run while those pages are in
+// flight, and the two passes share one launch instead of running one after
+// the other.
 template <bool INSERT, bool COMPACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefix_scan_kernel(
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t B,
@@ -403,18 +404,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     int32_t num_pages, float* __restrict__ block_scores, int32_t ny, int32_t n_chunk_ids, NewRows NR) {
   __shared__ h8 s_img[2][kPfxImgH8];
   const int id = (int)blockIdx.x;
-  // chunk ids id and 2 * gridDim.x - 1 - id (the launcher keeps the count
-  // within twice the grid): the second ones, numbered from the end, fall on
-  // the last workgroups rather than on the first ones, which also insert
+  // chunk ids id and 2 * gridDim.x - 1 - id, those below n_chunk_ids (the
+  // launcher keeps the count within twice the grid; an id past it would map
+  // to a request past the batch in the unpacked chunk map): the second ones,
+  // numbered from the end, fall on the last workgroups rather than on the
+  // first ones, which also insert
   // (packed ids: the context lengths the chunk map needs are loaded first,
   // alongside the prefix's table entries, instead of inside the scan's chain)
   const int lane = threadIdx.x & 63;
   const int lane_len = COMPACT && lane < B ? lens[lane] : 0;
   auto scan = [&] {
     const int G = (int)gridDim.x;
-    nvfp4_scan_chunk<1, false, INSERT, false, COMPACT, COMPACT>(id, table, lens, max_pages, q_idx, out_scale, pages,
-                                                                num_pages, block_scores, nullptr, B, prefix_pages, NR,
-                                                                lane_len);
+    if (id < n_chunk_ids)
+      nvfp4_scan_chunk<1, false, INSERT, false, COMPACT, COMPACT>(id, table, lens, max_pages, q_idx, out_scale, pages,
+                                                                  num_pages, block_scores, nullptr, B, prefix_pages,
+                                                                  NR, lane_len);
     if (2 * G - 1 - id < n_chunk_ids)
       nvfp4_scan_chunk<1, false, INSERT, false, COMPACT, COMPACT>(2 * G - 1 - id, table, lens, max_pages, q_idx,
                                                                   out_scale, pages, num_pages, block_scores, nullptr, B,

@@ -116,6 +116,9 @@ CASES = {
     "prefix_fused_b32": lambda: W.make_workload(5, seed=38, B=32, len_div=32),
     "prefix_short_r1": lambda: W.make_workload(5, seed=39, len_div=64, R=1,
                                                lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 4500)]),
+    # 65 requests (unpacked scan ids) whose suffixes fit one chunk: fewer scan chunk ids (65) than
+    # fused workgroups (128), so most workgroups run no chunk
+    "prefix_fused_sparse_ids": lambda: W.make_workload(5, seed=40, len_div=8, R=1, lengths=[8 * 32868] * 65),
     # contexts shorter than, equal to and just past the shared prefix, two rows each
     "prefix_short": lambda: W.make_workload(5, seed=10, len_div=64, R=2,
                                             lengths=[64 * n for n in (0, 1, 100, 4095, 4096, 4097, 4200, 9000)]),
@@ -313,7 +316,8 @@ def test_debug_dequant_exhaustive(M, oracle, layout, mode):
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
                                   "fp8_prefill", "fp8_prefill_r512", "many_reqs", "fp8_many_reqs", "r5", "r6", "r7",
                                   "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "wide_table", "wide_table_r4",
-                                  "prefix_fused_wide", "prefix_fused_b32", "prefix_short_r1"])
+                                  "prefix_fused_wide", "prefix_fused_b32", "prefix_short_r1",
+                                  "prefix_fused_sparse_ids"])
 def test_index_scores(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -575,7 +579,7 @@ def test_full_step_with_new_rows(M, oracle, case, fused):
 
 @pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r8", "many_reqs", "r5",
                                   "r6", "r7", "fp8_r7", "union_r3", "cfg5_small", "prefix_fused_wide",
-                                  "prefix_fused_b32", "prefix_short_r1"])
+                                  "prefix_fused_b32", "prefix_short_r1", "prefix_fused_sparse_ids"])
 def test_insert_index_equals_separate_calls(M, oracle, case):
     """msa_insert_index_score: the caches bitwise as msa_kv_insert_nvfp4 writes them (and as
     the oracle writes them), and bitwise the block scores of msa_index_score after that insert."""
