@@ -160,6 +160,10 @@ CASES = {
     "topk8": lambda: W.make_workload(3, seed=30, B=4, len_div=24, topk=8),
     "topk32": lambda: W.make_workload(3, seed=31, B=4, len_div=12, topk=32),
     "topk32_r4": lambda: W.make_workload(4, seed=32, B=3, len_div=24, R=4, topk=32),
+    # the largest and smallest selections: 64 blocks (the whole union when a context has at most 64)
+    # and the latest block alone
+    "topk64": lambda: W.make_workload(3, seed=41, B=4, len_div=6, topk=64),
+    "topk1": lambda: W.make_workload(3, seed=42, B=4, len_div=48, topk=1),
     "fp8_topk8": lambda: W.make_workload(3, seed=33, B=3, len_div=24, topk=8, cache="fp8"),
     # a block table wider than 3,072 entries (short contexts): the selection reads its scores from
     # memory on demand and attention reads the table row from memory instead of LDS
@@ -556,7 +560,7 @@ def _sampled_caches(oracle, wl, rows):
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
                                   "union_r4", "union_r2", "fp8_prefill", "fp8_prefill_r512", "r5", "r6", "r7",
                                   "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "union_r7", "topk8", "topk32",
-                                  "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4"])
+                                  "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
@@ -601,7 +605,7 @@ def test_insert_index_equals_separate_calls(M, oracle, case):
 
 @pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8", "union_r4", "union_r2", "r5", "r6",
                                   "r7", "fp8_r6", "union_r3", "union_r7", "topk8", "topk32", "topk32_r4",
-                                  "fp8_topk8", "wide_table", "wide_table_r4"])
+                                  "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"])
 def test_select_decode_equals_separate_calls(M, oracle, case):
     """msa_select_decode: same selection as msa_block_maxpool_topk and bitwise the same
     output as msa_sparse_decode on that selection."""
@@ -701,6 +705,21 @@ def test_full_size_config3_sampled(M, oracle):
     _print_case("config 3 full size", wl)
     rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 7]
     _check_full_step(M, oracle, wl, sample=rows)
+
+
+def test_full_size_config2_sampled(M, oracle):
+    """Configuration 2 at full size (B=8, 32K tokens): rows split over 4 attention workgroups."""
+    wl = W.make_workload(2, seed=0)
+    _print_case("config 2 full size", wl)
+    _check_full_step(M, oracle, wl, sample=[0, 6])
+
+
+def test_full_size_config7_sampled(M, oracle):
+    """The forced-dense configuration at full size (B=32, 8K tokens, top-64 of 64 blocks): every
+    block is selected, so attention covers each whole context."""
+    wl = W.make_workload(7, seed=0)
+    _print_case("config 7 full size", wl)
+    _check_full_step(M, oracle, wl, sample=[0, 17, 31])
 
 
 def test_full_size_config4_sampled(M, oracle):
