@@ -247,9 +247,11 @@ def recorded_traffic(key="insert-index-kernel-traffic-bytes-per-launch"):
     return int(fields[key]) if key in fields else None
 
 
-def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4"):
+def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4", scan="owner"):
     """Device state of the benchmark workload: filled caches (``n_replicas`` copies),
-    decoders, the step's new rows and quantised queries."""
+    decoders, the step's new rows and quantised queries.  scan="owner": the batch
+    carries the owner map (NVFP4 decode batches without a shared prefix), which the
+    index scan then reads in physical page order; "table": it walks the table rows."""
     import torch
 
     import block_sparse_attention_index_amd as M
@@ -266,6 +268,20 @@ def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4"):
     table = torch.from_numpy(wl.block_table).to(dev)
     lens = torch.from_numpy(wl.lengths).to(dev)
     batch = M.Batch(table, lens, wl.R, wl.prefix_pages)
+    table_batch, owner_us = batch, None
+    if scan == "owner" and kv == "nvfp4" and not wl.prefix_pages and wl.R <= M.MSA_MAX_ROWS:
+        # the block table's inverse, kept with the table (the step itself records the pages of
+        # its new rows); built here once, its build time reported beside the step
+        own = M.msa_page_owner(batch, wl.num_pages)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            M.msa_page_owner(batch, wl.num_pages, own)
+        e1.record()
+        torch.cuda.synchronize()
+        owner_us = e0.elapsed_time(e1) * 1e3 / 10
+        batch = M.Batch(table, lens, wl.R, wl.prefix_pages, page_owner=own)
     if wl.prefix_tokens:  # the shared prefix is written once, into the pages every request's table names
         xi, xk, xv = W.torch_rows(wl, 0, dev, prefix=True)
         slots = torch.from_numpy(wl.slots(0, np.arange(wl.prefix_tokens, dtype=np.int64))).to(dev)
@@ -302,7 +318,8 @@ def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4"):
     new = (new_k, new_v, new_i, new_slots)
     torch.cuda.synchronize()
 
-    return SimpleNamespace(torch=torch, M=M, W=W, wl=wl, decs=decs, q_idx=q_idx, q=q, new=new, batch=batch)
+    return SimpleNamespace(torch=torch, M=M, W=W, wl=wl, decs=decs, q_idx=q_idx, q=q, new=new, batch=batch,
+                           table_batch=table_batch, owner_us=owner_us)
 
 
 def main():
@@ -318,6 +335,9 @@ def main():
                          "7 = 32 x 8K with top-64 (every block selected: the forced-dense traffic check)")
     ap.add_argument("--kv", choices=["nvfp4", "fp8"], default="nvfp4",
                     help="cache format of keys, values and index keys (default NVFP4, the metric's own)")
+    ap.add_argument("--scan", choices=["owner", "table"], default="owner",
+                    help="index scan order: physical page order from the block table's inverse (owner map; "
+                         "NVFP4 decode without a shared prefix) or each request's table row")
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--layers-per-graph", type=int, default=10,
@@ -341,7 +361,8 @@ def main():
         bench_qkv(args)
         return
 
-    st = setup(args.seed, args.replicas, args.config, args.kv)
+    st = setup(args.seed, args.replicas, args.config, args.kv, args.scan)
+    owned = st.batch.page_owner is not None
     headline = args.config == CONFIG_ID and args.kv == "nvfp4"
     torch, M, W, wl, decs, q_idx, q, new = st.torch, st.M, st.W, st.wl, st.decs, st.q_idx, st.q, st.new
 
@@ -418,6 +439,13 @@ def main():
     if prefill:
         del calls["insert_index"]
     P = wl.prefix_pages
+    if owned:  # the table-order scan on the same caches, for comparison
+        from block_sparse_attention_index_amd.decoder import MsaDecoder
+
+        tdec = {id(d): MsaDecoder(st.table_batch, d.k, d.v, d.idx, wl.topk) for d in decs}
+        calls["index_table_order"] = lambda d: tdec[id(d)].index(q_idx, wl.q_scale, None, stream)
+        calls["insert_index_table_order"] = lambda d: tdec[id(d)].insert_index(new[0], new[1], new[2], q_idx,
+                                                                              wl.q_scale, None, stream)
     if P:
         # the prefix kernel alone: a batch whose table ends with the shared pages leaves the
         # per-request scan nothing to do
@@ -441,6 +469,8 @@ def main():
             b_.record(stream)
         torch.cuda.synchronize()
         us[name] = a_.elapsed_time(b_) * 1e3 / (replays * reps)
+    if owned:
+        us["page_owner_build"] = st.owner_us
     log("per-kernel us (graph of back-to-back launches): " + ", ".join(f"{k} {v:.1f}" for k, v in us.items()))
 
     # ---- the practical HBM read ceiling in this process: a plain streaming read of as many
@@ -516,6 +546,7 @@ def main():
                    "ctx_tokens_max": int(wl.lengths.max()), "kv_cache": wl.cache, "index_cache": wl.cache,
                    "topk_blocks": wl.topk, "block_tokens": 128, "parallelism": "single-gpu",
                    "cache_replicas": len(decs), "hip_graph": use_graph,
+                   "index_scan": "physical page order (owner map)" if owned else "block-table order",
                    "layer_steps_per_graph": per_graph if use_graph else None},
         "roofline": ({"bound": "mfma", "kernel": "prefill_index_kernel (dense indexer on v_mfma_f32_16x16x32_f16)",
                       "flops_per_launch": prefill_flops, "avg_launch_us": us["index"],
@@ -523,7 +554,8 @@ def main():
                       "unit": "TFLOP/s", "frac": prefill_flops / (us["index"] * 1e-6) / 1e12 / PEAK_F16_MFMA_TFLOPS,
                       "traffic": None, "index_GBps": idx_gbps} if prefill else
                      {"bound": "hbm", "scope": "dominant kernel, per launch (the whole step: step_hbm)",
-                      "kernel": f"index_{wl.cache}_kernel with the insert fused in (steps 0-2)",
+                      "kernel": (f"index_{wl.cache}_owned_kernel" if owned else f"index_{wl.cache}_kernel")
+                      + " with the insert fused in (steps 0-2)",
                       "achieved": idx_gbps,
                       "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS,
                       "traffic": recorded_traffic() if headline else None,

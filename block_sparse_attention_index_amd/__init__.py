@@ -41,7 +41,8 @@ class msa_cache(C.Structure):
 
 class msa_batch(C.Structure):
     _fields_ = [("num_reqs", C.c_int32), ("rows_per_req", C.c_int32), ("max_pages_per_req", C.c_int32),
-                ("shared_prefix_pages", C.c_int32), ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p)]
+                ("shared_prefix_pages", C.c_int32), ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p),
+                ("page_owner", C.c_void_p)]
 
 
 def _load() -> C.CDLL:
@@ -55,6 +56,7 @@ def _load() -> C.CDLL:
         "msa_kv_insert_nvfp4": (C.c_int, [vp, vp, vp, vp, i32, P(msa_cache), P(msa_cache), P(msa_cache), vp]),
         "msa_quantize_e4m3": (C.c_int, [vp, i64, f32, vp, vp]),
         "msa_index_score": (C.c_int, [P(msa_batch), vp, i32, f32, P(msa_cache), vp, vp, vp]),
+        "msa_page_owner": (C.c_int, [P(msa_batch), i32, vp, vp]),
         "msa_block_maxpool_topk": (C.c_int, [P(msa_batch), vp, i32, i32, vp, vp, vp]),
         "msa_workspace_bytes": (sz, [P(msa_batch), i32]),
         "msa_sparse_decode": (C.c_int, [P(msa_batch), vp, i32, f32, f32, P(msa_cache), P(msa_cache), vp, vp, i32,
@@ -135,11 +137,14 @@ class Batch:
     """Block table and context lengths (device int32) of one decode step."""
 
     def __init__(self, block_table: torch.Tensor, ctx_lens: torch.Tensor, rows_per_req: int,
-                 shared_prefix_pages: int = 0):
+                 shared_prefix_pages: int = 0, page_owner: torch.Tensor | None = None):
+        """page_owner: None, or a device int32 [index pool pages] owner map (msa_page_owner builds it)."""
         assert block_table.dtype == torch.int32 and ctx_lens.dtype == torch.int32
-        self.block_table, self.ctx_lens = block_table, ctx_lens
+        assert page_owner is None or (page_owner.dtype == torch.int32 and page_owner.is_contiguous())
+        self.block_table, self.ctx_lens, self.page_owner = block_table, ctx_lens, page_owner
         B, P = block_table.shape
-        self.struct = msa_batch(B, rows_per_req, P, shared_prefix_pages, _ptr(block_table), _ptr(ctx_lens))
+        self.struct = msa_batch(B, rows_per_req, P, shared_prefix_pages, _ptr(block_table), _ptr(ctx_lens),
+                                _ptr(page_owner))
 
     def ref(self):
         return C.byref(self.struct)
@@ -196,6 +201,14 @@ def msa_index_score(batch: Batch, q_idx, q_dtype: int, q_scale: float, idx_cache
                     token_scores=None, stream=None) -> None:
     _check(lib.msa_index_score(batch.ref(), _ptr(q_idx), q_dtype, float(q_scale), idx_cache.ref(),
                                _ptr(block_scores), _ptr(token_scores), _stream(stream)), "msa_index_score")
+
+
+def msa_page_owner(batch: Batch, num_pages: int, page_owner=None, stream=None):
+    """The block table's inverse over an index pool of num_pages pages (device int32 [num_pages])."""
+    if page_owner is None:
+        page_owner = torch.empty(num_pages, dtype=torch.int32, device=batch.block_table.device)
+    _check(lib.msa_page_owner(batch.ref(), int(num_pages), _ptr(page_owner), _stream(stream)), "msa_page_owner")
+    return page_owner
 
 
 def msa_insert_index_score(batch: Batch, k_new, v_new, idx_new, q_idx, q_dtype: int, q_scale: float,

@@ -42,6 +42,8 @@ int check_batch(const msa_batch* b, int max_rows = MSA_MAX_ROWS) {
   if (b->shared_prefix_pages < 0 || b->shared_prefix_pages > b->max_pages_per_req) return MSA_ERR_INVALID_ARG;
   // grid dimensions: y and z are 16-bit on this hardware
   if (b->num_reqs > 65535) return MSA_ERR_INVALID_ARG;
+  // owner entries b * max_pages + j are 32-bit
+  if (b->page_owner && (int64_t)b->num_reqs * b->max_pages_per_req >= (int64_t)1 << 31) return MSA_ERR_INVALID_ARG;
   return MSA_OK;
 }
 
@@ -208,6 +210,14 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
                                   sel_count, out, workspace, stream) == 0
              ? MSA_OK
              : MSA_ERR_HIP;
+}
+
+int msa_page_owner(const msa_batch* batch, int32_t num_pages, int32_t* page_owner, hipStream_t stream) {
+  int st;
+  if ((st = check_batch(batch, MSA_MAX_PREFILL_ROWS)) != MSA_OK) return st;
+  if (num_pages < 1 || !page_owner) return MSA_ERR_INVALID_ARG;
+  if ((int64_t)batch->num_reqs * batch->max_pages_per_req >= (int64_t)1 << 31) return MSA_ERR_INVALID_ARG;
+  return msa_launch_page_owner(batch, num_pages, page_owner, stream) == 0 ? MSA_OK : MSA_ERR_HIP;
 }
 
 int msa_insert_index_score(const msa_batch* batch, const float* k_new, const float* v_new, const float* idx_new,

@@ -21,6 +21,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                                                   num_pages, block_scores, token_scores, B, p0, NR);
 }
 
+// The scan in physical page order, for a batch that carries page_owner (the
+// block table's inverse: entry p = b * max_pages + j where table[b][j] == p).
+// Workgroup b < B belongs to request b: it writes the request's new rows
+// (INSERT), scores the one or two pages that hold rows L_b - R .. L_b - 1
+// through the block table, records those pages in page_owner and writes the
+// -inf scores of the blocks past the context.  Workgroup B + i takes pool
+// pages 4i .. 4i+3, one per wave.  A wave reads its page's owner entry and
+// issues the page's loads before anything else; the page counts only if the
+// entry names a block of some request that lies before that request's
+// new-row pages and whose table entry names the page back (free pages and
+// stale entries are dropped after their loads).  So no lookup chain (lengths,
+// chunk, table) stands before the page loads, as one does in the
+// chunk-mapped scan; the price is that every pool page is read, in use or not.
+template <int R, bool INSERT, bool F16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_nvfp4_owned_kernel(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t max_pages, int32_t* owner,
+    const uint8_t* __restrict__ q_idx, float out_scale, const uint8_t* __restrict__ pages, int32_t num_pages,
+    float* __restrict__ block_scores, int32_t B, NewRows NR) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, col = lane & 15;
+  __shared__ uint4 s_scales[4][64];
+  if ((int)blockIdx.x < B) {
+    const int b = (int)blockIdx.x;
+    const int L = clamp_len(lens[b], max_pages);
+    const int t0 = max(L - R, 0);
+    if (INSERT && t0 < L) {
+      insert_new_rows<R>(table, max_pages, num_pages, b, L, t0, L, NR);
+      // the index keys just written are read back by this workgroup's waves
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    const int npb = (L + kPage - 1) / kPage;
+    const int j = t0 / kPage + wave;  // R <= 128: the new rows lie on at most two pages
+    if (wave < 2 && j < npb) {
+      int phys = table[(int64_t)b * max_pages + j];
+      if (phys >= num_pages) phys = -1;
+      ScanQueries<R, F16> q;
+      q.load(q_idx, b, lane);
+      if (phys >= 0) {
+        if (lane == 0) owner[phys] = b * max_pages + j;
+        PageRegs pr;
+        load_page(pr, pages + (int64_t)phys * kNvSlab, col, grp, lane);
+        score_resident_page<R, false, F16>(pr, q, &s_scales[wave][0], L, j, b, lane, max_pages, out_scale, 0,
+                                           block_scores, nullptr);
+      } else {
+        empty_block<R, false>(j, b, lane, max_pages, 0, block_scores, nullptr);
+      }
+    }
+    fill_past_chunks<R>(block_scores, b, npb, max_pages);
+    return;
+  }
+  const int p = ((int)blockIdx.x - B) * 4 + wave;
+  if (p >= num_pages) return;
+  const int own = owner[p];
+  PageRegs pr;
+  load_page(pr, pages + (int64_t)p * kNvSlab, col, grp, lane);
+  // (the scheduler would otherwise start on the page's first words between its loads)
+  __builtin_amdgcn_sched_barrier(0);
+  // the owner's length, table entry and queries load together, in one round
+  // behind the page (request 0's stand in for an entry that names no
+  // request); a page that is not the owner's is scored all the same, its
+  // stores dropped, so that no branch waits on one load before issuing the next
+  const bool named = (own >= 0) & (own / max_pages < B);
+  const int b = named ? own / max_pages : 0, j = named ? own - b * max_pages : 0;
+  const int Lraw = lens[b], back = table[(int64_t)b * max_pages + j];
+  ScanQueries<R, F16> q;
+  q.load(q_idx, b, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const int L = clamp_len(Lraw, max_pages);
+  const bool mine = named & (back == p) & (j < max(L - R, 0) / kPage);
+  score_resident_page<R, false, F16>(pr, q, &s_scales[wave][0], L, j, b, lane, max_pages, out_scale, 0, block_scores,
+                                     nullptr, mine);
+}
+
+// page_owner from the block table: every entry -1, then entry table[b][j] =
+// b * max_pages + j for the blocks j < ceil(L_b / 128) of every request whose
+// page lies in the pool (a page named twice keeps one of the two).
+__global__ __launch_bounds__(256) void page_owner_clear_kernel(int32_t* __restrict__ owner, int32_t num_pages) {
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < num_pages; p += (int64_t)gridDim.x * 256)
+    owner[p] = -1;
+}
+
+__global__ __launch_bounds__(256) void page_owner_scatter_kernel(const int32_t* __restrict__ table,
+                                                                 const int32_t* __restrict__ lens, int32_t max_pages,
+                                                                 int32_t num_pages, int32_t* __restrict__ owner) {
+  const int b = (int)blockIdx.y;
+  const int npb = (clamp_len(lens[b], max_pages) + kPage - 1) / kPage;
+  for (int j = (int)blockIdx.x * 256 + (int)threadIdx.x; j < npb; j += (int)gridDim.x * 256) {
+    const int p = table[(int64_t)b * max_pages + j];
+    if (p >= 0 && p < num_pages) owner[p] = b * max_pages + j;
+  }
+}
+
 // FP8 caches (one E4M3 byte per element, FP32 tensor scale): the same scan
 // over 128 B per token.  Keys and index queries are both FP8, so one
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) multiplies 16 tokens'
@@ -275,6 +369,38 @@ static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale,
                        ts, bt->num_reqs, p0, nr);
 }
 
+template <int R, bool INSERT>
+static void launch_owned(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                         const NewRows& nr, hipStream_t s) {
+  const dim3 grid((unsigned)(bt->num_reqs + (ic->num_pages + 3) / 4));
+  hipLaunchKernelGGL((index_nvfp4_owned_kernel<R, INSERT, (R >= 3)>), grid, dim3(256), 0, s, bt->block_table,
+                     bt->ctx_lens, bt->max_pages_per_req, bt->page_owner, q, out_scale, (const uint8_t*)ic->pages,
+                     ic->num_pages, bs, bt->num_reqs, nr);
+}
+
+template <bool INSERT>
+static int launch_owned_rows(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
+                             const NewRows& nr, hipStream_t s) {
+  switch (bt->rows_per_req) {
+    case 1: launch_owned<1, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 2: launch_owned<2, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 3: launch_owned<3, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 4: launch_owned<4, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 5: launch_owned<5, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 6: launch_owned<6, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 7: launch_owned<7, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    case 8: launch_owned<8, INSERT>(bt, q, out_scale, ic, bs, nr, s); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The physical-order scan takes decode batches with an owner map, no shared
+// prefix and no token scores (NVFP4 index cache).
+static bool owned_scan(const msa_batch* bt, const float* ts) {
+  return bt->page_owner && !ts && bt->shared_prefix_pages == 0 && bt->rows_per_req <= MSA_MAX_ROWS;
+}
+
 template <bool INSERT>
 static int launch_nvfp4_rows(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                              float* ts, const NewRows& nr, hipStream_t s) {
@@ -316,6 +442,8 @@ extern "C" int msa_launch_index_score(const msa_batch* bt, const void* q_idx, in
   const float out_scale = ic->tensor_scale * q_scale;
   if (ic->dtype == MSA_FP8_E4M3)  // the shared-prefix declaration is not used with FP8 caches
     return launch_fp8_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, NewRows{}, s);
+  if (owned_scan(bt, token_scores))
+    return launch_owned_rows<false>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, NewRows{}, s);
   const int fused = launch_prefix_scan(bt, (const uint8_t*)q_idx, q_scale, ic, block_scores, token_scores, NewRows{},
                                        false, s);
   if (fused <= 0) return fused;
@@ -332,8 +460,21 @@ extern "C" int msa_launch_insert_index_score(const msa_batch* bt, const float* k
   const float out_scale = ic->tensor_scale * q_scale;
   if (ic->dtype == MSA_FP8_E4M3)
     return launch_fp8_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, nr, s);
+  if (owned_scan(bt, token_scores))
+    return launch_owned_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, nr, s);
   const int fused = launch_prefix_scan(bt, (const uint8_t*)q_idx, q_scale, ic, block_scores, token_scores, nr, true, s);
   if (fused <= 0) return fused;
   if (msa_launch_prefix_index(bt, q_idx, q_scale, ic, block_scores, token_scores, s) != 0) return -1;
   return launch_nvfp4_rows<true>(bt, (const uint8_t*)q_idx, out_scale, ic, block_scores, token_scores, nr, s);
+}
+
+extern "C" int msa_launch_page_owner(const msa_batch* bt, int32_t num_pages, int32_t* owner, hipStream_t s) {
+  const int64_t need = ((int64_t)num_pages + 255) / 256;
+  const unsigned clear_wgs = (unsigned)(need < 4096 ? need : 4096);
+  hipLaunchKernelGGL(page_owner_clear_kernel, dim3(clear_wgs), dim3(256), 0, s, owner, num_pages);
+  const int cols = (bt->max_pages_per_req + 255) / 256;
+  const unsigned per_req = (unsigned)(cols < 64 ? cols : 64);
+  hipLaunchKernelGGL(page_owner_scatter_kernel, dim3(per_req, (unsigned)bt->num_reqs), dim3(256), 0, s,
+                     bt->block_table, bt->ctx_lens, bt->max_pages_per_req, num_pages, owner);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -40,6 +40,7 @@ int msa_launch_index_score(const msa_batch* b, const void* q_idx, int32_t q_dtyp
 int msa_launch_insert_index_score(const msa_batch* b, const float* k_new, const float* v_new, const float* idx_new,
                                   const void* q_idx, float q_scale, const msa_cache* kc, const msa_cache* vc,
                                   const msa_cache* ic, float* block_scores, float* token_scores, hipStream_t stream);
+int msa_launch_page_owner(const msa_batch* b, int32_t num_pages, int32_t* owner, hipStream_t stream);
 int msa_launch_prefix_index(const msa_batch* b, const void* q_idx, float q_scale, const msa_cache* ic,
                             float* block_scores, float* token_scores, hipStream_t stream);
 int msa_launch_prefill_index(const msa_batch* b, const void* q_idx, float q_scale, const msa_cache* ic,

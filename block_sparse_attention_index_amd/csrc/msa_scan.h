@@ -203,7 +203,8 @@ __device__ __forceinline__ void load_queries_f16(const uint8_t* __restrict__ q_i
 template <int R, bool kTok>
 __device__ __forceinline__ void score_page_f16(const PageRegs& pr, const h8 (&Q)[f16_tiles<R>()][4], int L, int j,
                                                int b, int lane, int max_pages, float out_scale, int64_t T,
-                                               float* __restrict__ block_scores, float* __restrict__ token_scores) {
+                                               float* __restrict__ block_scores, float* __restrict__ token_scores,
+                                               bool keep = true) {
   constexpr int QT = f16_tiles<R>();
   const int n = lane & 15, a = lane >> 4;
   float mx[QT];
@@ -248,7 +249,7 @@ __device__ __forceinline__ void score_page_f16(const PageRegs& pr, const h8 (&Q)
     float m = mx[qt];
     m = rows_max4(m);
     const int qi = 16 * qt + n;
-    if (a == 0 && qi < R * kGroups) block_scores[((int64_t)b * R * kGroups + qi) * max_pages + j] = m * out_scale;
+    if (keep && a == 0 && qi < R * kGroups) block_scores[((int64_t)b * R * kGroups + qi) * max_pages + j] = m * out_scale;
   }
 }
 
@@ -267,6 +268,129 @@ struct NewRows {
   int32_t kv_num_pages;
   float ts_k, ts_v, ts_i;
 };
+
+// The step's new tokens of request b that fall in [t0, t1) (t0 < t1, within
+// [L - R, L)), written into the three caches by a whole workgroup of 256
+// threads (one 16-lane row per 16-element group, as the insert kernel does).
+// The caller makes them visible to its waves (workgroup release, barrier,
+// acquire) before reading the pages.
+template <int R>
+__device__ __forceinline__ void insert_new_rows(const int32_t* __restrict__ table, int32_t max_pages, int32_t num_pages,
+                                                int b, int L, int t0, int t1, const NewRows& NR) {
+  const int i = threadIdx.x & 15;
+  const int nrow = (t1 - t0) * 72;  // 16-dim groups: 32 keys, 32 values, 8 index keys per token
+  // row rr: token t0 + rr / 72, then 32 key, 32 value and 8 index-key groups
+  auto locate = [&](int rr, int& tok, int& c, int& head, int& grp) {
+    tok = t0 + rr / 72;
+    int u = rr % 72;
+    c = u < 32 ? 0 : (u < 64 ? 1 : 2);
+    u -= 32 * c;
+    head = u >> 3;
+    grp = u & 7;
+  };
+  // a batch of rows per 16-lane row of threads: every source load issues
+  // before the first store (which could alias them), so a batch is one
+  // memory round -- sized for all of a chunk's rows (one round) up to four
+  // new rows, two rounds beyond.  The new tokens lie on at most two pages
+  // (R <= 128), whose table entries load with the sources.
+  constexpr int kBatch = (72 * R + 15) / 16 < 18 ? (72 * R + 15) / 16 : 18;
+  const int pa = t0 / kPage;
+  const int ph_a = table[(int64_t)b * max_pages + pa], ph_b = table[(int64_t)b * max_pages + (t1 - 1) / kPage];
+  for (int rb = threadIdx.x >> 4; rb < nrow; rb += 16 * kBatch) {
+    float x[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      int tok, c, head, grp;
+      locate(min(rb + 16 * k, nrow - 1), tok, c, head, grp);
+      const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
+      x[k] = src[(((int64_t)b * R + tok - (L - R)) * (c == 2 ? 1 : kGroups) + head) * kDim + grp * 16 + i];
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (rb + 16 * k >= nrow) break;  // uniform over the 16-lane row
+      int tok, c, head, grp;
+      locate(rb + 16 * k, tok, c, head, grp);
+      const int heads = c == 2 ? 1 : kGroups;
+      const int ph = tok / kPage == pa ? ph_a : ph_b;
+      const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
+      uint8_t* base = c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages);
+      uint32_t code;
+      const uint32_t sc = nvfp4_row_quantize(x[k], c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i), code);
+      nvfp4_row_store(base + ((int64_t)(valid ? ph : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i, code, sc,
+                      c == 1, valid);
+    }
+  }
+}
+
+// Index queries of request b in the scan's operand form: the FP4 form's A
+// operands (the query of row r masked to one scale group per MFMA row) or the
+// FP16 form's tiles of 16 index queries.
+template <int R, bool F16>
+struct ScanQueries {
+  v8i A[F16 ? 1 : R][2];
+  h8 Qh[F16 ? f16_tiles<R>() : 1][4];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ q_idx, int b, int lane) {
+    if constexpr (F16) {
+      load_queries_f16<R>(q_idx, b, lane, Qh);
+    } else {
+      const int grp = lane >> 4, i = lane & 15;
+      const int gq = i >> 2, jj = i & 3;
+      const bool on = (jj == grp);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint8_t* q = q_idx + (((int64_t)b * R + r) * kGroups + gq) * kDim;
+        uint4 lo = on ? *reinterpret_cast<const uint4*>(q + 16 * grp) : make_uint4(0, 0, 0, 0);
+        uint4 hi = on ? *reinterpret_cast<const uint4*>(q + 64 + 16 * grp) : make_uint4(0, 0, 0, 0);
+        A[r][0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+        A[r][1] = v8i{0, 0, 0, 0, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+  }
+};
+
+// Page j of request b, resident in pr: its scale bytes go through the wave's
+// LDS slot, then the scores of all R rows (positions past L - R + r masked),
+// their block maxima and the block-score stores (token scores too with kTok);
+// keep = false scores the page but stores nothing.
+template <int R, bool kTok, bool F16>
+__device__ __forceinline__ void score_resident_page(PageRegs& pr, const ScanQueries<R, F16>& q, uint4* slot, int L,
+                                                    int j, int b, int lane, int max_pages, float out_scale, int64_t T,
+                                                    float* __restrict__ block_scores,
+                                                    float* __restrict__ token_scores, bool keep = true) {
+  const int grp = lane >> 4, col = lane & 15;
+  stage_scales(pr, slot, lane, col);
+  if constexpr (F16) {
+    score_page_f16<R, kTok>(pr, q.Qh, L, j, b, lane, max_pages, out_scale, T, block_scores, token_scores, keep);
+  } else {
+    int pos_lim[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) pos_lim[r] = L - R + r;
+    float m[R];
+    score_page<R, kTok>(pr, q.A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float mm = wave_max16(m[r]);
+      if (keep && col == 0) block_scores[(((int64_t)b * R + r) * kGroups + grp) * max_pages + j] = mm * out_scale;
+    }
+  }
+}
+
+// Block j of request b holds no visible token (past the context, or its page
+// is outside the pool): -inf block scores for all R rows (token scores too).
+template <int R, bool kTok>
+__device__ __forceinline__ void empty_block(int j, int b, int lane, int max_pages, int64_t T,
+                                            float* __restrict__ block_scores, float* __restrict__ token_scores) {
+  const int grp = lane >> 4, col = lane & 15;
+  if (kTok)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      for (int c = 0; c < 8; ++c)
+        token_scores[(((int64_t)b * R + r) * kGroups + grp) * T + j * kPage + 16 * c + col] = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (col == 0) block_scores[(((int64_t)b * R + r) * kGroups + grp) * max_pages + j] = -__builtin_inff();
+}
 
 // One chunk of the scan, run by a whole workgroup of 4 waves: page
 // p0 + 4*chunk + wave of request b per wave (one page per wave).  The scan
@@ -301,49 +425,7 @@ __device__ __forceinline__ void nvfp4_scan_chunk(
     const int lo = (p0 + chunk * 4) * kPage;
     const int t0 = max(max(L - R, 0), lo), t1 = min(L, lo + 4 * kPage);
     if (t0 < t1) {
-      const int i = threadIdx.x & 15;
-      const int nrow = (t1 - t0) * 72;  // 16-dim groups: 32 keys, 32 values, 8 index keys per token
-      // row rr: token t0 + rr / 72, then 32 key, 32 value and 8 index-key groups
-      auto locate = [&](int rr, int& tok, int& c, int& head, int& grp) {
-        tok = t0 + rr / 72;
-        int u = rr % 72;
-        c = u < 32 ? 0 : (u < 64 ? 1 : 2);
-        u -= 32 * c;
-        head = u >> 3;
-        grp = u & 7;
-      };
-      // a batch of rows per 16-lane row of threads: every source load issues
-      // before the first store (which could alias them), so a batch is one
-      // memory round -- sized for all of a chunk's rows (one round) up to
-      // four new rows, two rounds beyond.  The new tokens lie on at most two
-      // pages (R <= 128), whose table entries load with the sources.
-      constexpr int kBatch = (72 * R + 15) / 16 < 18 ? (72 * R + 15) / 16 : 18;
-      const int pa = t0 / kPage;
-      const int ph_a = table[(int64_t)b * max_pages + pa], ph_b = table[(int64_t)b * max_pages + (t1 - 1) / kPage];
-      for (int rb = threadIdx.x >> 4; rb < nrow; rb += 16 * kBatch) {
-        float x[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          int tok, c, head, grp;
-          locate(min(rb + 16 * k, nrow - 1), tok, c, head, grp);
-          const float* src = c == 0 ? NR.k : (c == 1 ? NR.v : NR.idx);
-          x[k] = src[(((int64_t)b * R + tok - (L - R)) * (c == 2 ? 1 : kGroups) + head) * kDim + grp * 16 + i];
-        }
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          if (rb + 16 * k >= nrow) break;  // uniform over the 16-lane row
-          int tok, c, head, grp;
-          locate(rb + 16 * k, tok, c, head, grp);
-          const int heads = c == 2 ? 1 : kGroups;
-          const int ph = tok / kPage == pa ? ph_a : ph_b;
-          const bool valid = ph >= 0 && ph < (c == 2 ? num_pages : NR.kv_num_pages);
-          uint8_t* base = c == 0 ? NR.kpages : (c == 1 ? NR.vpages : NR.ipages);
-          uint32_t code;
-          const uint32_t sc = nvfp4_row_quantize(x[k], c == 0 ? NR.ts_k : (c == 1 ? NR.ts_v : NR.ts_i), code);
-          nvfp4_row_store(base + ((int64_t)(valid ? ph : 0) * heads + head) * kNvSlab, tok & (kPage - 1), grp, i,
-                          code, sc, c == 1, valid);
-        }
-      }
+      insert_new_rows<R>(table, max_pages, num_pages, b, L, t0, t1, NR);
       // the index keys just written are read back by this workgroup's waves
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
@@ -366,61 +448,16 @@ __device__ __forceinline__ void nvfp4_scan_chunk(
   int phys = j < npb ? table[(int64_t)b * max_pages + j] : -1;
   if (phys >= num_pages) phys = -1;
 
-  // A operands: queries of row r masked to one scale group per MFMA row
-  // (FP16 form: 16 index queries per tile instead).
-  v8i A[F16 ? 1 : R][2];
-  h8 Qh[F16 ? f16_tiles<R>() : 1][4];
-  if constexpr (F16) load_queries_f16<R>(q_idx, b, lane, Qh);
-  if constexpr (!F16) {
-    const int i = lane & 15;
-    const int gq = i >> 2, jj = i & 3;
-    const bool on = (jj == grp);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint8_t* q = q_idx + (((int64_t)b * R + r) * kGroups + gq) * kDim;
-      uint4 lo = on ? *reinterpret_cast<const uint4*>(q + 16 * grp) : make_uint4(0, 0, 0, 0);
-      uint4 hi = on ? *reinterpret_cast<const uint4*>(q + 64 + 16 * grp) : make_uint4(0, 0, 0, 0);
-      A[r][0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
-      A[r][1] = v8i{0, 0, 0, 0, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-  }
-  int pos_lim[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) pos_lim[r] = L - R + r;
-
-  auto finish = [&](int j, const float (&m)[R]) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float mm = wave_max16(m[r]);
-      if (col == 0) block_scores[(((int64_t)b * R + r) * kGroups + grp) * max_pages + j] = mm * out_scale;
-    }
-  };
-  auto empty_page = [&](int j) {
-    float m[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) m[r] = -__builtin_inff();
-    if (kTok)
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        for (int c = 0; c < 8; ++c)
-          token_scores[(((int64_t)b * R + r) * kGroups + grp) * T + j * kPage + 16 * c + col] = -__builtin_inff();
-    finish(j, m);
-  };
-
+  ScanQueries<R, F16> q;
+  q.load(q_idx, b, lane);
   __shared__ uint4 s_scales[4][64];
   if (phys >= 0) {
     PageRegs pr;
     load_page(pr, pages + (int64_t)phys * kNvSlab, col, grp, lane);
-    stage_scales(pr, &s_scales[wave][0], lane, col);
-    if constexpr (F16) {
-      score_page_f16<R, kTok>(pr, Qh, L, j, b, lane, max_pages, out_scale, T, block_scores, token_scores);
-    } else {
-      float m[R];
-      score_page<R, kTok>(pr, A, pos_lim, j, b, grp, col, out_scale, T, token_scores, m);
-      finish(j, m);
-    }
+    score_resident_page<R, kTok, F16>(pr, q, &s_scales[wave][0], L, j, b, lane, max_pages, out_scale, T,
+                                      block_scores, token_scores);
   } else {
-    empty_page(j);
+    empty_block<R, kTok>(j, b, lane, max_pages, T, block_scores, token_scores);
   }
   fill_past();
 }

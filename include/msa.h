@@ -124,6 +124,23 @@ typedef struct {
  * scores (undefined results, not checked on the device).  Contexts shorter
  * than the prefix are fine (invisible tokens are masked as usual).  With an
  * F32 index cache P is not used.  0 <= P <= max_pages_per_req.
+ *
+ * page_owner (may be NULL) lets the NVFP4 decode scan (msa_index_score and
+ * msa_insert_index_score with an NVFP4 index cache, R <= MSA_MAX_ROWS, no
+ * token_scores, P = 0) read the index pool in physical page order instead of
+ * walking each request's table row.  Entry p names the block that page p
+ * holds, b * max_pages_per_req + j where block_table[b][j] == p.  Required:
+ * for every request b and every block j below the page of its first new row
+ * (j < floor(max(L_b - R, 0) / 128)), page_owner[block_table[b][j]] names
+ * (b, j); other entries may hold anything (-1 for a free page), since an entry
+ * counts only if the table row it names points back at the page.  Such a call
+ * reads every page of the index pool once, in use or not, and sets the
+ * entries of the pages that hold the step's new rows, so a decode loop whose
+ * tables only grow keeps the map current by itself; msa_page_owner builds it
+ * from scratch (after the batch's requests change).  Pages of old blocks must
+ * not be shared between requests (a page can name one owner).  Other calls
+ * and the other cases ignore it.  B * max_pages_per_req must stay below 2^31
+ * when it is set.
  */
 typedef struct {
   int32_t num_reqs;            /* B >= 1                                        */
@@ -134,6 +151,8 @@ typedef struct {
   int32_t shared_prefix_pages; /* P: leading table entries shared by every row, 0 if none */
   const int32_t* block_table;  /* device [B][max_pages_per_req] physical page ids */
   const int32_t* ctx_lens;     /* device [B] L_b, new rows included              */
+  int32_t* page_owner;         /* device [index cache num_pages] or NULL: the block
+                                  table's inverse, see below                     */
 } msa_batch;
 
 /*
@@ -214,6 +233,17 @@ int msa_quantize_e4m3(const float* x, int64_t n, float scale, uint8_t* out, hipS
  */
 int msa_index_score(const msa_batch* batch, const void* q_idx, int32_t q_dtype, float q_scale,
                     const msa_cache* idx_cache, float* block_scores, float* token_scores, hipStream_t stream);
+
+/*
+ * Builds batch->page_owner's content from the block table into page_owner
+ * (device [num_pages], num_pages = the index cache's pool size): every entry
+ * -1, then entry block_table[b][j] = b * max_pages_per_req + j for the blocks
+ * j < ceil(L_b / 128) of every request whose page id lies in [0, num_pages)
+ * (a page named by two blocks keeps one of them).  Two kernels on stream; the
+ * batch's own page_owner field is not read.  MSA_ERR_INVALID_ARG for a bad
+ * batch, num_pages < 1, a NULL page_owner, or B * max_pages_per_req >= 2^31.
+ */
+int msa_page_owner(const msa_batch* batch, int32_t num_pages, int32_t* page_owner, hipStream_t stream);
 
 /*
  * Steps 0+1+2 in one launch (NVFP4 caches, FP8 index queries): the step's

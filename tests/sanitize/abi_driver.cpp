@@ -31,6 +31,7 @@ STUB(msa_launch_select_decode, const msa_batch*, const float*, int32_t, const vo
 STUB(msa_launch_sparse_decode_noalloc, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, hipStream_t)
 STUB(msa_launch_stream_read, const void*, int64_t, int32_t, uint32_t*, hipStream_t)
+STUB(msa_launch_page_owner, const msa_batch*, int32_t, int32_t*, hipStream_t)
 STUB(msa_launch_sparse_decode, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, void*, hipStream_t)
 extern "C" size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk) {
@@ -108,6 +109,24 @@ int main() {
   b2 = bt;
   b2.num_reqs = 1 << 20, b2.rows_per_req = 8192;
   expect(msa_index_score(&b2, p, MSA_FP8_E4M3, 1.0f, &ic, f, nullptr, nullptr), MSA_ERR_INVALID_ARG, 0, "rows overflow");
+
+  // owner map: its builder, and a batch that carries one
+  int32_t* own = reinterpret_cast<int32_t*>(buf);
+  expect(msa_page_owner(&bt, 16, own, nullptr), MSA_OK, 1, "page_owner ok");
+  expect(msa_page_owner(&bt, 0, own, nullptr), MSA_ERR_INVALID_ARG, 0, "page_owner no pages");
+  expect(msa_page_owner(&bt, 16, nullptr, nullptr), MSA_ERR_INVALID_ARG, 0, "page_owner null");
+  expect(msa_page_owner(nullptr, 16, own, nullptr), MSA_ERR_INVALID_ARG, 0, "page_owner null batch");
+  b2 = bt;
+  b2.num_reqs = 65535, b2.max_pages_per_req = 40000;
+  expect(msa_page_owner(&b2, 16, own, nullptr), MSA_ERR_INVALID_ARG, 0, "page_owner entry overflow");
+  b2.page_owner = own;
+  expect(msa_index_score(&b2, p, MSA_FP8_E4M3, 1.0f, &ic, f, nullptr, nullptr), MSA_ERR_INVALID_ARG, 0,
+         "index owner entry overflow");
+  b2 = bt;
+  b2.page_owner = own;
+  expect(msa_index_score(&b2, p, MSA_FP8_E4M3, 1.0f, &ic, f, nullptr, nullptr), MSA_OK, 1, "index with owner");
+  expect(msa_insert_index_score(&b2, f, f, f, p, MSA_FP8_E4M3, 1.0f, &kc, &vc, &ic, f, nullptr, nullptr), MSA_OK, 1,
+         "insert_index with owner");
 
   // selection
   expect(msa_block_maxpool_topk(&bt, f, 0, 16, i32, i32, nullptr), MSA_OK, 1, "topk ok");

@@ -56,7 +56,8 @@ class Cache(C.Structure):
 
 class Batch(C.Structure):
     _fields_ = [("num_reqs", C.c_int32), ("rows_per_req", C.c_int32), ("max_pages_per_req", C.c_int32),
-                ("shared_prefix_pages", C.c_int32), ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p)]
+                ("shared_prefix_pages", C.c_int32), ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p),
+                ("page_owner", C.c_void_p)]
 
 
 def test_status_strings(lib):
@@ -118,6 +119,14 @@ def test_host_validation_without_gpu(lib):
                                  C.byref(v), fake, fake, fake, None, C.c_size_t(0), None) == -1
     assert lib.msa_select_decode(C.byref(good), fake, 16, fake, 1, C.c_float(1.0), C.c_float(0.088), C.byref(k),
                                  C.byref(v), fake, fake, None, None, C.c_size_t(0), None) == -1
+    # owner map builder: a pool of at least one page, an output, 32-bit owner entries
+    lib.msa_page_owner.restype = C.c_int
+    assert lib.msa_page_owner(None, 16, fake, None) == -1
+    assert lib.msa_page_owner(C.byref(good), 0, fake, None) == -1
+    assert lib.msa_page_owner(C.byref(good), 16, None, None) == -1
+    wide = Batch(65535, 1, 40000, 0, fake, fake, fake)
+    assert lib.msa_page_owner(C.byref(wide), 16, fake, None) == -1
+    assert lib.msa_index_score(C.byref(wide), fake, 1, C.c_float(1.0), C.byref(idx), fake, None, None) == -1
     # fused insert + index: NVFP4 caches, FP8 queries, every row pointer present, value cache dim-major
     f32i = Cache(0, 0, 1, 16, 1.0, fake)
     ins = lib.msa_insert_index_score

@@ -42,17 +42,21 @@ def _dev(x, dt=None):
     return t if dt is None else t.to(dt)
 
 
-def gpu_setup(M, wl, hold_new=False, shared=True):
+def gpu_setup(M, wl, hold_new=False, shared=True, owner=False):
     """Device caches holding the workload's rows.  hold_new: leave out each request's
     last R positions (the step's new tokens) and return their rows, request-major
     [B*R], as a fourth value (k, v, idx, slots); rows of positions below 0 are zero
     with slot -1 (no token).  shared: declare the workload's shared prefix pages in
-    the batch (the indexer then scores them once for all requests)."""
+    the batch (the indexer then scores them once for all requests).  owner: the
+    batch carries the owner map msa_page_owner builds (physical-order scan)."""
     from block_sparse_attention_index_amd.decoder import MsaDecoder, make_caches
 
     dtype = {"nvfp4": M.MSA_NVFP4, "fp8": M.MSA_FP8_E4M3, "f32": M.MSA_F32}[wl.cache]
     k, v, idx = make_caches(dtype, wl.num_pages, wl.tensor_scale)
     batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R, wl.prefix_pages if shared else 0)
+    if owner:
+        own = M.msa_page_owner(batch, wl.num_pages)
+        batch = M.Batch(batch.block_table, batch.ctx_lens, wl.R, batch.struct.shared_prefix_pages, page_owner=own)
     dec = MsaDecoder(batch, k, v, idx, wl.topk)
     n_new = wl.B * wl.R
     nk = np.zeros((n_new, 4, 128), np.float32)
@@ -169,6 +173,11 @@ CASES = {
     # memory on demand and attention reads the table row from memory instead of LDS
     "wide_table": lambda: W.make_workload(3, seed=34, B=3, len_div=32, table_width=3100),
     "wide_table_r4": lambda: W.make_workload(4, seed=35, B=2, len_div=32, R=4, table_width=3100),
+    # pools with pages no request uses, scattered among the used ones (the physical-order scan
+    # reads them and drops them)
+    "spare_pool": lambda: W.make_workload(3, seed=43, B=6, len_div=40, spare_pages=333),
+    "spare_pool_r4": lambda: W.make_workload(4, seed=44, lengths=[0, 1, 4, 127, 128, 131, 2052, 5000], R=4,
+                                             spare_pages=77),
 }
 
 
@@ -487,12 +496,12 @@ def test_sparse_decode_on_oracle_selection(M, oracle, case):
 
 
 # ---------------------------------------------------------------- whole step
-def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False):
+def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False, owner=False):
     if new_rows:  # the step itself inserts each request's last R rows
-        dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True)
+        dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True, owner=owner)
         dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new, fused=fused)
     else:
-        dec, q_idx, q = gpu_setup(M, wl)
+        dec, q_idx, q = gpu_setup(M, wl, owner=owner)
         dec.step(q_idx, q, wl.q_scale, wl.sm_scale, fused=fused)
     torch.cuda.synchronize()
     g_sel, g_cnt = dec.sel.cpu().numpy(), dec.cnt.cpu().numpy()
@@ -696,6 +705,114 @@ def test_graph_replay_matches_eager(M, oracle, case, new_rows):
         x = torch.randn(1000, device="cuda").sum()  # unrelated eager work between replays
         torch.cuda.synchronize()
         del x
+
+
+# ---------------------------------------------------------------- physical-order scan (owner map)
+
+def _owner_np(wl, lengths):
+    """The owner map of a table and lengths, built by hand: b * max_pages + j at page
+    table[b][j] for j < ceil(L_b / 128), -1 elsewhere."""
+    own = np.full(wl.num_pages, -1, np.int32)
+    for b in range(wl.B):
+        for j in range(-(-int(lengths[b]) // 128)):
+            own[wl.block_table[b, j]] = b * wl.max_pages + j
+    return own
+
+
+OWNER_CASES = ["cfg2_small", "cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r5", "r8", "many_reqs",
+               "wide_table", "wide_table_r4", "spare_pool", "spare_pool_r4", "topk64"]
+
+
+@pytest.mark.parametrize("case", ["cfg3_small", "ragged", "wide_table", "spare_pool", "spare_pool_r4"])
+def test_page_owner_builds_the_inverse_table(M, oracle, case):
+    """msa_page_owner: bitwise the map built by hand from the table and lengths."""
+    wl = CASES[case]()
+    _print_case(case, wl)
+    batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R)
+    out = torch.full((wl.num_pages,), 12345, dtype=torch.int32, device="cuda")
+    M.msa_page_owner(batch, wl.num_pages, out)
+    assert np.array_equal(out.cpu().numpy(), _owner_np(wl, wl.lengths))
+
+
+@pytest.mark.parametrize("case", OWNER_CASES)
+@pytest.mark.parametrize("insert", [False, True])
+def test_owned_scan_equals_table_scan(M, oracle, case, insert):
+    """The scan in physical page order: bitwise the block scores of the chunk-mapped scan
+    (and, with the fused insert, bitwise the same cache bytes).  Its owner map is the one
+    the previous step left (lengths L_b - R: the pages of the step's new rows may be
+    missing), and every other entry holds junk, some of it naming real blocks whose table
+    entries point elsewhere.  Afterwards the map holds the pages of the new rows too."""
+    wl = CASES[case]()
+    _print_case(f"{case} insert={insert}", wl)
+    dec_a, q_idx, _, (nk, nv, ni, ns) = gpu_setup(M, wl, hold_new=True)
+    dec_b, _, _, _ = gpu_setup(M, wl, hold_new=True)
+    prev = np.maximum(wl.lengths.astype(np.int64) - wl.R, 0)
+    own = _owner_np(wl, prev)
+    rng = np.random.default_rng(7)
+    junk = own < 0
+    own[junk] = rng.integers(-3, wl.B * wl.max_pages + 3, size=int(junk.sum()), dtype=np.int32)
+    own_t = _dev(own)
+    dec_b.batch = M.Batch(dec_b.batch.block_table, dec_b.batch.ctx_lens, wl.R, page_owner=own_t)
+    dec_a.insert(nk, nv, ni, ns)
+    dec_a.index(q_idx, wl.q_scale)
+    dec_b.block_scores.fill_(3.0)
+    if insert:
+        dec_b.insert_index(nk, nv, ni, q_idx, wl.q_scale)
+    else:
+        dec_b.insert(nk, nv, ni, ns)
+        dec_b.index(q_idx, wl.q_scale)
+    torch.cuda.synchronize()
+    for ca, cb in ((dec_a.idx, dec_b.idx), (dec_a.k, dec_b.k), (dec_a.v, dec_b.v)):
+        assert torch.equal(ca.pages, cb.pages)
+    assert torch.equal(dec_a.block_scores.view(torch.int32), dec_b.block_scores.view(torch.int32))
+    after = own_t.cpu().numpy()
+    full = _owner_np(wl, wl.lengths)
+    used = full >= 0
+    assert np.array_equal(after[used], full[used])
+    assert np.array_equal(after[~used], own[~used])  # only the new rows' pages are written
+
+
+@pytest.mark.parametrize("case", ["cfg3_small", "ragged_r4", "r8", "spare_pool", "topk64"])
+@pytest.mark.parametrize("new_rows", [False, True])
+def test_full_step_owned_scan(M, oracle, case, new_rows):
+    """Steps 0-4 with the physical-order scan (fused launches), against the oracle."""
+    wl = CASES[case]()
+    _print_case(f"{case} owner map new_rows={new_rows}", wl)
+    _check_full_step(M, oracle, wl, new_rows=new_rows, owner=True)
+
+
+def test_graph_replay_owned_scan(M, oracle):
+    """The physical-order step captured and replayed (the owner-map writes repeat the same
+    values): every replay bitwise the eager result."""
+    wl = CASES["spare_pool"]()
+    _print_case("graph replay owner map", wl)
+    dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True, owner=True)
+    dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new)
+    torch.cuda.synchronize()
+    eager, eager_bs = dec.out.clone(), dec.block_scores.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new)
+    for _ in range(3):
+        dec.out.zero_()
+        dec.block_scores.fill_(1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out.view(torch.int32), eager.view(torch.int32))
+        assert torch.equal(dec.block_scores.view(torch.int32), eager_bs.view(torch.int32))
+        x = torch.randn(1000, device="cuda").sum()
+        torch.cuda.synchronize()
+        del x
+
+
+def test_full_size_config3_owned_sampled(M, oracle):
+    """Configuration 3 at full size through the physical-order scan, the step inserting its
+    new rows (the benchmark's launch configuration); three sampled requests end to end."""
+    wl = W.make_workload(3, seed=0)
+    _print_case("config 3 full size, owner map", wl)
+    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 7]
+    _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
 
 
 def test_full_size_config3_sampled(M, oracle):

@@ -97,12 +97,14 @@ class Workload:
 
 def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int = 1,
                   lengths: list[int] | None = None, R: int | None = None, cache: str | None = None,
-                  topk: int = TOPK, table_width: int | None = None) -> Workload:
+                  topk: int = TOPK, table_width: int | None = None, spare_pages: int = 0) -> Workload:
     """Build the shapes of a configuration.  ``B``/``len_div`` shrink it for
     parity tests; ``lengths`` overrides the drawn lengths (edge cases);
     ``cache`` = "fp8" stores the same shapes in FP8 caches instead of NVFP4;
     ``topk`` sets the selected blocks per row; ``table_width`` pads the block
-    table with unused columns (page 0) up to that many entries per request."""
+    table with unused columns (page 0) up to that many entries per request;
+    ``spare_pages`` adds that many pages no request uses to the pool (scattered
+    among the used ones when the table is permuted)."""
     cfg = CONFIGS[config]
     rng = np.random.default_rng([seed, 0])
     B = cfg["B"] if B is None else B
@@ -125,7 +127,7 @@ def make_workload(config: int, seed: int = 0, B: int | None = None, len_div: int
     own_pages = [max(0, -(-int(L) // PAGE) - prefix_pages) for L in lens]
     max_pages = max(1, max(prefix_pages + n for n in own_pages))
     num_pages = prefix_pages + sum(own_pages)
-    num_pages = max(num_pages, 1)
+    num_pages = max(num_pages, 1) + spare_pages
     if cfg["table"] == "contiguous":
         perm = np.arange(num_pages, dtype=np.int64)
     else:
