@@ -229,9 +229,10 @@ INDEX_KERNEL_SOURCES = ["include/msa.h", "block_sparse_attention_index_amd/csrc/
 
 def recorded_traffic(key="insert-index-kernel-traffic-bytes-per-launch"):
     """HBM bytes per launch of the step's index kernel (with the insert fused in,
-    or, by key, the plain scan) as the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary records them (copy-kernel calibrated), or None when the
-    summary is absent or the kernel's sources changed since it was taken."""
+    or, by key, the plain scan; "owned-" keys: the physical-order scan) as the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary records them
+    (copy-kernel calibrated), or None when the summary is absent or the
+    kernel's sources changed since it was taken."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
@@ -558,12 +559,14 @@ def main():
                       + " with the insert fused in (steps 0-2)",
                       "achieved": idx_gbps,
                       "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": idx_gbps / PEAK_HBM_GBPS,
-                      "traffic": recorded_traffic() if headline else None,
+                      "traffic": recorded_traffic(("owned-" if owned else "") +
+                                                  "insert-index-kernel-traffic-bytes-per-launch") if headline else None,
                       "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2 + WRITE_SIZE x 1, copy-calibrated)",
                       "bytes_per_launch": nbytes["insert_index"], "avg_launch_us": us["insert_index"],
                       "plain_scan": {"bytes_per_launch": nbytes["index"], "avg_launch_us": us["index"],
                                      "achieved": nbytes["index"] / (us["index"] * 1e-6) / 1e9,
-                                     "traffic": recorded_traffic("index-kernel-traffic-bytes-per-launch")
+                                     "traffic": recorded_traffic(("owned-" if owned else "") +
+                                                                 "index-kernel-traffic-bytes-per-launch")
                                      if headline else None}}),
         "prefix_mfma": None if not P else {
             "kernel": "prefix_index_kernel (shared-prefix scores on v_mfma_f32_16x16x32_f16)",
