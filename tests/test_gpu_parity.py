@@ -178,6 +178,10 @@ CASES = {
     "spare_pool": lambda: W.make_workload(3, seed=43, B=6, len_div=40, spare_pages=333),
     "spare_pool_r4": lambda: W.make_workload(4, seed=44, lengths=[0, 1, 4, 127, 128, 131, 2052, 5000], R=4,
                                              spare_pages=77),
+    # two rows: new rows on one page, across a page boundary (129: positions 127 and 128), and
+    # contexts shorter than the rows
+    "ragged_r2": lambda: W.make_workload(4, seed=45, lengths=[0, 1, 2, 128, 129, 130, 2049, 5000], R=2,
+                                         spare_pages=19),
 }
 
 
@@ -719,8 +723,8 @@ def _owner_np(wl, lengths):
     return own
 
 
-OWNER_CASES = ["cfg2_small", "cfg3_small", "cfg4_small", "ragged", "ragged_r4", "r3", "r5", "r8", "many_reqs",
-               "wide_table", "wide_table_r4", "spare_pool", "spare_pool_r4", "topk64"]
+OWNER_CASES = ["cfg2_small", "cfg3_small", "cfg4_small", "ragged", "ragged_r2", "union_r2", "ragged_r4", "r3", "r5",
+               "r7", "r8", "many_reqs", "wide_table", "wide_table_r4", "spare_pool", "spare_pool_r4", "topk64"]
 
 
 @pytest.mark.parametrize("case", ["cfg3_small", "ragged", "wide_table", "spare_pool", "spare_pool_r4"])
@@ -772,7 +776,7 @@ def test_owned_scan_equals_table_scan(M, oracle, case, insert):
     assert np.array_equal(after[~used], own[~used])  # only the new rows' pages are written
 
 
-@pytest.mark.parametrize("case", ["cfg3_small", "ragged_r4", "r8", "spare_pool", "topk64"])
+@pytest.mark.parametrize("case", ["cfg3_small", "ragged_r2", "ragged_r4", "r8", "spare_pool", "topk64"])
 @pytest.mark.parametrize("new_rows", [False, True])
 def test_full_step_owned_scan(M, oracle, case, new_rows):
     """Steps 0-4 with the physical-order scan (fused launches), against the oracle."""
