@@ -810,6 +810,60 @@ def test_graph_replay_owned_scan(M, oracle):
         del x
 
 
+def _random_case(seed):
+    """A seeded random small batch: B, R, ragged lengths (empty contexts included), topk, cache
+    format, spare pool pages, owner map, new rows."""
+    rng = np.random.default_rng([seed, 99])
+    R = int(rng.choice([1, 1, 2, 3, 4, 8]))
+    B = int(rng.integers(1, 13))
+    lengths = rng.integers(0, 3200, size=B)
+    lengths[rng.random(B) < 0.15] = 0
+    lengths[rng.random(B) < 0.15] = rng.integers(1, 5)
+    topk = int(rng.choice([1, 4, 16, 16, 32, 64]))
+    cache = "fp8" if rng.random() < 0.3 else "nvfp4"
+    spare = int(rng.integers(0, 50))
+    owner = cache == "nvfp4" and rng.random() < 0.6
+    new_rows = bool(rng.random() < 0.6)
+    wl = W.make_workload(4 if R > 1 else 3, seed=seed, lengths=lengths.tolist(), R=R, topk=topk, cache=cache,
+                         spare_pages=spare)
+    return wl, owner, new_rows
+
+
+@pytest.mark.parametrize("seed", list(range(500, 548)))
+def test_random_small_batches(M, oracle, seed):
+    """Seeded random small batches through the whole step (fused launches), against the oracle."""
+    wl, owner, new_rows = _random_case(seed)
+    _print_case(f"random seed={seed} owner={owner} new_rows={new_rows} topk={wl.topk} cache={wl.cache}", wl)
+    _check_full_step(M, oracle, wl, new_rows=new_rows, owner=owner)
+
+
+@pytest.mark.parametrize("seed", list(range(600, 608)))
+def test_random_prefill_chunks(M, oracle, seed):
+    """Seeded random prompt chunks (9 to 300 causal rows per request, 1 to 3 requests) through the
+    dense indexer, the selection and the prefill attention, against the oracle."""
+    rng = np.random.default_rng([seed, 98])
+    B = int(rng.integers(1, 4))
+    R = int(rng.integers(9, 301))
+    lengths = rng.integers(R, R + 4000, size=B)
+    topk = int(rng.choice([4, 16, 32]))
+    cache = "fp8" if rng.random() < 0.3 else "nvfp4"
+    wl = W.make_workload(6, seed=seed, lengths=lengths.tolist(), R=R, topk=topk, cache=cache)
+    _print_case(f"random prefill seed={seed} topk={topk} cache={cache}", wl)
+    _check_full_step(M, oracle, wl, new_rows=bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("seed", list(range(700, 706)))
+def test_random_shared_prefix(M, oracle, seed):
+    """Seeded random shared-prefix batches (the prefix shrunk to 16-64 pages, 1 to 80 requests,
+    1 to 4 rows) through the prefix product, the fused scan and the rest of the step."""
+    rng = np.random.default_rng([seed, 97])
+    wl = W.make_workload(5, seed=seed, B=int(rng.integers(1, 81)), len_div=int(rng.choice([32, 64, 128])),
+                         R=int(rng.choice([1, 1, 2, 4])))
+    new_rows = bool(rng.random() < 0.6)
+    _print_case(f"random shared prefix seed={seed} new_rows={new_rows}", wl)
+    _check_full_step(M, oracle, wl, new_rows=new_rows)
+
+
 def test_full_size_config3_owned_sampled(M, oracle):
     """Configuration 3 at full size through the physical-order scan, the step inserting its
     new rows (the benchmark's launch configuration); three sampled requests end to end."""
