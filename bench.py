@@ -251,7 +251,7 @@ def recorded_traffic(key="insert-index-kernel-traffic-bytes-per-launch"):
 def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4", scan="owner"):
     """Device state of the benchmark workload: filled caches (``n_replicas`` copies),
     decoders, the step's new rows and quantised queries.  scan="owner": the batch
-    carries the owner map (NVFP4 decode batches without a shared prefix), which the
+    carries the owner map (decode batches without a shared prefix), which the
     index scan then reads in physical page order; "table": it walks the table rows."""
     import torch
 
@@ -270,7 +270,7 @@ def setup(seed=0, n_replicas=2, config=CONFIG_ID, kv="nvfp4", scan="owner"):
     lens = torch.from_numpy(wl.lengths).to(dev)
     batch = M.Batch(table, lens, wl.R, wl.prefix_pages)
     table_batch, owner_us = batch, None
-    if scan == "owner" and kv == "nvfp4" and not wl.prefix_pages and wl.R <= M.MSA_MAX_ROWS:
+    if scan == "owner" and not wl.prefix_pages and wl.R <= M.MSA_MAX_ROWS:
         # the block table's inverse, kept with the table (the step itself records the pages of
         # its new rows); built here once, its build time reported beside the step
         own = M.msa_page_owner(batch, wl.num_pages)

@@ -125,9 +125,9 @@ typedef struct {
  * than the prefix are fine (invisible tokens are masked as usual).  With an
  * F32 index cache P is not used.  0 <= P <= max_pages_per_req.
  *
- * page_owner (may be NULL) lets the NVFP4 decode scan (msa_index_score and
- * msa_insert_index_score with an NVFP4 index cache, R <= MSA_MAX_ROWS, no
- * token_scores, P = 0) read the index pool in physical page order instead of
+ * page_owner (may be NULL) lets the decode scan (msa_index_score and
+ * msa_insert_index_score with an NVFP4 or FP8 index cache, R <= MSA_MAX_ROWS,
+ * no token_scores, P = 0) read the index pool in physical page order instead of
  * walking each request's table row.  Entry p names the block that page p
  * holds, b * max_pages_per_req + j where block_table[b][j] == p.  Required:
  * for every request b and every block j below the page of its first new row

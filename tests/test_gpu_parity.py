@@ -180,6 +180,9 @@ CASES = {
                                              spare_pages=77),
     # two rows: new rows on one page, across a page boundary (129: positions 127 and 128), and
     # contexts shorter than the rows
+    "fp8_spare_pool": lambda: W.make_workload(3, seed=46, B=5, len_div=40, spare_pages=211, cache="fp8"),
+    "fp8_spare_pool_r3": lambda: W.make_workload(4, seed=47, lengths=[0, 2, 3, 127, 128, 130, 2051, 4000], R=3,
+                                                 spare_pages=97, cache="fp8"),
     "ragged_r2": lambda: W.make_workload(4, seed=45, lengths=[0, 1, 2, 128, 129, 130, 2049, 5000], R=2,
                                          spare_pages=19),
 }
@@ -724,7 +727,9 @@ def _owner_np(wl, lengths):
 
 
 OWNER_CASES = ["cfg2_small", "cfg3_small", "cfg4_small", "ragged", "ragged_r2", "union_r2", "ragged_r4", "r3", "r5",
-               "r7", "r8", "many_reqs", "wide_table", "wide_table_r4", "spare_pool", "spare_pool_r4", "topk64"]
+               "r7", "r8", "many_reqs", "wide_table", "wide_table_r4", "spare_pool", "spare_pool_r4", "topk64",
+               "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r5", "fp8_r7", "fp8_r8", "fp8_many_reqs",
+               "fp8_spare_pool", "fp8_spare_pool_r3"]
 
 
 @pytest.mark.parametrize("case", ["cfg3_small", "ragged", "wide_table", "spare_pool", "spare_pool_r4"])
@@ -776,7 +781,8 @@ def test_owned_scan_equals_table_scan(M, oracle, case, insert):
     assert np.array_equal(after[~used], own[~used])  # only the new rows' pages are written
 
 
-@pytest.mark.parametrize("case", ["cfg3_small", "ragged_r2", "ragged_r4", "r8", "spare_pool", "topk64"])
+@pytest.mark.parametrize("case", ["cfg3_small", "ragged_r2", "ragged_r4", "r8", "spare_pool", "topk64",
+                                  "fp8_ragged_r4", "fp8_spare_pool", "fp8_spare_pool_r3", "fp8_topk8"])
 @pytest.mark.parametrize("new_rows", [False, True])
 def test_full_step_owned_scan(M, oracle, case, new_rows):
     """Steps 0-4 with the physical-order scan (fused launches), against the oracle."""
@@ -822,7 +828,7 @@ def _random_case(seed):
     topk = int(rng.choice([1, 4, 16, 16, 32, 64]))
     cache = "fp8" if rng.random() < 0.3 else "nvfp4"
     spare = int(rng.integers(0, 50))
-    owner = cache == "nvfp4" and rng.random() < 0.6
+    owner = rng.random() < 0.6
     new_rows = bool(rng.random() < 0.6)
     wl = W.make_workload(4 if R > 1 else 3, seed=seed, lengths=lengths.tolist(), R=R, topk=topk, cache=cache,
                          spare_pages=spare)
@@ -870,6 +876,15 @@ def test_full_size_config3_owned_sampled(M, oracle):
     wl = W.make_workload(3, seed=0)
     _print_case("config 3 full size, owner map", wl)
     rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 7]
+    _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
+
+
+def test_full_size_config3_fp8_owned_sampled(M, oracle):
+    """The 128K-context batch in FP8 caches at full size through the physical-order scan,
+    the step inserting its new rows; two sampled requests end to end."""
+    wl = W.make_workload(3, seed=0, cache="fp8")
+    _print_case("config 3 fp8 full size, owner map", wl)
+    rows = [int(np.argmin(wl.lengths)), 11]
     _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
 
 
