@@ -78,11 +78,13 @@ def algorithmic_bytes(wl, sel, cnt):
             "total": idx + kv + q_bytes + out_bytes + table + insert, "kv_tokens": kv_tokens}
 
 
-def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
+def cpu_baseline(wl, sample_reqs, min_seconds=10.0, last_rows=None):
     """The oracle (plain FP64 C, OpenMP over (request, row, group)) timed on a
     bounded sample of the same workload: all four steps for `sample_reqs`
-    requests, repeated until min_seconds of work; scaled to whole-batch
-    steps/s by context tokens (work is linear in them)."""
+    requests (with last_rows, only the last rows of each request's chunk: a
+    shorter chunk at the same context), repeated until min_seconds of work;
+    scaled to whole-batch steps/s by rows x context tokens (work is linear in
+    both)."""
     import oracle as O
     import workload as W
 
@@ -102,9 +104,11 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
         s = wl.slots(int(b), pos)
         ci.write(s, xi), ck.write(s, xk), cv.write(s, xv)
     qi32, q32 = W.queries(wl)
-    qi = O.decode_queries(O.quantize_queries(qi32[rows], wl.q_scale), O.FP8_E4M3, wl.q_scale)
-    q = O.decode_queries(O.quantize_queries(q32[rows], wl.q_scale), O.FP8_E4M3, wl.q_scale)
-    bt = O.OracleBatch(wl.block_table[rows], wl.lengths[rows], wl.R)
+    R = wl.R if last_rows is None else min(last_rows, wl.R)
+    qi32, q32 = np.ascontiguousarray(qi32[rows][:, wl.R - R:]), np.ascontiguousarray(q32[rows][:, wl.R - R:])
+    qi = O.decode_queries(O.quantize_queries(qi32, wl.q_scale), O.FP8_E4M3, wl.q_scale)
+    q = O.decode_queries(O.quantize_queries(q32, wl.q_scale), O.FP8_E4M3, wl.q_scale)
+    bt = O.OracleBatch(wl.block_table[rows], wl.lengths[rows], R)
     reps, t0 = 0, time.perf_counter()
     while True:
         O.decode_step(bt, qi, q, wl.sm_scale, ci, ck, cv, wl.topk)
@@ -113,13 +117,14 @@ def cpu_baseline(wl, sample_reqs, min_seconds=10.0):
         if el >= min_seconds:
             break
     per_sample = el / reps
-    frac = float(wl.lengths[rows].astype(np.int64).sum()) / float(wl.lengths.astype(np.int64).sum())
+    frac = (R * float(wl.lengths[rows].astype(np.int64).sum())) / (wl.R * float(wl.lengths.astype(np.int64).sum()))
     full_step = per_sample / frac
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    part = "" if R == wl.R else f", the last {R} of each chunk's {wl.R} rows"
     return {"value": 1.0 / full_step, "unit": "layer-steps/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(rows)} of {wl.B} requests ({int(wl.lengths[rows].sum())} of "
-                      f"{int(wl.lengths.sum())} context tokens), full step x{reps} in {el:.1f} s, "
-                      f"scaled by context tokens"}
+                      f"{int(wl.lengths.sum())} context tokens{part}), full step x{reps} in {el:.1f} s, "
+                      f"scaled by rows x context tokens"}
 
 
 QKV_HEADS = 45  # 32 query heads, 4 key, 4 value, 4 index queries, 1 index key
@@ -523,9 +528,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         rng = np.random.default_rng(args.seed)
-        sample = sorted(rng.choice(wl.B, size=min(args.cpu_sample, wl.B), replace=False).tolist())
-        log(f"cpu baseline: oracle on requests {sample}")
-        cpu = cpu_baseline(wl, sample)
+        prefill_rows = 64 if wl.R > M.MSA_MAX_ROWS else None  # a prompt chunk: one request, its last rows
+        n_sample = 1 if prefill_rows else min(args.cpu_sample, wl.B)
+        sample = sorted(rng.choice(wl.B, size=n_sample, replace=False).tolist())
+        log(f"cpu baseline: oracle on requests {sample}" + (f", last {prefill_rows} rows" if prefill_rows else ""))
+        cpu = cpu_baseline(wl, sample, last_rows=prefill_rows)
         log(f"cpu baseline: {cpu['value']:.3f} steps/s on {cpu['cores']} threads")
 
     line = {

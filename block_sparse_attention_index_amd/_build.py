@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["msa_api.hip", "msa_insert.hip", "msa_index.hip", "msa_prefix.hip", "msa_topk.hip", "msa_attn.hip",
-           "msa_qkv.hip", "msa_stream.hip"]
+           "msa_qkv.hip", "msa_stream.hip", "msa_prefill_attn.hip"]
 # Per-file flags (none at present: every file keeps IEEE NaN semantics, so the
 # indexers' max-pools skip NaN scores as the definition does).
 EXTRA_FLAGS = {}

@@ -143,6 +143,8 @@ int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t 
 
 size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk) {
   if (check_batch(batch, MSA_MAX_PREFILL_ROWS) != MSA_OK || topk < 1 || topk > MSA_MAX_TOPK) return 0;
+  // prefill chunks (NVFP4 / FP8 only): the block-major route's partials, 0 where it does not apply
+  if (batch->rows_per_req > MSA_MAX_ROWS) return msa_prefill_block_bytes(batch, topk);
   // F32 caches: per-block partial results; NVFP4 / FP8: the partials of rows split over several workgroups
   const size_t f32 = msa_decode_partials_bytes(batch, topk), split = msa_split_partials_bytes(batch);
   return f32 > split ? f32 : split;
@@ -164,7 +166,7 @@ int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, fl
   if (!finite_pos(sm_scale) || (q_dtype == MSA_FP8_E4M3 && !finite_pos(q_scale))) return MSA_ERR_INVALID_ARG;
   if (workspace_bytes < msa_workspace_bytes(batch, topk)) return MSA_ERR_WORKSPACE;
   return msa_launch_sparse_decode(batch, q, q_dtype, q_scale, sm_scale, k_cache, v_cache, sel_blocks, sel_count,
-                                  topk, out, workspace, stream) == 0
+                                  topk, out, workspace, workspace_bytes, stream) == 0
              ? MSA_OK
              : MSA_ERR_HIP;
 }
@@ -207,7 +209,7 @@ int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t
   if (!finite_pos(sm_scale) || !finite_pos(q_scale)) return MSA_ERR_INVALID_ARG;
   if (workspace && workspace_bytes < msa_workspace_bytes(batch, topk)) return MSA_ERR_WORKSPACE;
   return msa_launch_select_decode(batch, block_scores, topk, q, q_scale, sm_scale, k_cache, v_cache, sel_blocks,
-                                  sel_count, out, workspace, stream) == 0
+                                  sel_count, out, workspace, workspace ? workspace_bytes : 0, stream) == 0
              ? MSA_OK
              : MSA_ERR_HIP;
 }

@@ -856,11 +856,18 @@ extern "C" size_t msa_split_partials_bytes(const msa_batch* bt) {
 template <bool SELECT, bool FP8>
 static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, float sm_scale,
                          const msa_cache* kc, const msa_cache* vc, const float* block_scores, int32_t* sel,
-                         int32_t* cnt, int32_t topk, float* out, float* part, hipStream_t s) {
+                         int32_t* cnt, int32_t topk, float* out, float* part, size_t part_bytes, hipStream_t s) {
   const int R = bt->rows_per_req, P = bt->max_pages_per_req;
   // scores enter the kernel's softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   const int km = SELECT ? select_kmax(P) : 8;
+  const size_t block_bytes = FP8 ? 0 : msa_prefill_block_bytes(bt, topk);
+  if (R > MSA_MAX_ROWS && part && block_bytes > 0 && part_bytes >= block_bytes) {
+    // prefill chunk with room for the block-major partials (NVFP4): the selection
+    // first (when fused), then each selected block once for all the rows that chose it
+    if (SELECT && msa_launch_topk(bt, block_scores, 0, topk, sel, cnt, s) != 0) return -1;
+    return msa_launch_prefill_block_attend(bt, q, q_scale, sm_scale, kc, vc, sel, cnt, topk, out, part, s);
+  }
   if (R > MSA_MAX_ROWS) {  // prefill chunk: one row per workgroup
     const dim3 pgrid(kGroups * R, bt->num_reqs);
 #define MSA_PREFILL(K)                                                                                          \
@@ -923,14 +930,14 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
 extern "C" int msa_launch_sparse_decode(const msa_batch* bt, const void* q, int32_t q_dtype, float q_scale,
                                         float sm_scale, const msa_cache* kc, const msa_cache* vc,
                                         const int32_t* sel, const int32_t* cnt, int32_t topk, float* out,
-                                        void* workspace, hipStream_t s) {
+                                        void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int B = bt->num_reqs, R = bt->rows_per_req, P = bt->max_pages_per_req;
   if (kc->dtype == MSA_NVFP4)
     return launch_attend<false, false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
-                                       (int32_t*)cnt, topk, out, (float*)workspace, s);
+                                       (int32_t*)cnt, topk, out, (float*)workspace, workspace_bytes, s);
   if (kc->dtype == MSA_FP8_E4M3)
     return launch_attend<false, true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, nullptr, (int32_t*)sel,
-                                      (int32_t*)cnt, topk, out, (float*)workspace, s);
+                                      (int32_t*)cnt, topk, out, (float*)workspace, workspace_bytes, s);
   const int S = (int)f32_splits(bt, topk);
   float* part_o = (float*)workspace;
   float* part_ml = part_o + (size_t)B * kGroups * S * R * kHpg * kDim;
@@ -967,16 +974,17 @@ extern "C" int msa_launch_sparse_decode_noalloc(const msa_batch* bt, const void*
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return -1;
     g_scratch_addr[dev].store(ptr, std::memory_order_release);
   }
-  return msa_launch_sparse_decode(bt, q, q_dtype, q_scale, sm_scale, kc, vc, sel, cnt, topk, out, ptr, s);
+  return msa_launch_sparse_decode(bt, q, q_dtype, q_scale, sm_scale, kc, vc, sel, cnt, topk, out, ptr,
+                                  MSA_NOALLOC_SCRATCH_BYTES, s);
 }
 
 extern "C" int msa_launch_select_decode(const msa_batch* bt, const float* block_scores, int32_t topk,
                                         const void* q, float q_scale, float sm_scale, const msa_cache* kc,
                                         const msa_cache* vc, int32_t* sel, int32_t* cnt, float* out,
-                                        void* workspace, hipStream_t s) {
+                                        void* workspace, size_t workspace_bytes, hipStream_t s) {
   if (kc->dtype == MSA_FP8_E4M3)
     return launch_attend<true, true>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
-                                     out, (float*)workspace, s);
+                                     out, (float*)workspace, workspace_bytes, s);
   return launch_attend<true, false>(bt, (const uint8_t*)q, q_scale, sm_scale, kc, vc, block_scores, sel, cnt, topk,
-                                    out, (float*)workspace, s);
+                                    out, (float*)workspace, workspace_bytes, s);
 }

@@ -51,12 +51,16 @@ size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk);
 size_t msa_split_partials_bytes(const msa_batch* b);
 int msa_launch_select_decode(const msa_batch* b, const float* block_scores, int32_t topk, const void* q,
                              float q_scale, float sm_scale, const msa_cache* kc, const msa_cache* vc, int32_t* sel,
-                             int32_t* cnt, float* out, void* workspace, hipStream_t stream);
+                             int32_t* cnt, float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t msa_prefill_block_bytes(const msa_batch* b, int32_t topk);
+int msa_launch_prefill_block_attend(const msa_batch* b, const uint8_t* q, float q_scale, float sm_scale,
+                                    const msa_cache* kc, const msa_cache* vc, const int32_t* sel, const int32_t* cnt,
+                                    int32_t topk, float* out, void* workspace, hipStream_t stream);
 int msa_launch_sparse_decode_noalloc(const msa_batch* b, const void* q, int32_t q_dtype, float q_scale,
                                      float sm_scale, const msa_cache* kc, const msa_cache* vc, const int32_t* sel,
                                      const int32_t* cnt, int32_t topk, float* out, hipStream_t stream);
 int msa_launch_stream_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, hipStream_t stream);
 int msa_launch_sparse_decode(const msa_batch* b, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
                              const msa_cache* kc, const msa_cache* vc, const int32_t* sel, const int32_t* cnt,
-                             int32_t topk, float* out, void* workspace, hipStream_t stream);
+                             int32_t topk, float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 }

@@ -27,13 +27,16 @@ STUB(msa_launch_insert_index_score, const msa_batch*, const float*, const float*
      const msa_cache*, const msa_cache*, const msa_cache*, float*, float*, hipStream_t)
 STUB(msa_launch_topk, const msa_batch*, const float*, int32_t, int32_t, int32_t*, int32_t*, hipStream_t)
 STUB(msa_launch_select_decode, const msa_batch*, const float*, int32_t, const void*, float, float, const msa_cache*,
-     const msa_cache*, int32_t*, int32_t*, float*, void*, hipStream_t)
+     const msa_cache*, int32_t*, int32_t*, float*, void*, size_t, hipStream_t)
 STUB(msa_launch_sparse_decode_noalloc, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
      const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, hipStream_t)
 STUB(msa_launch_stream_read, const void*, int64_t, int32_t, uint32_t*, hipStream_t)
 STUB(msa_launch_page_owner, const msa_batch*, int32_t, int32_t*, hipStream_t)
 STUB(msa_launch_sparse_decode, const msa_batch*, const void*, int32_t, float, float, const msa_cache*,
-     const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, void*, hipStream_t)
+     const msa_cache*, const int32_t*, const int32_t*, int32_t, float*, void*, size_t, hipStream_t)
+extern "C" size_t msa_prefill_block_bytes(const msa_batch* b, int32_t topk) {  // any size for prefill chunks
+  return b->rows_per_req > MSA_MAX_ROWS ? (size_t)b->num_reqs * b->rows_per_req * topk * 4 * 2112 : 0;
+}
 extern "C" size_t msa_decode_partials_bytes(const msa_batch* b, int32_t topk) {
   return (size_t)b->num_reqs * 4 * (size_t)b->rows_per_req * 8 * (size_t)topk * 130 * 4;
 }
@@ -139,6 +142,16 @@ int main() {
   expect(ws == std::max(msa_decode_partials_bytes(&bt, 16), msa_split_partials_bytes(&bt)) ? MSA_OK : -99, MSA_OK, 0,
          "workspace size");
   expect(msa_workspace_bytes(nullptr, 16) == 0 ? MSA_OK : -99, MSA_OK, 0, "workspace size of no batch");
+  {  // a prefill chunk: the block-major route's partials, and no per-block F32 partials
+    msa_batch pb = bt;
+    pb.rows_per_req = 64;
+    const size_t pws = msa_workspace_bytes(&pb, 16);
+    expect(pws == msa_prefill_block_bytes(&pb, 16) && pws > 0 ? MSA_OK : -99, MSA_OK, 0, "prefill workspace size");
+    expect(msa_sparse_decode(&pb, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, p, pws, nullptr), MSA_OK,
+           1, "prefill decode ok");
+    expect(msa_sparse_decode(&pb, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, p, pws - 1, nullptr),
+           MSA_ERR_WORKSPACE, 0, "prefill decode workspace");
+  }
   expect(msa_sparse_decode(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, p, ws, nullptr), MSA_OK, 1,
          "decode ok");
   expect(msa_sparse_decode(&bt, p, MSA_FP8_E4M3, 1.0f, 0.088f, &kc, &vc, i32, i32, 16, f, p, ws - 1, nullptr),

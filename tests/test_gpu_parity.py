@@ -503,12 +503,18 @@ def test_sparse_decode_on_oracle_selection(M, oracle, case):
 
 
 # ---------------------------------------------------------------- whole step
-def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False, owner=False):
+def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False, owner=False, workspace=True):
+    """workspace=False (fused only): msa_select_decode without a workspace (no split rows, and
+    prefill chunks in the per-row form instead of the block-major one)."""
     if new_rows:  # the step itself inserts each request's last R rows
         dec, q_idx, q, new = gpu_setup(M, wl, hold_new=True, owner=owner)
+        if not workspace:
+            dec.workspace = None
         dec.step(q_idx, q, wl.q_scale, wl.sm_scale, new_tokens=new, fused=fused)
     else:
         dec, q_idx, q = gpu_setup(M, wl, owner=owner)
+        if not workspace:
+            dec.workspace = None
         dec.step(q_idx, q, wl.q_scale, wl.sm_scale, fused=fused)
     torch.cuda.synchronize()
     g_sel, g_cnt = dec.sel.cpu().numpy(), dec.cnt.cpu().numpy()
@@ -670,6 +676,66 @@ def test_prefill_select_decode_on_oracle_scores(M, oracle, case):
     err = _out_err(got, ref)
     print(f"  max per-vector relative error {err[~empty].max() if (~empty).any() else 0:.3e}", flush=True)
     assert err[~empty].max(initial=0.0) <= OUT_TOL
+
+
+@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512", "fp8_prefill"])
+def test_prefill_row_route(M, oracle, case):
+    """Prefill chunks through msa_select_decode without a workspace: the per-row form (one
+    workgroup per row) instead of the block-major one, against the oracle."""
+    wl = CASES[case]()
+    _print_case(f"{case} per-row route", wl)
+    _check_full_step(M, oracle, wl, fused=True, workspace=False)
+
+
+@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512"])
+def test_prefill_hand_selections_both_routes(M, oracle, case):
+    """msa_sparse_decode on a prefill chunk with hand-made selections: blocks named twice,
+    ranks in no order, counts from 0 to topk, and entries inside the count that name no
+    block (-1, or past the table), which count as absent.  Through the block-major route
+    (the workspace) and the per-row route (the no-allocation call, whose scratch array is
+    too small for the block-major partials), each against the oracle's attention on the
+    same sets with the absent entries left out."""
+    wl = CASES[case]()
+    _print_case(f"{case} hand-made selections", wl)
+    dec, q_idx, q = gpu_setup(M, wl)
+    assert M.msa_workspace_bytes(dec.batch, wl.topk) > M.MSA_NOALLOC_SCRATCH_BYTES
+    rng = np.random.default_rng(5)
+    p = row_positions(wl)
+    nb = np.maximum(p // 128 + 1, 0)
+    shape = (wl.B, wl.R, 4, wl.topk)
+    cnt = rng.integers(0, wl.topk + 1, size=shape[:3]).astype(np.int32)
+    cnt[p < 0] = 0
+    ids = np.floor(rng.random(shape) * nb[:, :, None, None]).astype(np.int32)
+    k = np.arange(wl.topk)[None, None, None, :]
+    inside = k < cnt[..., None]
+    absent = inside & (rng.random(shape) < 0.05)
+    sel_gpu = np.where(inside, ids, -1).astype(np.int32)
+    sel_gpu[absent] = np.where(rng.random(int(absent.sum())) < 0.5, -1, wl.max_pages + 3)
+    sel_ref = np.full(shape, -1, np.int32)
+    cnt_ref = np.zeros(shape[:3], np.int32)
+    keep = inside & ~absent
+    for idx in np.ndindex(*shape[:3]):
+        v = ids[idx][keep[idx]]
+        sel_ref[idx][:v.size] = v
+        cnt_ref[idx] = v.size
+    dec.sel.copy_(_dev(sel_gpu))
+    dec.cnt.copy_(_dev(cnt))
+    dec.attend(q, wl.q_scale, wl.sm_scale)
+    out_block = dec.out.clone()
+    out_row = torch.full_like(dec.out, 7.0)
+    M.msa_sparse_decode_noalloc(dec.batch, q, dec.q_dtype, wl.q_scale, wl.sm_scale, dec.k, dec.v, dec.sel, dec.cnt,
+                                wl.topk, out_row)
+    torch.cuda.synchronize()
+    _, ck, cv = oracle_caches(oracle, wl)
+    _, _, _, qd = oracle_queries(oracle, wl)
+    ref = oracle.attention(oracle_batch(oracle, wl), qd, wl.sm_scale, ck, cv, sel_ref, cnt_ref)
+    empty = np.repeat(cnt_ref == 0, 8, axis=2)
+    for name, got_t in (("block-major", out_block), ("per-row", out_row)):
+        got = got_t.cpu().numpy().astype(np.float64)
+        assert (got[empty] == 0).all(), name
+        err = _out_err(got, ref)
+        print(f"  {name}: max per-vector relative error {err[~empty].max(initial=0.0):.3e}", flush=True)
+        assert err[~empty].max(initial=0.0) <= OUT_TOL, name
 
 
 def test_full_step_deterministic(M, oracle):
