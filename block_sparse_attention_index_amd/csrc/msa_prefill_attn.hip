@@ -27,7 +27,7 @@
 //     v_mfma_f32_16x16x32_f16, with the token order of the decode form (row i
 //     of M-tile m is token 32(i/4) + 8(m/2) + 4(m%2) + i%4), so that the
 //     softmax registers are the P operand as they stand.
-//  3. pf_combine_kernel, one workgroup per (request, row, group): with M the
+//  3. pf_combine_kernel, one workgroup per two (request, row, group): with M the
 //     largest partial max and w_k = exp2(m_k - M), out = v_scale *
 //     sum_k w_k l_k O_k / sum_k w_k l_k, summed over ranks k in order.
 #include <algorithm>
@@ -42,7 +42,7 @@ constexpr int kPfMaxPages = 8192;    // widest block table the bucketing counts 
 
 // Workspace layout (byte offsets from the caller's workspace).
 struct PfLayout {
-  size_t o, ml, list, items, nitems, total;
+  size_t o, ml, list, items, total;
   int max_items;
 };
 
@@ -58,8 +58,7 @@ static PfLayout pf_layout(const msa_batch* bt, int topk) {
   l.ml = up(l.o + slots * kHpg * kDim * sizeof(_Float16));
   l.list = up(l.ml + slots * kHpg * 2 * sizeof(float));
   l.items = up(l.list + B * kGroups * N * sizeof(int32_t));
-  l.nitems = up(l.items + B * kGroups * max_items * sizeof(int4));
-  l.total = up(l.nitems + B * kGroups * sizeof(int32_t));
+  l.total = up(l.items + B * kGroups * max_items * sizeof(int4));
   l.max_items = (int)max_items;
   return l;
 }
@@ -68,14 +67,17 @@ static PfLayout pf_layout(const msa_batch* bt, int topk) {
 // Entry i of (b, g) is row i / topk, rank i % topk; it counts when the rank is
 // below the row's count and the block id lies in [0, max_pages).  list gets
 // the entries block by block (r * 64 + k; within a block in no fixed order),
-// items the work items {block, first entry, rows}.
+// items the work items {block, first entry, rows, physical page or -1 when the
+// table entry lies outside the pool}, then {0, 0, 0, -1} up to max_items, so
+// that a workgroup of the attention launch reads its item with no count first.
 // Workgroup 0 also writes the empty partial (slot `empty`: output 0, max -inf,
 // denominator 0) that the merge reads for absent ranks.
 __global__ __launch_bounds__(1024) void pf_bucket_kernel(const int32_t* __restrict__ sel,
                                                          const int32_t* __restrict__ cnt, int32_t R,
                                                          int32_t max_pages, int32_t topk, int32_t max_items,
+                                                         const int32_t* __restrict__ table, int32_t num_pages,
                                                          int32_t* __restrict__ list, int4* __restrict__ items,
-                                                         int32_t* __restrict__ n_items, int64_t empty,
+                                                         int64_t empty,
                                                          _Float16* __restrict__ part_o,
                                                          float* __restrict__ part_ml) {
   constexpr int NT = 1024, PER = kPfMaxPages / NT;
@@ -120,17 +122,23 @@ __global__ __launch_bounds__(1024) void pf_bucket_kernel(const int32_t* __restri
   __syncthreads();
   int be = xe - se, bi = xi - si;
   for (int w = 0; w < wave; ++w) be += s_wave[0][w], bi += s_wave[1][w];
-  if (tid == NT - 1) n_items[bg] = bi + si;
+  int total = 0;  // items of (b, g)
+  for (int w = 0; w < NT / 64; ++w) total += s_wave[1][w];
   __syncthreads();  // every count is read: the array becomes the cursors
   int4* it = items + (int64_t)bg * max_items;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int j = tid * PER + e;
-    for (int t = 0; t * kPfRows < c[e]; ++t)
-      it[bi++] = make_int4(j, be + t * kPfRows, min(kPfRows, c[e] - t * kPfRows), 0);
+    if (c[e] > 0) {
+      int ph = table[(int64_t)b * max_pages + j];
+      ph = ph >= 0 && ph < num_pages ? ph : -1;
+      for (int t = 0; t * kPfRows < c[e]; ++t)
+        it[bi++] = make_int4(j, be + t * kPfRows, min(kPfRows, c[e] - t * kPfRows), ph);
+    }
     s_cnt[j] = be;
     be += c[e];
   }
+  for (int i = total + tid; i < max_items; i += NT) it[i] = make_int4(0, 0, 0, -1);
   __syncthreads();
   int32_t* out = list + (int64_t)bg * N;
   for (int i = tid; i < N; i += NT) {
@@ -151,10 +159,9 @@ __device__ __forceinline__ constexpr int pf_tile_token(int m, int i) {
 // FP32 (max of the scaled scores in base 2, or -inf when no token of the block
 // is visible to the row; denominator).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pf_block_attend_kernel(
-    const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int32_t R, int32_t max_pages,
-    const uint8_t* __restrict__ q, float qk2, const uint8_t* __restrict__ kpages, const uint8_t* __restrict__ vpages,
-    int32_t num_pages, int32_t topk, int32_t max_items, const int32_t* __restrict__ list,
-    const int4* __restrict__ items, const int32_t* __restrict__ n_items, _Float16* __restrict__ part_o,
+    const int32_t* __restrict__ lens, int32_t R, int32_t max_pages, const uint8_t* __restrict__ q, float qk2,
+    const uint8_t* __restrict__ kpages, const uint8_t* __restrict__ vpages, int32_t topk, int32_t max_items,
+    const int32_t* __restrict__ list, const int4* __restrict__ items, _Float16* __restrict__ part_o,
     float* __restrict__ part_ml) {
   // operand images: piece (m, s, lane) of K holds token tok(m, lane % 16), dims
   // 32 (lane / 16) + 8s .. + 7; piece (nt, kk, lane) of V holds dim 16 nt + lane % 16,
@@ -162,14 +169,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   __shared__ h8 s_k[8 * 4 * 64];
   __shared__ h8 s_v[8 * 4 * 64];
   const int bg = (int)blockIdx.y, b = bg / kGroups, g = bg % kGroups;
-  if ((int)blockIdx.x >= n_items[bg]) return;
   const int4 item = items[(int64_t)bg * max_items + blockIdx.x];
-  const int j = item.x, first = item.y, rows = item.z;
+  const int j = item.x, first = item.y, rows = item.z, ph = item.w;
+  if (rows == 0) return;  // past the last item of (b, g)
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, a = lane >> 4;
   const int L = clamp_len(lens[b], max_pages);
-  const int ph = table[(int64_t)b * max_pages + j];
-  const bool valid = ph >= 0 && ph < num_pages;  // uniform: a page outside the pool adds nothing
+  const bool valid = ph >= 0;  // uniform: a page outside the pool adds nothing
   const int32_t* ent = list + (int64_t)bg * R * topk + first;
   // this wave's passes: rows 4 quad .. 4 quad + 3 for quad = wave + 4i; the entry
   // (r * 64 + k, or -1) of this lane's query column n of tile qt, row 4 quad + 2 qt + n / 8
@@ -298,14 +304,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           for (int qt = 0; qt < 2; ++qt)
             S[qt][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, Q[qt][s], S[qt][m], 0, 0, 0);
         }
-      // ---- block-local softmax in base 2 (token of S[qt][m][i] = 32a + 8(m/2) + 4(m%2) + i)
+      // ---- block-local softmax in base 2 (token of S[qt][m][i] = 32a + 8(m/2) + 4(m%2) + i):
+      // the max is taken on the raw scores (qk2 > 0 keeps the order), and the scale
+      // and the max's subtraction are one fused multiply-add
       const bool partial = __any(lim[0] < kPage - 1 || lim[1] < kPage - 1) != 0;
       h8 P[2][4];
       float mx[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) S[qt][m] *= qk2;
         if (partial) {
           const int lr = lim[qt] - 32 * a;
 #pragma unroll
@@ -319,13 +325,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int m = 0; m < 8; ++m)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v = fmaxf(v, S[qt][m][i]);
-        mx[qt] = rows_max4(v);
-        const float base = mx[qt] == -__builtin_inff() ? 0.f : mx[qt];
+        mx[qt] = rows_max4(v) * qk2;
+        const float nbase = mx[qt] == -__builtin_inff() ? 0.f : -mx[qt];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           h8 pk;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pk[e] = (_Float16)__builtin_amdgcn_exp2f(S[qt][2 * kk + (e >> 2)][e & 3] - base);
+          for (int e = 0; e < 8; ++e)
+            pk[e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][2 * kk + (e >> 2)][e & 3], qk2, nbase));
           P[qt][kk] = pk;
         }
       }
@@ -372,26 +379,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 }
 
 // ---------------------------------------------------------------- 3. merge
-// One workgroup per (request, row, group); thread t: head t / 32, dims 4 (t % 32) .. + 3.
-// The partials load 16 ranks at a time, all at once (an absent rank reads the
-// empty slot, so no load waits on a condition); each group of 16 then joins the
-// running result (max, weighted denominator and sum), in rank order.
+// One workgroup per two (request, row, group) rows; thread t: row 2 blockIdx + t / 128,
+// head (t % 128) / 16, dims 8 (t % 16) .. + 7 (one 16-byte load per rank).  The
+// partials load 16 ranks at a time, all at once (an absent rank reads the empty
+// slot, so no load waits on a condition); each group of 16 then joins the running
+// result (max, weighted denominator and sum), in rank order.
 __global__ __launch_bounds__(256) void pf_combine_kernel(const int32_t* __restrict__ sel,
-                                                         const int32_t* __restrict__ cnt, int32_t topk,
-                                                         int32_t max_pages, int64_t empty,
+                                                         const int32_t* __restrict__ cnt, int64_t rows,
+                                                         int32_t topk, int32_t max_pages, int64_t empty,
                                                          const _Float16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, float v_scale,
                                                          float* __restrict__ out) {
   constexpr int KC = 16;
-  const int64_t row = blockIdx.x;
-  const int hh = (int)threadIdx.x >> 5, d = 4 * ((int)threadIdx.x & 31);
+  const int64_t row = 2 * (int64_t)blockIdx.x + ((int)threadIdx.x >> 7);
+  if (row >= rows) return;  // (uniform per wave: a wave lies within one row)
+  const int hh = ((int)threadIdx.x >> 4) & 7, d = 8 * ((int)threadIdx.x & 15);
   const int32_t* srow = sel + row * topk;
   const int c = min(cnt[row], topk);
   float M = -__builtin_inff(), den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < c; k0 += KC) {
     float mk[KC], lk[KC];
-    uint2 ok[KC];
+    uint4 ok[KC];
     // lanes 0..15 of each wave load ranks k0 .. k0 + 15 at once; each rank is read from its lane
     const int vl = srow[min(k0 + ((int)threadIdx.x & (KC - 1)), topk - 1)];
 #pragma unroll
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const int32_t* __restri
       const int v = __builtin_amdgcn_readlane(vl, i);
       const int64_t s = ((k < c && v >= 0 && v < max_pages) ? row * topk + k : empty) * kHpg + hh;
       const float2 ml = *reinterpret_cast<const float2*>(part_ml + s * 2);
-      ok[i] = *reinterpret_cast<const uint2*>(part_o + s * kDim + d);
+      ok[i] = *reinterpret_cast<const uint4*>(part_o + s * kDim + d);
       mk[i] = ml.x;
       lk[i] = ml.y;
     }
@@ -409,19 +418,27 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const int32_t* __restri
     for (int i = 0; i < KC; ++i) Mc = fmaxf(Mc, mk[i]);
     // (a group with nothing visible leaves M at -inf and adds weights of 0)
     const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
-    den *= r, acc.x *= r, acc.y *= r, acc.z *= r, acc.w *= r;
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
     M = Mc;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const float wl = mk[i] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mk[i] - M) * lk[i];
-      const h2 lo = __builtin_bit_cast(h2, ok[i].x), hi = __builtin_bit_cast(h2, ok[i].y);
+      const uint32_t w4[4] = {ok[i].x, ok[i].y, ok[i].z, ok[i].w};
       den += wl;
-      acc.x += wl * (float)lo[0], acc.y += wl * (float)lo[1], acc.z += wl * (float)hi[0], acc.w += wl * (float)hi[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const h2 x = __builtin_bit_cast(h2, w4[e]);
+        acc[2 * e] += wl * (float)x[0];
+        acc[2 * e + 1] += wl * (float)x[1];
+      }
     }
   }
   const float inv = den > 0.f ? v_scale / den : 0.f;
-  *reinterpret_cast<float4*>(out + (row * kHpg + hh) * kDim + d) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  float* o = out + (row * kHpg + hh) * kDim + d;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
 }
 
 }  // namespace msa
@@ -443,20 +460,19 @@ extern "C" int msa_launch_prefill_block_attend(const msa_batch* bt, const uint8_
   float* part_ml = (float*)(ws + ly.ml);
   int32_t* list = (int32_t*)(ws + ly.list);
   int4* items = (int4*)(ws + ly.items);
-  int32_t* n_items = (int32_t*)(ws + ly.nitems);
   const int B = bt->num_reqs, R = bt->rows_per_req, P = bt->max_pages_per_req;
   const int64_t empty = (int64_t)B * R * kGroups * topk;  // the slot after the last (request, row, group, rank)
   hipLaunchKernelGGL(pf_bucket_kernel, dim3((unsigned)(B * kGroups)), dim3(1024), 0, s, sel, cnt, R, P, topk,
-                     ly.max_items, list, items, n_items, empty, part_o, part_ml);
+                     ly.max_items, bt->block_table, kc->num_pages, list, items, empty, part_o, part_ml);
   if (hipGetLastError() != hipSuccess) return -1;
   // scores enter the softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   hipLaunchKernelGGL(pf_block_attend_kernel, dim3((unsigned)ly.max_items, (unsigned)(B * kGroups)), dim3(256), 0, s,
-                     bt->block_table, bt->ctx_lens, R, P, q, qk2, (const uint8_t*)kc->pages,
-                     (const uint8_t*)vc->pages, kc->num_pages, topk, ly.max_items, list, items, n_items, part_o,
-                     part_ml);
+                     bt->ctx_lens, R, P, q, qk2, (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, topk,
+                     ly.max_items, list, items, part_o, part_ml);
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((int64_t)B * R * kGroups)), dim3(256), 0, s, sel, cnt, topk,
-                     P, empty, part_o, part_ml, vc->tensor_scale, out);
+  const int64_t rows = (int64_t)B * R * kGroups;
+  hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, s, sel, cnt, rows, topk, P,
+                     empty, part_o, part_ml, vc->tensor_scale, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
