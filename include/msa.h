@@ -287,7 +287,12 @@ int msa_block_maxpool_topk(const msa_batch* batch, const float* scores, int32_t 
  * FP8 caches keep the partials of rows whose selected blocks are spread over
  * 2 or 4 workgroups, which a batch gets when one workgroup per (request,
  * row, group) would leave that many times the CUs idle (at most one float
- * partial of 8 x 130 values per workgroup the device's CUs can hold).
+ * partial of 8 x 130 values per workgroup the device's CUs can hold).  For a
+ * prefill chunk (R > MSA_MAX_ROWS, max_pages_per_req <= 8192) it is the size
+ * of the block-major route's state: one partial per (request, row, group,
+ * rank) -- 8 x 128 FP16 outputs and 8 x 2 floats, 2,112 bytes -- plus the
+ * per-block row lists, about B x R x 4 x topk x 2.2 KB (1.1 GB for 4 chunks
+ * of 2,048 rows at topk 16); with a wider table, 0.
  */
 size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk);
 
@@ -305,7 +310,12 @@ size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk);
  * contents needed).  Two calls that share a workspace must not run
  * concurrently.
  * With NVFP4 or FP8 caches R may be up to MSA_MAX_PREFILL_ROWS (each row of a
- * prefill chunk attends to its own selection).
+ * prefill chunk attends to its own selection).  NVFP4 chunks whose workspace
+ * holds msa_workspace_bytes() (> 0) go block-major: every selected block is
+ * dequantised once for all the rows that chose it, each (row, rank) writes a
+ * partial, and a second launch merges each row's partials in rank order
+ * (bitwise reproducible; the result differs from the one-workgroup-per-row
+ * form that FP8 chunks and smaller workspaces take by rounding only).
  */
 int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
                       const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
@@ -343,8 +353,9 @@ int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_d
  * at least msa_workspace_bytes() bytes, MSA_ERR_WORKSPACE otherwise): with
  * it, a batch that would leave CUs idle spreads each row's selected blocks
  * over several workgroups and merges their partial results in a second
- * launch, and out then equals msa_sparse_decode's bit for bit; without it,
- * one workgroup per row.
+ * launch, and an NVFP4 prefill chunk runs the selection launch and then the
+ * block-major route; out then equals msa_sparse_decode's bit for bit.
+ * Without it, one workgroup per row.
  */
 int msa_select_decode(const msa_batch* batch, const float* block_scores, int32_t topk, const void* q,
                       int32_t q_dtype, float q_scale, float sm_scale, const msa_cache* k_cache,
