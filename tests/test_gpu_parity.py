@@ -180,6 +180,9 @@ CASES = {
                                              spare_pages=77),
     # two rows: new rows on one page, across a page boundary (129: positions 127 and 128), and
     # contexts shorter than the rows
+    "prefill_topk64": lambda: W.make_workload(6, seed=48, lengths=[9000, 3000], R=200, topk=64),
+    "prefill_topk1": lambda: W.make_workload(6, seed=49, lengths=[5000, 140], R=150, topk=1),
+    "prefill_wide_table": lambda: W.make_workload(6, seed=50, lengths=[4000, 2000], R=100, table_width=8300),
     "fp8_spare_pool": lambda: W.make_workload(3, seed=46, B=5, len_div=40, spare_pages=211, cache="fp8"),
     "fp8_spare_pool_r3": lambda: W.make_workload(4, seed=47, lengths=[0, 2, 3, 127, 128, 130, 2051, 4000], R=3,
                                                  spare_pages=97, cache="fp8"),
@@ -687,7 +690,20 @@ def test_prefill_row_route(M, oracle, case):
     _check_full_step(M, oracle, wl, fused=True, workspace=False)
 
 
-@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512"])
+@pytest.mark.parametrize("case", ["prefill_topk64", "prefill_topk1", "prefill_wide_table"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_prefill_more_cases(M, oracle, case, fused):
+    """Prefill chunks at the edges of the block-major route: 64 ranks per row (the merge's
+    groups of 16 ranks four times), one rank per row, and a block table wider than the route
+    counts in LDS (8,300 pages: the workspace size is 0 and the per-row form runs)."""
+    wl = CASES[case]()
+    _print_case(f"{case} fused={fused}", wl)
+    if case == "prefill_wide_table":
+        assert M.msa_workspace_bytes(M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R), wl.topk) == 0
+    _check_full_step(M, oracle, wl, fused=fused)
+
+
+@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512", "prefill_topk64"])
 def test_prefill_hand_selections_both_routes(M, oracle, case):
     """msa_sparse_decode on a prefill chunk with hand-made selections: blocks named twice,
     ranks in no order, counts from 0 to topk, and entries inside the count that name no
