@@ -861,10 +861,10 @@ static int launch_attend(const msa_batch* bt, const uint8_t* q, float q_scale, f
   // scores enter the kernel's softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
   const int km = SELECT ? select_kmax(P) : 8;
-  const size_t block_bytes = FP8 ? 0 : msa_prefill_block_bytes(bt, topk);
+  const size_t block_bytes = msa_prefill_block_bytes(bt, topk);
   if (R > MSA_MAX_ROWS && part && block_bytes > 0 && part_bytes >= block_bytes) {
-    // prefill chunk with room for the block-major partials (NVFP4): the selection
-    // first (when fused), then each selected block once for all the rows that chose it
+    // prefill chunk with room for the block-major partials: the selection first
+    // (when fused), then each selected block once for all the rows that chose it
     if (SELECT && msa_launch_topk(bt, block_scores, 0, topk, sel, cnt, s) != 0) return -1;
     return msa_launch_prefill_block_attend(bt, q, q_scale, sm_scale, kc, vc, sel, cnt, topk, out, part, s);
   }

@@ -158,6 +158,9 @@ __device__ __forceinline__ constexpr int pf_tile_token(int m, int i) {
 // part_o [slot][8 heads][128] FP16 (output / denominator), part_ml [slot][8][2]
 // FP32 (max of the scaled scores in base 2, or -inf when no token of the block
 // is visible to the row; denominator).
+// FP8: FP8 caches (one E4M3 byte per element, exact in FP16; the tensor scales
+// sit in qk2 and in the merge's v_scale), else NVFP4.
+template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pf_block_attend_kernel(
     const int32_t* __restrict__ lens, int32_t R, int32_t max_pages, const uint8_t* __restrict__ q, float qk2,
     const uint8_t* __restrict__ kpages, const uint8_t* __restrict__ vpages, int32_t topk, int32_t max_items,
@@ -232,39 +235,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   {
     // ---- dequantise: wave w writes K M-tiles and V dim tiles 2w, 2w + 1, each
-    // lane the pieces it will read (16 code bytes and their scales per tile)
-    const uint8_t* ks = kpages + ((int64_t)ph * kGroups + g) * kNvSlab;
-    const uint8_t* vs = vpages + ((int64_t)ph * kGroups + g) * kNvSlab;
-    uint4 kc[2], vc[2], vsc[2][2];
-    uint32_t ksc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = pf_tile_token(2 * wave + i, n), d = 16 * (2 * wave + i) + n;
-      kc[i] = *reinterpret_cast<const uint4*>(ks + t * 64 + 16 * a);
-      ksc[i] = *reinterpret_cast<const uint16_t*>(ks + kScaleOff + t * 8 + 2 * a);  // groups 2a, 2a + 1
-      vc[i] = *reinterpret_cast<const uint4*>(vs + d * 64 + 16 * a);
-      // value scales of dim group 2w + i ([group][token]), tokens 32a .. 32a + 31
-      vsc[i][0] = *reinterpret_cast<const uint4*>(vs + kScaleOff + (2 * wave + i) * kPage + 32 * a);
-      vsc[i][1] = *reinterpret_cast<const uint4*>(vs + kScaleOff + (2 * wave + i) * kPage + 32 * a + 16);
-    }
+    // lane the pieces it will read (its 32 elements of one token / dim per tile)
+    constexpr int kSlab = FP8 ? kFp8Slab : kNvSlab;
+    const uint8_t* ks = kpages + ((int64_t)ph * kGroups + g) * kSlab;
+    const uint8_t* vs = vpages + ((int64_t)ph * kGroups + g) * kSlab;
     uint2 qn[2][4];
-    fetch_q(ents[0], qn);
+    if constexpr (FP8) {
+      // keys [token][dim], values [dim][token]: 32 bytes per tile and lane
+      uint4 kc[2][2], vc[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tile = 2 * wave + i;
-      const h2 sk = e4m3x2_to_h2<false>(ksc[i]);
-      const uint32_t kw[4] = {kc[i].x, kc[i].y, kc[i].z, kc[i].w};
-      const uint32_t vw[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
+      for (int i = 0; i < 2; ++i) {
+        const int t = pf_tile_token(2 * wave + i, n), d = 16 * (2 * wave + i) + n;
+        kc[i][0] = *reinterpret_cast<const uint4*>(ks + t * kDim + 32 * a);
+        kc[i][1] = *reinterpret_cast<const uint4*>(ks + t * kDim + 32 * a + 16);
+        vc[i][0] = *reinterpret_cast<const uint4*>(vs + d * kPage + 32 * a);
+        vc[i][1] = *reinterpret_cast<const uint4*>(vs + d * kPage + 32 * a + 16);
+      }
+      fetch_q(ents[0], qn);
+      auto to_h8 = [](uint32_t lo, uint32_t hi) {
+        const h2 x0 = e4m3x2_to_h2<false>(lo), x1 = e4m3x2_to_h2<true>(lo);
+        const h2 x2 = e4m3x2_to_h2<false>(hi), x3 = e4m3x2_to_h2<true>(hi);
+        return h8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+      };
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const _Float16 sc = st < 2 ? sk[0] : sk[1];  // dims 32a + 8st ..: group 2a + st / 2
-        s_k[(tile * 4 + st) * 64 + lane] = e2m1x8_to_h8(kw[st]) * h8{sc, sc, sc, sc, sc, sc, sc, sc};
-        const uint4 sq = vsc[i][st >> 1];  // tokens 32a + 8st .. + 7: bytes 8 (st % 2) .. of word st / 2
-        const uint32_t lo = (st & 1) ? sq.z : sq.x, hi = (st & 1) ? sq.w : sq.y;
-        const h2 s0 = e4m3x2_to_h2<false>(lo), s1 = e4m3x2_to_h2<true>(lo);
-        const h2 s2 = e4m3x2_to_h2<false>(hi), s3 = e4m3x2_to_h2<true>(hi);
-        s_v[(tile * 4 + st) * 64 + lane] =
-            e2m1x8_to_h8(vw[st]) * h8{s0[0], s0[1], s1[0], s1[1], s2[0], s2[1], s3[0], s3[1]};
+      for (int i = 0; i < 2; ++i) {
+        const int tile = 2 * wave + i;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {  // elements 32a + 8st .. + 7: bytes 8 (st % 2) .. of word st / 2
+          const uint4 kq = kc[i][st >> 1], vq = vc[i][st >> 1];
+          s_k[(tile * 4 + st) * 64 + lane] = to_h8((st & 1) ? kq.z : kq.x, (st & 1) ? kq.w : kq.y);
+          s_v[(tile * 4 + st) * 64 + lane] = to_h8((st & 1) ? vq.z : vq.x, (st & 1) ? vq.w : vq.y);
+        }
+      }
+    } else {
+      uint4 kc[2], vc[2], vsc[2][2];
+      uint32_t ksc[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = pf_tile_token(2 * wave + i, n), d = 16 * (2 * wave + i) + n;
+        kc[i] = *reinterpret_cast<const uint4*>(ks + t * 64 + 16 * a);
+        ksc[i] = *reinterpret_cast<const uint16_t*>(ks + kScaleOff + t * 8 + 2 * a);  // groups 2a, 2a + 1
+        vc[i] = *reinterpret_cast<const uint4*>(vs + d * 64 + 16 * a);
+        // value scales of dim group 2w + i ([group][token]), tokens 32a .. 32a + 31
+        vsc[i][0] = *reinterpret_cast<const uint4*>(vs + kScaleOff + (2 * wave + i) * kPage + 32 * a);
+        vsc[i][1] = *reinterpret_cast<const uint4*>(vs + kScaleOff + (2 * wave + i) * kPage + 32 * a + 16);
+      }
+      fetch_q(ents[0], qn);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int tile = 2 * wave + i;
+        const h2 sk = e4m3x2_to_h2<false>(ksc[i]);
+        const uint32_t kw[4] = {kc[i].x, kc[i].y, kc[i].z, kc[i].w};
+        const uint32_t vw[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const _Float16 sc = st < 2 ? sk[0] : sk[1];  // dims 32a + 8st ..: group 2a + st / 2
+          s_k[(tile * 4 + st) * 64 + lane] = e2m1x8_to_h8(kw[st]) * h8{sc, sc, sc, sc, sc, sc, sc, sc};
+          const uint4 sq = vsc[i][st >> 1];  // tokens 32a + 8st .. + 7: bytes 8 (st % 2) .. of word st / 2
+          const uint32_t lo = (st & 1) ? sq.z : sq.x, hi = (st & 1) ? sq.w : sq.y;
+          const h2 s0 = e4m3x2_to_h2<false>(lo), s1 = e4m3x2_to_h2<true>(lo);
+          const h2 s2 = e4m3x2_to_h2<false>(hi), s3 = e4m3x2_to_h2<true>(hi);
+          s_v[(tile * 4 + st) * 64 + lane] =
+              e2m1x8_to_h8(vw[st]) * h8{s0[0], s0[1], s1[0], s1[1], s2[0], s2[1], s3[0], s3[1]};
+        }
       }
     }
     // the first pass's queries: converted before the barrier, so that their loads
@@ -467,9 +500,15 @@ extern "C" int msa_launch_prefill_block_attend(const msa_batch* bt, const uint8_
   if (hipGetLastError() != hipSuccess) return -1;
   // scores enter the softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(pf_block_attend_kernel, dim3((unsigned)ly.max_items, (unsigned)(B * kGroups)), dim3(256), 0, s,
-                     bt->ctx_lens, R, P, q, qk2, (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, topk,
-                     ly.max_items, list, items, part_o, part_ml);
+  const dim3 grid((unsigned)ly.max_items, (unsigned)(B * kGroups));
+  if (kc->dtype == MSA_FP8_E4M3)
+    hipLaunchKernelGGL(pf_block_attend_kernel<true>, grid, dim3(256), 0, s, bt->ctx_lens, R, P, q, qk2,
+                       (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, topk, ly.max_items, list, items, part_o,
+                       part_ml);
+  else
+    hipLaunchKernelGGL(pf_block_attend_kernel<false>, grid, dim3(256), 0, s, bt->ctx_lens, R, P, q, qk2,
+                       (const uint8_t*)kc->pages, (const uint8_t*)vc->pages, topk, ly.max_items, list, items, part_o,
+                       part_ml);
   if (hipGetLastError() != hipSuccess) return -1;
   const int64_t rows = (int64_t)B * R * kGroups;
   hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, s, sel, cnt, rows, topk, P,

@@ -310,12 +310,12 @@ size_t msa_workspace_bytes(const msa_batch* batch, int32_t topk);
  * contents needed).  Two calls that share a workspace must not run
  * concurrently.
  * With NVFP4 or FP8 caches R may be up to MSA_MAX_PREFILL_ROWS (each row of a
- * prefill chunk attends to its own selection).  NVFP4 chunks whose workspace
- * holds msa_workspace_bytes() (> 0) go block-major: every selected block is
+ * prefill chunk attends to its own selection).  Chunks whose workspace holds
+ * msa_workspace_bytes() (> 0) go block-major: every selected block is
  * dequantised once for all the rows that chose it, each (row, rank) writes a
  * partial, and a second launch merges each row's partials in rank order
  * (bitwise reproducible; the result differs from the one-workgroup-per-row
- * form that FP8 chunks and smaller workspaces take by rounding only).
+ * form that smaller workspaces take by rounding only).
  */
 int msa_sparse_decode(const msa_batch* batch, const void* q, int32_t q_dtype, float q_scale, float sm_scale,
                       const msa_cache* k_cache, const msa_cache* v_cache, const int32_t* sel_blocks,
@@ -353,7 +353,7 @@ int msa_sparse_decode_noalloc(const msa_batch* batch, const void* q, int32_t q_d
  * at least msa_workspace_bytes() bytes, MSA_ERR_WORKSPACE otherwise): with
  * it, a batch that would leave CUs idle spreads each row's selected blocks
  * over several workgroups and merges their partial results in a second
- * launch, and an NVFP4 prefill chunk runs the selection launch and then the
+ * launch, and a prefill chunk runs the selection launch and then the
  * block-major route; out then equals msa_sparse_decode's bit for bit.
  * Without it, one workgroup per row.
  */

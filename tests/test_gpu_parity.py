@@ -703,7 +703,7 @@ def test_prefill_more_cases(M, oracle, case, fused):
     _check_full_step(M, oracle, wl, fused=fused)
 
 
-@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512", "prefill_topk64"])
+@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512", "prefill_topk64", "fp8_prefill"])
 def test_prefill_hand_selections_both_routes(M, oracle, case):
     """msa_sparse_decode on a prefill chunk with hand-made selections: blocks named twice,
     ranks in no order, counts from 0 to topk, and entries inside the count that name no
