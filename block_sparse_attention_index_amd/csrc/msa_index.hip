@@ -23,11 +23,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 
 // The scan in physical page order, for a batch that carries page_owner (the
 // block table's inverse: entry p = b * max_pages + j where table[b][j] == p).
-// Workgroup b < B belongs to request b: it writes the request's new rows
-// (INSERT), scores the one or two pages that hold rows L_b - R .. L_b - 1
-// through the block table, records those pages in page_owner and writes the
-// -inf scores of the blocks past the context.  Workgroup B + i takes pool
-// pages 4i .. 4i+3, one per wave.  A wave reads its page's owner entry and
+// Workgroup b < B belongs to request b: it writes the index keys of the
+// request's new rows (INSERT), scores the one or two pages that hold rows
+// L_b - R .. L_b - 1 through the block table, records those pages in
+// page_owner and writes the -inf scores of the blocks past the context.  With
+// INSERT, workgroup B + b writes request b's new keys and values (nothing in
+// this launch reads them, so they stay off the index keys' path to the
+// scoring).  The next workgroups, from B (2B with INSERT) on, take pool pages
+// 4i .. 4i+3, one per wave.  A wave reads its page's owner entry and
 // issues the page's loads before anything else; the page counts only if the
 // entry names a block of some request that lies before that request's
 // new-row pages and whose table entry names the page back (free pages and
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int L = clamp_len(lens[b], max_pages);
     const int t0 = max(L - R, 0);
     if (INSERT && t0 < L) {
-      insert_new_rows<R>(table, max_pages, num_pages, b, L, t0, L, NR);
+      insert_new_rows<R, kInsertIndex>(table, max_pages, num_pages, b, L, t0, L, NR);
       // the index keys just written are read back by this workgroup's waves
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
@@ -73,7 +76,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     fill_past_chunks<R>(block_scores, b, npb, max_pages);
     return;
   }
-  const int p = ((int)blockIdx.x - B) * 4 + wave;
+  if (INSERT && (int)blockIdx.x < 2 * B) {  // request b's new keys and values
+    const int b = (int)blockIdx.x - B;
+    const int L = clamp_len(lens[b], max_pages);
+    if (max(L - R, 0) < L) insert_new_rows<R, kInsertKV>(table, max_pages, num_pages, b, L, max(L - R, 0), L, NR);
+    return;
+  }
+  const int p = ((int)blockIdx.x - (INSERT ? 2 * B : B)) * 4 + wave;
   if (p >= num_pages) return;
   const int own = owner[p];
   PageRegs pr;
@@ -489,7 +498,9 @@ static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale,
 template <int R, bool INSERT>
 static void launch_owned(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                          const NewRows& nr, hipStream_t s) {
-  const dim3 grid((unsigned)(bt->num_reqs + (ic->num_pages + 3) / 4));
+  // request workgroups, their key / value writers (NVFP4 with INSERT), then the pool's pages
+  const int kv = INSERT && ic->dtype == MSA_NVFP4 ? bt->num_reqs : 0;
+  const dim3 grid((unsigned)(bt->num_reqs + kv + (ic->num_pages + 3) / 4));
   if (ic->dtype == MSA_FP8_E4M3)
     hipLaunchKernelGGL((index_fp8_owned_kernel<R, INSERT>), grid, dim3(256), 0, s, bt->block_table, bt->ctx_lens,
                        bt->max_pages_per_req, bt->page_owner, q, out_scale, (const uint8_t*)ic->pages, ic->num_pages,

@@ -274,15 +274,21 @@ struct NewRows {
 // threads (one 16-lane row per 16-element group, as the insert kernel does).
 // The caller makes them visible to its waves (workgroup release, barrier,
 // acquire) before reading the pages.
-template <int R>
+// Which caches insert_new_rows writes: all three, the index keys only, or the
+// keys and values only.
+enum InsertPart { kInsertAll = 0, kInsertIndex = 1, kInsertKV = 2 };
+
+template <int R, int PART = kInsertAll>
 __device__ __forceinline__ void insert_new_rows(const int32_t* __restrict__ table, int32_t max_pages, int32_t num_pages,
                                                 int b, int L, int t0, int t1, const NewRows& NR) {
+  // 16-dim groups per token: 32 keys, 32 values, 8 index keys (or a part of them)
+  constexpr int G = PART == kInsertIndex ? 8 : (PART == kInsertKV ? 64 : 72);
   const int i = threadIdx.x & 15;
-  const int nrow = (t1 - t0) * 72;  // 16-dim groups: 32 keys, 32 values, 8 index keys per token
-  // row rr: token t0 + rr / 72, then 32 key, 32 value and 8 index-key groups
+  const int nrow = (t1 - t0) * G;
+  // row rr: token t0 + rr / G, then its key, value and index-key groups
   auto locate = [&](int rr, int& tok, int& c, int& head, int& grp) {
-    tok = t0 + rr / 72;
-    int u = rr % 72;
+    tok = t0 + rr / G;
+    int u = rr % G + (PART == kInsertIndex ? 64 : 0);
     c = u < 32 ? 0 : (u < 64 ? 1 : 2);
     u -= 32 * c;
     head = u >> 3;
@@ -293,7 +299,7 @@ __device__ __forceinline__ void insert_new_rows(const int32_t* __restrict__ tabl
   // memory round -- sized for all of a chunk's rows (one round) up to four
   // new rows, two rounds beyond.  The new tokens lie on at most two pages
   // (R <= 128), whose table entries load with the sources.
-  constexpr int kBatch = (72 * R + 15) / 16 < 18 ? (72 * R + 15) / 16 : 18;
+  constexpr int kBatch = (G * R + 15) / 16 < 18 ? (G * R + 15) / 16 : 18;
   const int pa = t0 / kPage;
   const int ph_a = table[(int64_t)b * max_pages + pa], ph_b = table[(int64_t)b * max_pages + (t1 - 1) / kPage];
   for (int rb = threadIdx.x >> 4; rb < nrow; rb += 16 * kBatch) {
