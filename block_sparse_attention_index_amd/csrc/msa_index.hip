@@ -141,10 +141,11 @@ __global__ __launch_bounds__(256) void page_owner_scatter_kernel(const int32_t* 
 // L)) written into the three FP8 caches by a whole workgroup of 256 threads,
 // one thread per element (4 x 128 keys, 4 x 128 values, 128 index keys per
 // token).  The caller makes them visible to its waves before reading pages.
-template <int R>
+template <int R, int PART = kInsertAll>
 __device__ __forceinline__ void fp8_insert_rows(const int32_t* __restrict__ table, int32_t max_pages, int32_t num_pages,
                                                 int b, int L, int t0, int t1, NewRows NR) {
-  constexpr int kPerTok = 9 * kDim;
+  // elements per token: 4 x 128 keys, 4 x 128 values, 128 index keys (or a part of them)
+  constexpr int kPerTok = PART == kInsertIndex ? kDim : (PART == kInsertKV ? 8 * kDim : 9 * kDim);
   // element e: token t0 + e / kPerTok, then its keys, values, index key.
   // A batch of elements per thread: every source load issues before the
   // first store (which could alias them), so a batch is one memory round
@@ -156,7 +157,7 @@ __device__ __forceinline__ void fp8_insert_rows(const int32_t* __restrict__ tabl
   const int ph_a = table[(int64_t)b * max_pages + pa], ph_b = table[(int64_t)b * max_pages + (t1 - 1) / kPage];
   auto locate = [&](int e, int& tok, int& c, int& head, int& d) {
     tok = t0 + e / kPerTok;
-    int u = e % kPerTok;
+    int u = e % kPerTok + (PART == kInsertIndex ? 8 * kDim : 0);
     c = u < 4 * kDim ? 0 : (u < 8 * kDim ? 1 : 2);
     u -= c * 4 * kDim;
     head = u / kDim;
@@ -324,11 +325,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 }
 
 // The FP8 scan in physical page order (batches with page_owner), split as in
-// index_nvfp4_owned_kernel: workgroup b < B writes request b's new rows
-// (INSERT), scores the one or two pages that hold rows L_b - R .. L_b - 1
-// through the block table, records them in page_owner and writes the -inf
-// scores past the context; workgroup B + i takes pool pages 4i .. 4i+3, one
-// per wave, loading the page before its owner's length, table entry and
+// index_nvfp4_owned_kernel: workgroup b < B writes the index keys of request
+// b's new rows (INSERT), scores the one or two pages that hold rows L_b - R ..
+// L_b - 1 through the block table, records them in page_owner and writes the
+// -inf scores past the context; with INSERT, workgroup B + b writes the new
+// keys and values; the next workgroups take pool pages 4i .. 4i+3, one per
+// wave, loading the page before its owner's length, table entry and
 // queries.  A page that counts holds only blocks below the page of the first
 // new row, whose tokens every row sees, so that path applies no position mask.
 template <int R, bool INSERT>
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int L = clamp_len(lens[b], max_pages);
     const int t0 = max(L - R, 0);
     if (INSERT && t0 < L) {
-      fp8_insert_rows<R>(table, max_pages, num_pages, b, L, t0, L, NR);
+      fp8_insert_rows<R, kInsertIndex>(table, max_pages, num_pages, b, L, t0, L, NR);
       // the index keys just written are read back by this workgroup's waves
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
@@ -374,7 +376,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     fill_past_chunks<R>(block_scores, b, npb, max_pages);
     return;
   }
-  const int p = ((int)blockIdx.x - B) * 4 + wave;
+  if (INSERT && (int)blockIdx.x < 2 * B) {  // request b's new keys and values
+    const int b = (int)blockIdx.x - B;
+    const int L = clamp_len(lens[b], max_pages);
+    if (max(L - R, 0) < L) fp8_insert_rows<R, kInsertKV>(table, max_pages, num_pages, b, L, max(L - R, 0), L, NR);
+    return;
+  }
+  const int p = ((int)blockIdx.x - (INSERT ? 2 * B : B)) * 4 + wave;
   if (p >= num_pages) return;
   const int own = owner[p];
   uint4 kw[8][2];
@@ -498,8 +506,8 @@ static void launch_nvfp4(const msa_batch* bt, const uint8_t* q, float out_scale,
 template <int R, bool INSERT>
 static void launch_owned(const msa_batch* bt, const uint8_t* q, float out_scale, const msa_cache* ic, float* bs,
                          const NewRows& nr, hipStream_t s) {
-  // request workgroups, their key / value writers (NVFP4 with INSERT), then the pool's pages
-  const int kv = INSERT && ic->dtype == MSA_NVFP4 ? bt->num_reqs : 0;
+  // request workgroups, their key / value writers (with INSERT), then the pool's pages
+  const int kv = INSERT ? bt->num_reqs : 0;
   const dim3 grid((unsigned)(bt->num_reqs + kv + (ic->num_pages + 3) / 4));
   if (ic->dtype == MSA_FP8_E4M3)
     hipLaunchKernelGGL((index_fp8_owned_kernel<R, INSERT>), grid, dim3(256), 0, s, bt->block_table, bt->ctx_lens,
