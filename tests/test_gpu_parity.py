@@ -917,7 +917,7 @@ def _random_case(seed):
     return wl, owner, new_rows
 
 
-@pytest.mark.parametrize("seed", list(range(500, 548)))
+@pytest.mark.parametrize("seed", list(range(500, 572)))
 def test_random_small_batches(M, oracle, seed):
     """Seeded random small batches through the whole step (fused launches), against the oracle."""
     wl, owner, new_rows = _random_case(seed)
@@ -925,7 +925,7 @@ def test_random_small_batches(M, oracle, seed):
     _check_full_step(M, oracle, wl, new_rows=new_rows, owner=owner)
 
 
-@pytest.mark.parametrize("seed", list(range(600, 608)))
+@pytest.mark.parametrize("seed", list(range(600, 612)))
 def test_random_prefill_chunks(M, oracle, seed):
     """Seeded random prompt chunks (9 to 300 causal rows per request, 1 to 3 requests) through the
     dense indexer, the selection and the prefill attention, against the oracle."""
