@@ -188,7 +188,23 @@ CASES = {
                                                  spare_pages=97, cache="fp8"),
     "ragged_r2": lambda: W.make_workload(4, seed=45, lengths=[0, 1, 2, 128, 129, 130, 2049, 5000], R=2,
                                          spare_pages=19),
+    # more workgroup rows than half the 256 CUs, at most all of them: one workgroup per row, whose
+    # waves take two blocks each; 144-256 rows, with 8, 48 and from-memory candidate counts per
+    # lane, and FP8 caches
+    "cus_b48": lambda: W.make_workload(3, seed=51, B=48, len_div=48),
+    "cus_r4": lambda: W.make_workload(4, seed=52, B=16, len_div=32, R=4),
+    "cus_ragged": lambda: W.make_workload(3, seed=53, lengths=[1, 127, 128, 129, 2047, 2048, 2049, 5000] * 5, R=1),
+    "cus_wide": lambda: W.make_workload(3, seed=54, B=36, len_div=32, table_width=1600),
+    "cus_wide_mem": lambda: W.make_workload(3, seed=55, B=36, len_div=32, table_width=3100),
+    "fp8_cus": lambda: W.make_workload(3, seed=56, B=40, len_div=48, cache="fp8"),
+    "fp8_cus_wide": lambda: W.make_workload(3, seed=57, B=36, len_div=32, table_width=1600, cache="fp8"),
+    # the same batch shape with 32 blocks per row (four per wave) and with 8
+    "cus_topk32": lambda: W.make_workload(3, seed=58, B=48, len_div=24, topk=32),
+    "cus_topk8": lambda: W.make_workload(3, seed=59, B=48, len_div=48, topk=8),
 }
+
+CUS_CASES = ["cus_b48", "cus_r4", "cus_ragged", "cus_wide", "cus_wide_mem", "fp8_cus", "fp8_cus_wide",
+             "cus_topk32", "cus_topk8"]
 
 
 # ---------------------------------------------------------------- step 0 / codecs
@@ -484,7 +500,7 @@ def _out_err(got, ref):
 @pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small",
                                   "ragged", "ragged_r4", "r3", "r8", "fp8_cfg3_small", "fp8_ragged_r4", "fp8_r8",
                                   "prefill_ragged", "fp8_prefill", "r5", "r7", "fp8_r6", "union_r3", "topk8",
-                                  "topk32", "topk32_r4", "fp8_topk8", "wide_table"])
+                                  "topk32", "topk32_r4", "fp8_topk8", "wide_table"] + CUS_CASES)
 def test_sparse_decode_on_oracle_selection(M, oracle, case):
     wl = CASES[case]()
     _print_case(case, wl)
@@ -585,7 +601,8 @@ def _sampled_caches(oracle, wl, rows):
                                   "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
                                   "union_r4", "union_r2", "fp8_prefill", "fp8_prefill_r512", "r5", "r6", "r7",
                                   "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "union_r7", "topk8", "topk32",
-                                  "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"])
+                                  "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"]
+                         + CUS_CASES)
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
@@ -596,7 +613,8 @@ def test_full_step(M, oracle, case, fused):
 
 @pytest.mark.parametrize("case", ["cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged", "ragged_r4", "r8",
                                   "prefix_wide", "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "r5",
-                                  "r6", "r7", "fp8_r5", "fp8_r7", "union_r3", "topk32", "prefix_fused_b32"])
+                                  "r6", "r7", "fp8_r5", "fp8_r7", "union_r3", "topk32", "prefix_fused_b32",
+                                  "cus_r4", "cus_ragged", "fp8_cus"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_full_step_with_new_rows(M, oracle, case, fused):
     """The step inserts each request's R new rows itself (fused: insert + index in one
@@ -630,7 +648,7 @@ def test_insert_index_equals_separate_calls(M, oracle, case):
 
 @pytest.mark.parametrize("case", ["cfg3_small", "cfg4_small", "ragged_r4", "r8", "union_r4", "union_r2", "r5", "r6",
                                   "r7", "fp8_r6", "union_r3", "union_r7", "topk8", "topk32", "topk32_r4",
-                                  "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"])
+                                  "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"] + CUS_CASES)
 def test_select_decode_equals_separate_calls(M, oracle, case):
     """msa_select_decode: same selection as msa_block_maxpool_topk and bitwise the same
     output as msa_sparse_decode on that selection."""
