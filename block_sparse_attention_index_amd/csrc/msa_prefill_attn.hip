@@ -48,7 +48,7 @@ struct PfLayout {
 
 static PfLayout pf_layout(const msa_batch* bt, int topk) {
   const size_t B = (size_t)bt->num_reqs, R = (size_t)bt->rows_per_req, P = (size_t)bt->max_pages_per_req;
-  const size_t slots = B * R * kGroups * (size_t)topk + 1;  // + the empty slot absent ranks read
+  const size_t slots = B * R * kGroups * (size_t)topk;
   const size_t N = R * (size_t)topk;  // entries of one (request, group)
   // sum over blocks of ceil(count / kPfRows) <= N / kPfRows + (blocks with a count)
   const size_t max_items = std::min(P, N) + (N + kPfRows - 1) / kPfRows;
@@ -70,38 +70,40 @@ static PfLayout pf_layout(const msa_batch* bt, int topk) {
 // items the work items {block, first entry, rows, physical page or -1 when the
 // table entry lies outside the pool}, then {0, 0, 0, -1} up to max_items, so
 // that a workgroup of the attention launch reads its item with no count first.
-// Workgroup 0 also writes the empty partial (slot `empty`: output 0, max -inf,
-// denominator 0) that the merge reads for absent ranks.
+// The entries are read kEB per thread at a time, every load of a batch before
+// its first LDS atomic, so that a batch is one memory round.
 __global__ __launch_bounds__(1024) void pf_bucket_kernel(const int32_t* __restrict__ sel,
                                                          const int32_t* __restrict__ cnt, int32_t R,
                                                          int32_t max_pages, int32_t topk, int32_t max_items,
                                                          const int32_t* __restrict__ table, int32_t num_pages,
-                                                         int32_t* __restrict__ list, int4* __restrict__ items,
-                                                         int64_t empty,
-                                                         _Float16* __restrict__ part_o,
-                                                         float* __restrict__ part_ml) {
-  constexpr int NT = 1024, PER = kPfMaxPages / NT;
-  static_assert(NT == kHpg * kDim, "one thread per element of the empty partial");
+                                                         int32_t* __restrict__ list, int4* __restrict__ items) {
+  constexpr int NT = 1024, PER = kPfMaxPages / NT, kEB = 16;
   __shared__ int s_cnt[kPfMaxPages];  // counts, then each block's next free entry
   __shared__ int s_wave[2][NT / 64];
   const int bg = (int)blockIdx.x, b = bg / kGroups, g = bg % kGroups;
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (bg == 0) {
-    part_o[empty * kHpg * kDim + tid] = (_Float16)0.f;
-    if (tid < 2 * kHpg) part_ml[empty * kHpg * 2 + tid] = (tid & 1) ? 0.f : -__builtin_inff();
-  }
   const int N = R * topk;
   for (int j = tid; j < kPfMaxPages; j += NT) s_cnt[j] = 0;
-  __syncthreads();
-  auto entry = [&](int i, int& v) {
-    const int r = i / topk, k = i % topk;
-    const int64_t row = ((int64_t)b * R + r) * kGroups + g;
-    v = sel[row * topk + k];
-    return k < cnt[row] && v >= 0 && v < max_pages;
+  // entries i0 + e NT + tid, e < kEB: their block ids, and whether each counts
+  auto load_batch = [&](int i0, int (&v)[kEB], bool (&ok)[kEB]) {
+#pragma unroll
+    for (int e = 0; e < kEB; ++e) {
+      const int i = i0 + e * NT + tid, ic = min(i, N - 1);
+      const int r = ic / topk, k = ic % topk;
+      const int64_t row = ((int64_t)b * R + r) * kGroups + g;
+      const int c = cnt[row];
+      v[e] = sel[row * topk + k];
+      ok[e] = i < N && k < c && v[e] >= 0 && v[e] < max_pages;
+    }
   };
-  for (int i = tid; i < N; i += NT) {
-    int v;
-    if (entry(i, v)) atomicAdd(&s_cnt[v], 1);
+  __syncthreads();
+  for (int i0 = 0; i0 < N; i0 += kEB * NT) {
+    int v[kEB];
+    bool ok[kEB];
+    load_batch(i0, v, ok);
+#pragma unroll
+    for (int e = 0; e < kEB; ++e)
+      if (ok[e]) atomicAdd(&s_cnt[v[e]], 1);
   }
   __syncthreads();
   // exclusive scans over the blocks of entries and of items: PER blocks per thread
@@ -126,12 +128,16 @@ __global__ __launch_bounds__(1024) void pf_bucket_kernel(const int32_t* __restri
   for (int w = 0; w < NT / 64; ++w) total += s_wave[1][w];
   __syncthreads();  // every count is read: the array becomes the cursors
   int4* it = items + (int64_t)bg * max_items;
+  // the table entries of this thread's blocks, loaded together (a clamped
+  // index for blocks past the table: only blocks with a count use them)
+  int phv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) phv[e] = table[(int64_t)b * max_pages + min(tid * PER + e, max_pages - 1)];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int j = tid * PER + e;
     if (c[e] > 0) {
-      int ph = table[(int64_t)b * max_pages + j];
-      ph = ph >= 0 && ph < num_pages ? ph : -1;
+      const int ph = phv[e] >= 0 && phv[e] < num_pages ? phv[e] : -1;
       for (int t = 0; t * kPfRows < c[e]; ++t)
         it[bi++] = make_int4(j, be + t * kPfRows, min(kPfRows, c[e] - t * kPfRows), ph);
     }
@@ -141,9 +147,15 @@ __global__ __launch_bounds__(1024) void pf_bucket_kernel(const int32_t* __restri
   for (int i = total + tid; i < max_items; i += NT) it[i] = make_int4(0, 0, 0, -1);
   __syncthreads();
   int32_t* out = list + (int64_t)bg * N;
-  for (int i = tid; i < N; i += NT) {
-    int v;
-    if (entry(i, v)) out[atomicAdd(&s_cnt[v], 1)] = (i / topk) * 64 + i % topk;
+  for (int i0 = 0; i0 < N; i0 += kEB * NT) {
+    int v[kEB];
+    bool ok[kEB];
+    load_batch(i0, v, ok);
+#pragma unroll
+    for (int e = 0; e < kEB; ++e) {
+      const int i = i0 + e * NT + tid;
+      if (ok[e]) out[atomicAdd(&s_cnt[v[e]], 1)] = (i / topk) * 64 + i % topk;
+    }
   }
 }
 
@@ -414,12 +426,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // ---------------------------------------------------------------- 3. merge
 // One workgroup per two (request, row, group) rows; thread t: row 2 blockIdx + t / 128,
 // head (t % 128) / 16, dims 8 (t % 16) .. + 7 (one 16-byte load per rank).  The
-// partials load 16 ranks at a time, all at once (an absent rank reads the empty
-// slot, so no load waits on a condition); each group of 16 then joins the running
-// result (max, weighted denominator and sum), in rank order.
+// partials load 16 ranks at a time, all at once: the slots of ranks 0..15 load
+// together with the row's count and selection, so no load waits on another, and
+// an absent rank's values (its slot was not written) are replaced by an empty
+// partial (max -inf, denominator 0, output 0) before use; later groups of 16 load
+// only while the count reaches them.  Each group then joins the running result
+// (max, weighted denominator and sum), in rank order.
 __global__ __launch_bounds__(256) void pf_combine_kernel(const int32_t* __restrict__ sel,
                                                          const int32_t* __restrict__ cnt, int64_t rows,
-                                                         int32_t topk, int32_t max_pages, int64_t empty,
+                                                         int32_t topk, int32_t max_pages,
                                                          const _Float16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, float v_scale,
                                                          float* __restrict__ out) {
@@ -428,23 +443,33 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const int32_t* __restri
   if (row >= rows) return;  // (uniform per wave: a wave lies within one row)
   const int hh = ((int)threadIdx.x >> 4) & 7, d = 8 * ((int)threadIdx.x & 15);
   const int32_t* srow = sel + row * topk;
-  const int c = min(cnt[row], topk);
+  const int c = cnt[row];
   float M = -__builtin_inff(), den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < c; k0 += KC) {
+  for (int k0 = 0; k0 < topk; k0 += KC) {
+    if (k0 > 0 && k0 >= c) break;
     float mk[KC], lk[KC];
     uint4 ok[KC];
     // lanes 0..15 of each wave load ranks k0 .. k0 + 15 at once; each rank is read from its lane
     const int vl = srow[min(k0 + ((int)threadIdx.x & (KC - 1)), topk - 1)];
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-      const int k = k0 + i;
-      const int v = __builtin_amdgcn_readlane(vl, i);
-      const int64_t s = ((k < c && v >= 0 && v < max_pages) ? row * topk + k : empty) * kHpg + hh;
+      const int64_t s = (row * topk + min(k0 + i, topk - 1)) * kHpg + hh;
       const float2 ml = *reinterpret_cast<const float2*>(part_ml + s * 2);
       ok[i] = *reinterpret_cast<const uint4*>(part_o + s * kDim + d);
       mk[i] = ml.x;
       lk[i] = ml.y;
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int k = k0 + i;
+      const int v = __builtin_amdgcn_readlane(vl, i);
+      const bool present = k < topk && k < c && v >= 0 && v < max_pages;
+      mk[i] = present ? mk[i] : -__builtin_inff();
+      lk[i] = present ? lk[i] : 0.f;
+      // a mask rather than a select, so that no load is moved under a branch
+      const uint32_t keep = present ? ~0u : 0u;
+      ok[i].x &= keep, ok[i].y &= keep, ok[i].z &= keep, ok[i].w &= keep;
     }
     float Mc = M;
 #pragma unroll
@@ -494,9 +519,8 @@ extern "C" int msa_launch_prefill_block_attend(const msa_batch* bt, const uint8_
   int32_t* list = (int32_t*)(ws + ly.list);
   int4* items = (int4*)(ws + ly.items);
   const int B = bt->num_reqs, R = bt->rows_per_req, P = bt->max_pages_per_req;
-  const int64_t empty = (int64_t)B * R * kGroups * topk;  // the slot after the last (request, row, group, rank)
   hipLaunchKernelGGL(pf_bucket_kernel, dim3((unsigned)(B * kGroups)), dim3(1024), 0, s, sel, cnt, R, P, topk,
-                     ly.max_items, bt->block_table, kc->num_pages, list, items, empty, part_o, part_ml);
+                     ly.max_items, bt->block_table, kc->num_pages, list, items);
   if (hipGetLastError() != hipSuccess) return -1;
   // scores enter the softmax in base 2
   const float qk2 = sm_scale * kc->tensor_scale * q_scale * 1.4426950408889634f;
@@ -512,6 +536,6 @@ extern "C" int msa_launch_prefill_block_attend(const msa_batch* bt, const uint8_
   if (hipGetLastError() != hipSuccess) return -1;
   const int64_t rows = (int64_t)B * R * kGroups;
   hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, s, sel, cnt, rows, topk, P,
-                     empty, part_o, part_ml, vc->tensor_scale, out);
+                     part_o, part_ml, vc->tensor_scale, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
