@@ -543,9 +543,13 @@ def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False, own
     ci, ck, cv = oracle_caches(oracle, wl) if sample is None else _sampled_caches(oracle, wl, rows)
     _, _, qi, qd = oracle_queries(oracle, wl)
     bt = oracle.OracleBatch(wl.block_table[rows], wl.lengths[rows], wl.R)
-    res = oracle.decode_step(bt, qi[rows], qd[rows], wl.sm_scale, ci, ck, cv, wl.topk)
-    # block scores (max-pooled) against the oracle's, with the derived bound
+    # the oracle's steps 1-4 in order (its decode_step), the index scores taken once with their
+    # sums of |terms| for the score bound
     ts, ab = oracle.index_scores(bt, qi[rows], ci, with_abs=True)
+    res = {"block_scores": oracle.block_maxpool(bt, ts)}
+    res["sel"], res["cnt"] = oracle.select(bt, res["block_scores"], wl.topk)
+    res["out"] = oracle.attention(bt, qd[rows], wl.sm_scale, ck, cv, res["sel"], res["cnt"])
+    # block scores (max-pooled) against the oracle's, with the derived bound
     absmax = ab.reshape(ab.shape[:3] + (wl.max_pages, 128)).max(-1)
     fin = np.isfinite(res["block_scores"])
     assert np.array_equal(np.isfinite(g_bs[rows]), fin)
@@ -564,13 +568,15 @@ def _check_full_step(M, oracle, wl, sample=None, fused=True, new_rows=False, own
           f"{mism} invalid", flush=True)
     assert mism == 0
     # outputs: against oracle attention on the GPU's (validated) selection, and on the oracle's where equal
-    ref_own = oracle.attention(bt, qd[rows], wl.sm_scale, ck, cv, g_sel[rows], g_cnt[rows])
-    err = _out_err(g_out[rows], ref_own)
-    print(f"  max per-vector relative error {err.max():.3e}", flush=True)
-    assert err.max() <= OUT_TOL
     same = np.array([[[set(g_sel[b, r, g, :g_cnt[b, r, g]]) == set(res["sel"][i, r, g, :res["cnt"][i, r, g]])
                        for g in range(4)] for r in range(wl.R)] for i, b in enumerate(rows)])
     same_h = np.repeat(same, 8, axis=2)
+    # (where every set is the oracle's, the oracle's output on its own selection is that reference)
+    ref_own = res["out"] if same.all() else oracle.attention(bt, qd[rows], wl.sm_scale, ck, cv, g_sel[rows],
+                                                               g_cnt[rows])
+    err = _out_err(g_out[rows], ref_own)
+    print(f"  max per-vector relative error {err.max():.3e}", flush=True)
+    assert err.max() <= OUT_TOL
     err2 = _out_err(g_out[rows], res["out"])
     assert err2[same_h].max(initial=0.0) <= OUT_TOL
     return dec
@@ -596,14 +602,18 @@ def _sampled_caches(oracle, wl, rows):
     return ci, ck, cv
 
 
-@pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged",
-                                  "ragged_r4", "r3", "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small",
-                                  "fp8_ragged", "fp8_ragged_r4", "fp8_r8", "prefill_r512", "prefill_ragged",
-                                  "union_r4", "union_r2", "fp8_prefill", "fp8_prefill_r512", "r5", "r6", "r7",
-                                  "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "union_r7", "topk8", "topk32",
-                                  "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"]
-                         + CUS_CASES)
-@pytest.mark.parametrize("fused", [True, False])
+FULL_STEP_CASES = ["cfg1_f32", "cfg2_small", "cfg3_small", "cfg4_small", "cfg5_small", "ragged", "ragged_r4", "r3",
+                   "r8", "prefix_wide", "prefix_short", "fp8_cfg3_small", "fp8_ragged", "fp8_ragged_r4", "fp8_r8",
+                   "union_r4", "union_r2", "r5", "r6", "r7", "fp8_r5", "fp8_r6", "fp8_r7", "union_r3", "union_r7",
+                   "topk8", "topk32", "topk32_r4", "fp8_topk8", "wide_table", "wide_table_r4", "topk64", "topk1"]
+# Prefill chunks given a workspace run the same kernels fused or not (the top-k launch, then the
+# block-major route), and the wide-batch cases' separate route is covered on the oracle's
+# selection: both run fused only.
+FUSED_ONLY_CASES = ["prefill_r512", "prefill_ragged", "fp8_prefill", "fp8_prefill_r512"] + CUS_CASES
+
+
+@pytest.mark.parametrize("case,fused", [(c, f) for c in FULL_STEP_CASES for f in (True, False)]
+                         + [(c, True) for c in FUSED_ONLY_CASES])
 def test_full_step(M, oracle, case, fused):
     """Steps 0-4 (insert, index, selection, attention); fused = selection and attention in one launch."""
     wl = CASES[case]()
@@ -708,12 +718,14 @@ def test_prefill_row_route(M, oracle, case):
     _check_full_step(M, oracle, wl, fused=True, workspace=False)
 
 
-@pytest.mark.parametrize("case", ["prefill_topk64", "prefill_topk1", "prefill_wide_table"])
-@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("case,fused", [("prefill_topk64", True), ("prefill_topk1", True),
+                                        ("prefill_wide_table", True), ("prefill_wide_table", False)])
 def test_prefill_more_cases(M, oracle, case, fused):
     """Prefill chunks at the edges of the block-major route: 64 ranks per row (the merge's
     groups of 16 ranks four times), one rank per row, and a block table wider than the route
-    counts in LDS (8,300 pages: the workspace size is 0 and the per-row form runs)."""
+    counts in LDS (8,300 pages: the workspace size is 0 and the per-row form runs, whose fused
+    selection differs from the separate one; the block-major route runs the same kernels
+    either way)."""
     wl = CASES[case]()
     _print_case(f"{case} fused={fused}", wl)
     if case == "prefill_wide_table":
@@ -970,31 +982,44 @@ def test_random_shared_prefix(M, oracle, seed):
     _check_full_step(M, oracle, wl, new_rows=new_rows)
 
 
+def _table_order_step_equal(M, wl, dec):
+    """The step again in block-table order (no owner map), on the caches the physical-order
+    step left with its new rows written: bitwise the same block scores, selections and outputs."""
+    from block_sparse_attention_index_amd.decoder import MsaDecoder
+
+    b = dec.batch
+    dec2 = MsaDecoder(M.Batch(b.block_table, b.ctx_lens, wl.R), dec.k, dec.v, dec.idx, wl.topk)
+    qi32, q32 = W.queries(wl)
+    q_idx = M.msa_quantize_e4m3(_dev(qi32), wl.q_scale)
+    q = M.msa_quantize_e4m3(_dev(q32), wl.q_scale)
+    dec2.block_scores.fill_(3.0), dec2.sel.fill_(-5), dec2.cnt.fill_(-5), dec2.out.fill_(7.0)
+    dec2.step(q_idx, q, wl.q_scale, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dec2.block_scores.view(torch.int32), dec.block_scores.view(torch.int32))
+    assert torch.equal(dec2.cnt, dec.cnt) and torch.equal(dec2.sel, dec.sel)
+    assert torch.equal(dec2.out.view(torch.int32), dec.out.view(torch.int32))
+
+
 def test_full_size_config3_owned_sampled(M, oracle):
-    """Configuration 3 at full size through the physical-order scan, the step inserting its
-    new rows (the benchmark's launch configuration); three sampled requests end to end."""
+    """Configuration 3 at full size (B=32, 64K-192K tokens) through the physical-order scan,
+    the step inserting its new rows (the benchmark's launch configuration); three sampled
+    requests end to end against the oracle, then the whole batch in block-table order bitwise."""
     wl = W.make_workload(3, seed=0)
     _print_case("config 3 full size, owner map", wl)
     rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 7]
-    _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
+    dec = _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
+    _table_order_step_equal(M, wl, dec)
 
 
 def test_full_size_config3_fp8_owned_sampled(M, oracle):
     """The 128K-context batch in FP8 caches at full size through the physical-order scan,
-    the step inserting its new rows; two sampled requests end to end."""
+    the step inserting its new rows; three sampled requests end to end against the oracle,
+    then the whole batch in block-table order bitwise."""
     wl = W.make_workload(3, seed=0, cache="fp8")
     _print_case("config 3 fp8 full size, owner map", wl)
-    rows = [int(np.argmin(wl.lengths)), 11]
-    _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
-
-
-def test_full_size_config3_sampled(M, oracle):
-    """Configuration 3 at full size (B=32, 64K-192K tokens), in the bench's launch
-    configuration; the oracle checks three sampled requests end to end."""
-    wl = W.make_workload(3, seed=0)
-    _print_case("config 3 full size", wl)
-    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 7]
-    _check_full_step(M, oracle, wl, sample=rows)
+    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths)), 11]
+    dec = _check_full_step(M, oracle, wl, sample=rows, new_rows=True, owner=True)
+    _table_order_step_equal(M, wl, dec)
 
 
 def test_full_size_config2_sampled(M, oracle):
@@ -1016,15 +1041,6 @@ def test_full_size_config4_sampled(M, oracle):
     wl = W.make_workload(4, seed=0)
     _print_case("config 4 full size", wl)
     _check_full_step(M, oracle, wl, sample=[0, 5])
-
-
-def test_full_size_config3_fp8_sampled(M, oracle):
-    """The 128K-context batch in FP8 caches at full size, the step inserting its new rows; the
-    oracle checks two sampled requests end to end."""
-    wl = W.make_workload(3, seed=0, cache="fp8")
-    _print_case("config 3 fp8 full size", wl)
-    rows = [int(np.argmin(wl.lengths)), int(np.argmax(wl.lengths))]
-    _check_full_step(M, oracle, wl, sample=rows, new_rows=True)
 
 
 def test_full_size_config5_sampled(M, oracle):
