@@ -733,28 +733,32 @@ def test_prefill_more_cases(M, oracle, case, fused):
     _check_full_step(M, oracle, wl, fused=fused)
 
 
-@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512", "prefill_topk64", "fp8_prefill"])
-def test_prefill_hand_selections_both_routes(M, oracle, case):
-    """msa_sparse_decode on a prefill chunk with hand-made selections: blocks named twice,
-    ranks in no order, counts from 0 to topk, and entries inside the count that name no
-    block (-1, or past the table), which count as absent.  Through the block-major route
-    (the workspace) and the per-row route (the no-allocation call, whose scratch array is
-    too small for the block-major partials), each against the oracle's attention on the
-    same sets with the absent entries left out."""
-    wl = CASES[case]()
-    _print_case(f"{case} hand-made selections", wl)
+def _hand_selection_check(M, oracle, wl, names, distinct=False):
+    """msa_sparse_decode with hand-made selections through the workspace call and the
+    no-allocation call (names: what each route is), both against the oracle's attention on
+    the same sets with the absent entries left out.  distinct: a block named again within a
+    row is replaced by -1 (the selection never repeats a block; a row group's union attends
+    each block once per row, so repeats are only compared on one-row routes)."""
     dec, q_idx, q = gpu_setup(M, wl)
-    assert M.msa_workspace_bytes(dec.batch, wl.topk) > M.MSA_NOALLOC_SCRATCH_BYTES
     rng = np.random.default_rng(5)
     p = row_positions(wl)
     nb = np.maximum(p // 128 + 1, 0)
     shape = (wl.B, wl.R, 4, wl.topk)
     cnt = rng.integers(0, wl.topk + 1, size=shape[:3]).astype(np.int32)
+    odd = rng.random(shape[:3])
+    cnt[odd < 0.03] = wl.topk + 3
+    cnt[(odd >= 0.03) & (odd < 0.06)] = -2
     cnt[p < 0] = 0
     ids = np.floor(rng.random(shape) * nb[:, :, None, None]).astype(np.int32)
     k = np.arange(wl.topk)[None, None, None, :]
     inside = k < cnt[..., None]
     absent = inside & (rng.random(shape) < 0.05)
+    if distinct:  # later repeats within a row become absent entries
+        for idx in np.ndindex(*shape[:3]):
+            _, first = np.unique(ids[idx], return_index=True)
+            rep = np.ones(wl.topk, bool)
+            rep[first] = False
+            absent[idx] |= rep & inside[idx]
     sel_gpu = np.where(inside, ids, -1).astype(np.int32)
     sel_gpu[absent] = np.where(rng.random(int(absent.sum())) < 0.5, -1, wl.max_pages + 3)
     sel_ref = np.full(shape, -1, np.int32)
@@ -767,21 +771,50 @@ def test_prefill_hand_selections_both_routes(M, oracle, case):
     dec.sel.copy_(_dev(sel_gpu))
     dec.cnt.copy_(_dev(cnt))
     dec.attend(q, wl.q_scale, wl.sm_scale)
-    out_block = dec.out.clone()
-    out_row = torch.full_like(dec.out, 7.0)
+    out_ws = dec.out.clone()
+    out_na = torch.full_like(dec.out, 7.0)
     M.msa_sparse_decode_noalloc(dec.batch, q, dec.q_dtype, wl.q_scale, wl.sm_scale, dec.k, dec.v, dec.sel, dec.cnt,
-                                wl.topk, out_row)
+                                wl.topk, out_na)
     torch.cuda.synchronize()
     _, ck, cv = oracle_caches(oracle, wl)
     _, _, _, qd = oracle_queries(oracle, wl)
     ref = oracle.attention(oracle_batch(oracle, wl), qd, wl.sm_scale, ck, cv, sel_ref, cnt_ref)
     empty = np.repeat(cnt_ref == 0, 8, axis=2)
-    for name, got_t in (("block-major", out_block), ("per-row", out_row)):
+    for name, got_t in zip(names, (out_ws, out_na)):
         got = got_t.cpu().numpy().astype(np.float64)
         assert (got[empty] == 0).all(), name
         err = _out_err(got, ref)
         print(f"  {name}: max per-vector relative error {err[~empty].max(initial=0.0):.3e}", flush=True)
         assert err[~empty].max(initial=0.0) <= OUT_TOL, name
+    return dec
+
+
+@pytest.mark.parametrize("case", ["prefill_ragged", "prefill_r512", "prefill_topk64", "fp8_prefill"])
+def test_prefill_hand_selections_both_routes(M, oracle, case):
+    """msa_sparse_decode on a prefill chunk with hand-made selections: blocks named twice,
+    ranks in no order, counts from 0 to topk (a few above topk, which read as topk, and a few
+    negative, which read as 0), and entries inside the count that name no block (-1, or past
+    the table), which count as absent.  Through the block-major route (the workspace) and the
+    per-row route (the no-allocation call, whose scratch array is too small for the
+    block-major partials), each against the oracle's attention on the same sets with the
+    absent entries left out."""
+    wl = CASES[case]()
+    _print_case(f"{case} hand-made selections", wl)
+    wl_batch = M.Batch(_dev(wl.block_table), _dev(wl.lengths), wl.R)
+    assert M.msa_workspace_bytes(wl_batch, wl.topk) > M.MSA_NOALLOC_SCRATCH_BYTES
+    _hand_selection_check(M, oracle, wl, ("block-major", "per-row"))
+
+
+@pytest.mark.parametrize("case", ["cfg1_f32", "cfg2_small", "cfg3_small", "ragged_r4", "union_r4", "fp8_cfg3_small",
+                                  "cus_b48", "topk32"])
+def test_decode_hand_selections(M, oracle, case):
+    """The same hand-made selections through the decode forms: FP32 per-block partials, rows
+    split over 4 and 2 workgroups, one workgroup per row, row-group unions, FP8, through the
+    workspace call and the no-allocation call (the same kernels, its scratch array in place
+    of the workspace)."""
+    wl = CASES[case]()
+    _print_case(f"{case} hand-made selections", wl)
+    _hand_selection_check(M, oracle, wl, ("workspace", "no-allocation"), distinct=case == "union_r4")
 
 
 def test_full_step_deterministic(M, oracle):
